@@ -1,0 +1,68 @@
+"""Plant plausible mistakes in the oracle and check that the pins catch each.
+
+Each mutant is the oracle's C source with one textual change (a dropped term,
+a wrong sign, a wrong index, a different rounding), compiled with the same gcc
+flags into a temporary library.  The pins of ``pins.py`` run against it; at
+least one must fail.  The mistakes are planted in the oracle, on the CPU only.
+"""
+
+import os
+
+import pytest
+
+import oracle
+import pins
+
+MUTANTS = {
+    "sigmoid_sign": ("return 1.0 / (1.0 + exp(-t));", "return 1.0 / (1.0 + exp(t));"),
+    "fwd_drops_alpha": ("return x * oracle_sigmoid(alpha * x);", "return x * oracle_sigmoid(x);"),
+    "fwd_drops_x": ("return x * oracle_sigmoid(alpha * x);", "return oracle_sigmoid(alpha * x);"),
+    "bwd_sign": ("return dy * s * (1.0 + t * one_minus_s);", "return dy * s * (1.0 - t * one_minus_s);"),
+    "bwd_chain_drops_alpha": ("return dy * s * (1.0 + t * one_minus_s);",
+                              "return dy * s * (1.0 + x * one_minus_s);"),
+    "bwd_drops_dy": ("return dy * s * (1.0 + t * one_minus_s);", "return s * (1.0 + t * one_minus_s);"),
+    "bwd_drops_one": ("return dy * s * (1.0 + t * one_minus_s);", "return dy * s * (t * one_minus_s);"),
+    "bwd_one_minus_s_is_s": ("double one_minus_s = 1.0 - s;", "double one_minus_s = s;"),
+    "bwd_t_without_alpha": ("    double t = alpha * x;\n    double s = oracle_sigmoid(t);",
+                            "    double t = x;\n    double s = oracle_sigmoid(alpha * x);"),
+    "bf16_truncates": ("double r = nearbyint(a / spacing) * spacing;",
+                       "double r = floor(a / spacing) * spacing;"),
+    "bf16_ties_away": ("double r = nearbyint(a / spacing) * spacing;",
+                       "double r = round(a / spacing) * spacing;"),
+    "bf16_wrong_spacing": ("double spacing = ldexp(1.0, k - 7);", "double spacing = ldexp(1.0, k - 8);"),
+    "bf16_wrong_subnormal_floor": ("if (k < -126)\n        k = -126;", "if (k < -140)\n        k = -140;"),
+    "bf16_via_f32": ("double r = nearbyint(a / spacing) * spacing;",
+                     "double r = nearbyint((double)(float)a / spacing) * spacing;"),
+    "f32_flushes_subnormals": ("return (float)v;", "return fabs(v) < 0x1p-126 ? (float)(0.0 * v) : (float)v;"),
+    "bf16_widen_shift": ("uint32_t w = (uint32_t)bits << 16;", "uint32_t w = (uint32_t)bits << 15;"),
+    "scale_drops_abs": ("*scale = fabs(dy) * s * (1.0 + fabs(t) * one_minus_s);",
+                        "*scale = fabs(dy) * s * (1.0 + t * one_minus_s);"),
+    "split_drops_last": ("jobs[k].end = n * (size_t)(k + 1) / (size_t)threads;",
+                         "jobs[k].end = n * (size_t)(k + 1) / (size_t)threads - (k + 1 == threads);"),
+    "alpha_rounded_to_int": ("oracle_job j = {dtype, x, NULL, y, NULL, (double)alpha, 0, 0};",
+                             "oracle_job j = {dtype, x, NULL, y, NULL, (double)(int)alpha, 0, 0};"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle.SOURCE) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, source, tmp_path):
+    old, new = MUTANTS[name]
+    assert source.count(old) == 1, f"mutation site for {name} not unique/present"
+    src = tmp_path / "mutant.c"
+    src.write_text(source.replace(old, new))
+    lib = oracle.build(str(src), str(tmp_path / "libmutant.so"))
+    o = oracle.Oracle(oracle.load(lib))
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(o)
+        except AssertionError:
+            caught.append(pin.__name__)
+            break
+    assert caught, f"no pin caught mutant {name}"
