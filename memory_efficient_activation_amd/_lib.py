@@ -1,0 +1,86 @@
+"""ctypes loader for libmeswish.so (the C ABI declared in include/meswish.h).
+
+Argument marshalling only: every element of every pass is computed by the
+HIP kernels inside the library.  There is no CPU fallback -- if the library
+is missing or the tensors are not on a HIP device, calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "libmeswish.so")
+
+# Status codes and dtypes (mirror include/meswish.h).
+OK, EINVAL, EALIAS, EHIP, ETOOMANY = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+MAX_GROUP = 64
+
+EXPORTED = ("swish_fwd", "swish_bwd", "swish_fwd_grouped", "swish_bwd_grouped",
+            "meswish_strerror", "meswish_version", "meswish_copy")
+
+
+class FwdDesc(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("y", ctypes.c_void_p), ("n", ctypes.c_size_t)]
+
+
+class BwdDesc(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("dy", ctypes.c_void_p), ("dx", ctypes.c_void_p),
+                ("n", ctypes.c_size_t)]
+
+
+class MeswishError(RuntimeError):
+    """A non-zero status returned by libmeswish."""
+
+    def __init__(self, status: int, what: str, message: str):
+        super().__init__(f"{what}: {message} (status {status})")
+        self.status = status
+
+
+def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
+    vp, sz, f, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float, ctypes.c_int
+    lib.swish_fwd.argtypes = [vp, vp, sz, f, i, vp]
+    lib.swish_fwd.restype = i
+    lib.swish_bwd.argtypes = [vp, vp, vp, sz, f, i, vp]
+    lib.swish_bwd.restype = i
+    lib.swish_fwd_grouped.argtypes = [ctypes.POINTER(FwdDesc), i, f, i, vp]
+    lib.swish_fwd_grouped.restype = i
+    lib.swish_bwd_grouped.argtypes = [ctypes.POINTER(BwdDesc), i, f, i, vp]
+    lib.swish_bwd_grouped.restype = i
+    lib.meswish_strerror.argtypes = [i]
+    lib.meswish_strerror.restype = ctypes.c_char_p
+    lib.meswish_version.argtypes = []
+    lib.meswish_version.restype = i
+    lib.meswish_copy.argtypes = [vp, vp, sz, vp]
+    lib.meswish_copy.restype = i
+    return lib
+
+
+_LIB = None
+_LOCK = threading.Lock()
+
+
+def library(path: str | None = None) -> ctypes.CDLL:
+    """Load libmeswish.so once (after torch, so that both share one HIP runtime)."""
+    global _LIB
+    if path is not None:
+        import torch  # noqa: F401  (the HIP runtime torch loads is the one the library binds to)
+        return _declare(ctypes.CDLL(path))
+    with _LOCK:
+        if _LIB is None:
+            if not os.path.exists(LIBRARY):
+                raise RuntimeError(
+                    f"{LIBRARY} is not built; run `python -c 'import __graft_entry__ as g; "
+                    "g.build()'` (hipcc --offload-arch=gfx950)")
+            import torch  # noqa: F401
+            _LIB = _declare(ctypes.CDLL(LIBRARY))
+    return _LIB
+
+
+def check(status: int, what: str) -> None:
+    if status != OK:
+        msg = library().meswish_strerror(status).decode()
+        raise MeswishError(status, what, msg)

@@ -1,0 +1,41 @@
+"""Build libmeswish.so in-tree with hipcc for gfx950."""
+
+from __future__ import annotations
+
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SOURCE = os.path.join(HERE, "csrc", "meswish.hip")
+INCLUDE = os.path.join(ROOT, "include")
+LIBRARY = os.path.join(HERE, "libmeswish.so")
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    # No packed-fp32 instructions (v_pk_*_f32) anywhere in the device code.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    path = os.path.join(rocm, "bin", "hipcc")
+    return path if os.path.exists(path) else "hipcc"
+
+
+def build(output: str = LIBRARY, extra_flags: list[str] | None = None) -> str:
+    """Compile libmeswish.so (always recompiles) and return its path."""
+    tmp = output + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", SOURCE, "-o", tmp]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, output)
+    return output
+
+
+if __name__ == "__main__":
+    print(build())

@@ -1,0 +1,841 @@
+// meswish.hip -- HIP kernels and C-ABI launchers of libmeswish for gfx950.
+//
+// The operation (blog post "Memory efficient Swish", adeeplearner.github.io,
+// 2021-05-17):
+//   forward  ("How is Swish implemented?")               y  = x * Sigmoid(t)
+//   backward ("How is the memory efficient version Swish implemented?")
+//                                                          dx = dy * s * (1 + t (1 - s))
+// with t = alpha x and s = Sigmoid(t) = 1 / (1 + e^-t) ("What is a Swish
+// activation function?").  The backward reads only x and dy: the input is
+// the one tensor kept between the passes.
+//
+// Design for MI355X (CDNA4):
+//   * The work is element-wise with an arithmetic intensity of about one to
+//     two flops per byte ("What activations cost, in memory and in
+//     arithmetic", Conclusion), far below the ~20 flop/byte ridge of the
+//     chip's vector ALUs, so HBM bandwidth is the bound: no LDS, no MFMA, no
+//     atomics, no barriers.  Each lane moves 16-byte vectors (4 binary32 or
+//     8 bfloat16), a wave touches 1 KiB contiguous per access, and a thread
+//     issues all its loads of an iteration before any arithmetic.
+//   * Grid-stride over tiles of kBlock * kUnroll vectors; the grid is sized
+//     to the device's compute units (256 on MI355X, 8 XCDs).
+//   * Arithmetic is binary32 with the hardware exp2 and reciprocal
+//     (v_exp_f32, v_rcp_f32).  The sigmoid is evaluated as
+//     e = 2^(-|t| log2 e) <= 1, p = 1/(1+e), q = e p, s = p (t >= 0) or q,
+//     1 - s = q (t >= 0) or p, so nothing overflows and 1 - s never cancels.
+//   * binary32 I/O: the exponent -|alpha x| log2 e is carried as a hi+lo
+//     pair so the exponential keeps binary32 accuracy at |alpha x| ~ 90.
+//   * e below the binary32 normal range (|alpha x| > 87.3) takes a rare
+//     branch that scales by powers of two (frexp/ldexp) so that subnormal
+//     results round once and keep gradual underflow (the hardware
+//     transcendentals flush subnormals).
+//   * bfloat16 I/O: widening is a 16-bit shift; narrowing is the gfx950
+//     v_cvt_pk_bf16_f32 (round to nearest even), two elements per op.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "meswish.h"
+
+#ifndef MESWISH_BLOCK
+#define MESWISH_BLOCK 256
+#endif
+#ifndef MESWISH_UNROLL
+#define MESWISH_UNROLL 4
+#endif
+#ifndef MESWISH_BLOCKS_PER_CU
+#define MESWISH_BLOCKS_PER_CU 8
+#endif
+#ifndef MESWISH_NT_LOAD
+#define MESWISH_NT_LOAD 0
+#endif
+#ifndef MESWISH_NT_STORE
+#define MESWISH_NT_STORE 0
+#endif
+
+namespace meswish {
+
+constexpr int kBlock = MESWISH_BLOCK;
+constexpr int kUnroll = MESWISH_UNROLL;
+constexpr int kTileVecs = kBlock * kUnroll;  // 16-byte vectors per tile
+
+// ---------------------------------------------------------------------------
+// Coefficients prepared on the host.
+// ---------------------------------------------------------------------------
+
+struct Coef {
+    float alpha;      // alpha
+    float cn_hi;      // binary32 nearest to -|alpha| log2(e)
+    float cn_lo_ln2;  // (-|alpha| log2(e) - cn_hi) * ln 2
+};
+
+static Coef make_coef(float alpha)
+{
+    const double log2e = 1.44269504088896340735992468100189214;
+    const double ln2 = 0.693147180559945309417232121458176568;
+    double c = -fabs((double)alpha) * log2e;
+    float hi = (float)c;
+    Coef k;
+    k.alpha = alpha;
+    k.cn_hi = hi;
+    k.cn_lo_ln2 = (float)((c - (double)hi) * ln2);
+    return k;
+}
+
+// ---------------------------------------------------------------------------
+// Element math.
+// ---------------------------------------------------------------------------
+
+constexpr float kLn2f = 0.693147180559945309f;
+// Below this exponent 2^v is no longer a binary32 normal number.
+constexpr float kMinNormalExp = -126.0f;
+// Below this exponent every result of the scaled branch rounds to zero:
+// |x| < 2^128 and 2^-300 * 2^128 < 2^-150.
+constexpr float kZeroExp = -300.0f;
+
+__device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2f(v); }
+__device__ __forceinline__ float rcp_hw(float v) { return __builtin_amdgcn_rcpf(v); }
+
+// e = exp(-|alpha x|) for exponents in the normal range.  vh receives the
+// (hi part of the) base-2 exponent, used to detect the out-of-range case.
+template <bool kPrecise>
+__device__ __forceinline__ float neg_exp(float x, const Coef& k, float& vh)
+{
+    float ax = fabsf(x);
+    vh = ax * k.cn_hi;
+    float e = exp2_hw(vh);
+    if (kPrecise) {
+        float err = fmaf(ax, k.cn_hi, -vh);           // exact error of vh
+        float w = fmaf(ax, k.cn_lo_ln2, err * kLn2f);  // rest of exponent, times ln 2
+        e = fmaf(e, w, e);                             // 2^vh * (1 + w)
+    }
+    return e;
+}
+
+template <bool kPrecise>
+__device__ __forceinline__ float fwd_fast(float x, const Coef& k, bool& scaled)
+{
+    float vh;
+    float e = neg_exp<kPrecise>(x, k, vh);
+    float p = rcp_hw(1.0f + e);
+    float q = e * p;
+    float s = (k.alpha * x >= 0.0f) ? p : q;
+    scaled |= vh < kMinNormalExp;
+    return x * s;
+}
+
+template <bool kPrecise>
+__device__ __forceinline__ float bwd_fast(float x, float dy, const Coef& k, bool& scaled)
+{
+    float vh;
+    float e = neg_exp<kPrecise>(x, k, vh);
+    float p = rcp_hw(1.0f + e);
+    float q = e * p;
+    float t = k.alpha * x;
+    bool pos = t >= 0.0f;
+    float s = pos ? p : q;
+    float c = pos ? q : p;  // 1 - s
+    float g = fmaf(t, c, 1.0f);
+    scaled |= vh < kMinNormalExp;
+    return dy * (s * g);
+}
+
+__device__ __forceinline__ bool needs_scaling(float x, const Coef& k)
+{
+    return fabsf(x) * k.cn_hi < kMinNormalExp;
+}
+
+// The branch for e = exp(-|t|) < 2^-126.  There p = 1/(1+e) rounds to 1.
+// For t >= 0, s rounds to 1 and y = x.  For t < 0, s = e = ef * 2^kf with
+// ef in [1, 2], and the result is assembled as mantissa * 2^exponent so that
+// it is rounded once, at the end, even when it is subnormal.
+__device__ __forceinline__ float fwd_scaled(float x, Coef k)
+{
+    if (k.alpha * x >= 0.0f)
+        return x;
+    float ax = fabsf(x);
+    float vh = ax * k.cn_hi;
+    if (vh < kZeroExp)
+        return x * 0.0f;
+    float err = fmaf(ax, k.cn_hi, -vh);
+    float w = fmaf(ax, k.cn_lo_ln2, err * kLn2f);
+    float kf = floorf(vh);
+    float ef = exp2_hw(vh - kf);
+    ef = fmaf(ef, w, ef);
+    int ex;
+    float mx = frexpf(x, &ex);
+    return ldexpf(mx * ef, ex + (int)kf);
+}
+
+// Same branch for the backward: for t >= 0, dx = dy; for t < 0,
+// 1 - s rounds to 1 and dx = dy * e * (1 + t).
+__device__ __forceinline__ float bwd_scaled(float x, float dy, Coef k)
+{
+    float t = k.alpha * x;
+    if (t >= 0.0f)
+        return dy;
+    float ax = fabsf(x);
+    float vh = ax * k.cn_hi;
+    if (vh < kZeroExp)
+        return dy * -0.0f;
+    float err = fmaf(ax, k.cn_hi, -vh);
+    float w = fmaf(ax, k.cn_lo_ln2, err * kLn2f);
+    float kf = floorf(vh);
+    float ef = exp2_hw(vh - kf);
+    ef = fmaf(ef, w, ef);
+    float g = 1.0f + t;
+    int ed;
+    float md = frexpf(dy, &ed);
+    return ldexpf(md * ef * g, ed + (int)kf);
+}
+
+// ---------------------------------------------------------------------------
+// Element types.
+// ---------------------------------------------------------------------------
+
+struct bf16_t {
+    uint16_t bits;
+};
+
+typedef float float2_v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    float2_v f = {lo, hi};
+    bf16x2_v b = __builtin_convertvector(f, bf16x2_v);
+    uint32_t u;
+    __builtin_memcpy(&u, &b, sizeof u);
+    return u;
+}
+
+template <typename IO> struct Io;
+
+template <> struct Io<float> {
+    static constexpr int kPerVec = 4;
+    static constexpr bool kPrecise = true;
+    __device__ static void unpack(const uint4& v, float (&f)[4])
+    {
+        f[0] = __uint_as_float(v.x);
+        f[1] = __uint_as_float(v.y);
+        f[2] = __uint_as_float(v.z);
+        f[3] = __uint_as_float(v.w);
+    }
+    __device__ static uint4 pack(const float (&f)[4])
+    {
+        return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
+                          __float_as_uint(f[2]), __float_as_uint(f[3]));
+    }
+    __device__ static float load1(const float* p, int64_t i) { return p[i]; }
+    __device__ static void store1(float* p, int64_t i, float v) { p[i] = v; }
+};
+
+template <> struct Io<bf16_t> {
+    static constexpr int kPerVec = 8;
+    static constexpr bool kPrecise = false;
+    __device__ static void unpack(const uint4& v, float (&f)[8])
+    {
+        f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+        f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+        f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+        f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+    }
+    __device__ static uint4 pack(const float (&f)[8])
+    {
+        return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                          pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+    }
+    __device__ static float load1(const bf16_t* p, int64_t i)
+    {
+        return __uint_as_float((uint32_t)p[i].bits << 16);
+    }
+    __device__ static void store1(bf16_t* p, int64_t i, float v)
+    {
+        p[i].bits = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+    }
+};
+
+__device__ __forceinline__ uint4 ld16(const uint4* p)
+{
+#if MESWISH_NT_LOAD
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+
+__device__ __forceinline__ void st16(uint4* p, const uint4& v)
+{
+#if MESWISH_NT_STORE
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
+// One 16-byte vector of the forward / backward.
+template <typename IO>
+__device__ __forceinline__ uint4 fwd_vec(const uint4& xv, const Coef& k)
+{
+    constexpr int E = Io<IO>::kPerVec;
+    float xf[E], yf[E];
+    Io<IO>::unpack(xv, xf);
+    bool scaled = false;
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+        yf[j] = fwd_fast<Io<IO>::kPrecise>(xf[j], k, scaled);
+    if (__builtin_expect(scaled, 0)) {
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            if (needs_scaling(xf[j], k))
+                yf[j] = fwd_scaled(xf[j], k);
+    }
+    return Io<IO>::pack(yf);
+}
+
+template <typename IO>
+__device__ __forceinline__ uint4 bwd_vec(const uint4& xv, const uint4& dv, const Coef& k)
+{
+    constexpr int E = Io<IO>::kPerVec;
+    float xf[E], df[E], gf[E];
+    Io<IO>::unpack(xv, xf);
+    Io<IO>::unpack(dv, df);
+    bool scaled = false;
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+        gf[j] = bwd_fast<Io<IO>::kPrecise>(xf[j], df[j], k, scaled);
+    if (__builtin_expect(scaled, 0)) {
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            if (needs_scaling(xf[j], k))
+                gf[j] = bwd_scaled(xf[j], df[j], k);
+    }
+    return Io<IO>::pack(gf);
+}
+
+// One element (head, tail and unaligned paths).
+template <typename IO, bool kBwd>
+__device__ __forceinline__ void one_element(const IO* x, const IO* dy, IO* out, int64_t i,
+                                            const Coef& k)
+{
+    float xv = Io<IO>::load1(x, i);
+    bool scaled = false;
+    float r;
+    if (kBwd) {
+        float dv = Io<IO>::load1(dy, i);
+        r = bwd_fast<Io<IO>::kPrecise>(xv, dv, k, scaled);
+        if (scaled)
+            r = bwd_scaled(xv, dv, k);
+    } else {
+        r = fwd_fast<Io<IO>::kPrecise>(xv, k, scaled);
+        if (scaled)
+            r = fwd_scaled(xv, k);
+    }
+    Io<IO>::store1(out, i, r);
+}
+
+// Vectors [v_begin, v_end) of the 16-byte-aligned body starting at x, dy, out
+// (already offset past the head), processed by this block as tiles of
+// kTileVecs vectors with stride `tile_stride` tiles.
+template <typename IO, bool kBwd>
+__device__ __forceinline__ void body_tile(const uint4* xv, const uint4* dv, uint4* ov,
+                                          int64_t tile_first, int64_t nvec, const Coef& k)
+{
+    int64_t i = tile_first + threadIdx.x;
+    if (tile_first + kTileVecs <= nvec) {
+        uint4 a[kUnroll], b[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            a[u] = ld16(xv + i + u * kBlock);
+        if (kBwd) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                b[u] = ld16(dv + i + u * kBlock);
+        }
+        // Keep every load of the tile ahead of the first use of its data, so
+        // that a thread has all of them in flight at once.
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            st16(ov + i + u * kBlock, kBwd ? bwd_vec<IO>(a[u], b[u], k) : fwd_vec<IO>(a[u], k));
+    } else {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            int64_t j = i + u * kBlock;
+            if (j < nvec) {
+                uint4 a = ld16(xv + j);
+                uint4 r;
+                if (kBwd)
+                    r = bwd_vec<IO>(a, ld16(dv + j), k);
+                else
+                    r = fwd_vec<IO>(a, k);
+                st16(ov + j, r);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernels.
+// ---------------------------------------------------------------------------
+
+// Single tensor, all pointers congruent modulo 16 bytes: `head` scalar
+// elements, then nvec 16-byte vectors, then `tail` scalar elements.
+template <typename IO, bool kBwd>
+__global__ __launch_bounds__(kBlock) void swish_vec_kernel(const IO* x, const IO* dy, IO* out,
+                                                           int64_t head, int64_t nvec,
+                                                           int64_t tail, Coef k)
+{
+    constexpr int E = Io<IO>::kPerVec;
+    const uint4* xv = reinterpret_cast<const uint4*>(x + head);
+    const uint4* dv = kBwd ? reinterpret_cast<const uint4*>(dy + head) : nullptr;
+    uint4* ov = reinterpret_cast<uint4*>(out + head);
+    const int64_t stride = (int64_t)gridDim.x * kTileVecs;
+    for (int64_t t0 = (int64_t)blockIdx.x * kTileVecs; t0 < nvec; t0 += stride)
+        body_tile<IO, kBwd>(xv, dv, ov, t0, nvec, k);
+    if (blockIdx.x == 0 && threadIdx.x < head + tail) {
+        int64_t i = threadIdx.x < head ? (int64_t)threadIdx.x
+                                       : head + nvec * E + (threadIdx.x - head);
+        one_element<IO, kBwd>(x, dy, out, i, k);
+    }
+}
+
+// Single tensor, element by element (pointers not congruent modulo 16).
+template <typename IO, bool kBwd>
+__global__ __launch_bounds__(kBlock) void swish_elem_kernel(const IO* x, const IO* dy, IO* out,
+                                                            int64_t n, Coef k)
+{
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride)
+        one_element<IO, kBwd>(x, dy, out, i, k);
+}
+
+// Grouped: up to MESWISH_MAX_GROUP tensors in one launch.  Tensor j covers
+// tiles [tile_begin[j], tile_begin[j+1]) of the concatenated tile space; a
+// block walks the tiles b, b + gridDim, ... and finds each tile's tensor by
+// a forward scan (tiles of one block are increasing, so the scan is
+// amortised O(1)).  The first tile of a tensor also does its scalar head and
+// tail.  A tensor whose pointers are not congruent modulo 16 bytes (flag 0)
+// is processed element by element, kTileVecs elements per tile.
+struct GroupArgs {
+    const void* x[MESWISH_MAX_GROUP];
+    const void* dy[MESWISH_MAX_GROUP];
+    void* out[MESWISH_MAX_GROUP];
+    int64_t n[MESWISH_MAX_GROUP];
+    int64_t tile_begin[MESWISH_MAX_GROUP + 1];
+    int32_t head[MESWISH_MAX_GROUP];  // -1: element-wise tensor
+    int32_t count;
+};
+
+template <typename IO, bool kBwd>
+__global__ __launch_bounds__(kBlock) void swish_group_kernel(GroupArgs g, Coef k)
+{
+    constexpr int E = Io<IO>::kPerVec;
+    const int64_t total = g.tile_begin[g.count];
+    int j = 0;
+    for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
+        while (tile >= g.tile_begin[j + 1])
+            ++j;
+        const IO* x = static_cast<const IO*>(g.x[j]);
+        const IO* dy = static_cast<const IO*>(g.dy[j]);
+        IO* out = static_cast<IO*>(g.out[j]);
+        const int64_t n = g.n[j];
+        const int64_t local = tile - g.tile_begin[j];
+        const int32_t head = g.head[j];
+        if (head < 0) {
+            int64_t e0 = local * kTileVecs;
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                int64_t i = e0 + u * kBlock + threadIdx.x;
+                if (i < n)
+                    one_element<IO, kBwd>(x, dy, out, i, k);
+            }
+            continue;
+        }
+        const int64_t nvec = (n - head) / E;
+        const int64_t tail = n - head - nvec * E;
+        body_tile<IO, kBwd>(reinterpret_cast<const uint4*>(x + head),
+                            kBwd ? reinterpret_cast<const uint4*>(dy + head) : nullptr,
+                            reinterpret_cast<uint4*>(out + head), local * kTileVecs, nvec, k);
+        if (local == 0 && threadIdx.x < head + tail) {
+            int64_t i = threadIdx.x < head ? (int64_t)threadIdx.x
+                                           : head + nvec * E + (threadIdx.x - head);
+            one_element<IO, kBwd>(x, dy, out, i, k);
+        }
+    }
+}
+
+// Plain 16-byte copy (measurement helper).
+__global__ __launch_bounds__(kBlock) void copy16_kernel(const uint4* src, uint4* dst, int64_t nvec)
+{
+    const int64_t stride = (int64_t)gridDim.x * kTileVecs;
+    for (int64_t t0 = (int64_t)blockIdx.x * kTileVecs; t0 < nvec; t0 += stride) {
+        int64_t i = t0 + threadIdx.x;
+        if (t0 + kTileVecs <= nvec) {
+            uint4 a[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                a[u] = ld16(src + i + u * kBlock);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                st16(dst + i + u * kBlock, a[u]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                if (i + u * kBlock < nvec)
+                    st16(dst + i + u * kBlock, ld16(src + i + u * kBlock));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+
+constexpr int kMaxDevices = 64;
+static std::atomic<int> g_cu_count[kMaxDevices];
+
+// Compute units of the current device (cached per device).
+static int cu_count()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return 256;
+    if (dev < kMaxDevices) {
+        int c = g_cu_count[dev].load(std::memory_order_relaxed);
+        if (c > 0)
+            return c;
+    }
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        c <= 0)
+        c = 256;
+    if (dev < kMaxDevices)
+        g_cu_count[dev].store(c, std::memory_order_relaxed);
+    return c;
+}
+
+static int64_t grid_for_tiles(int64_t tiles)
+{
+    int64_t cap = (int64_t)cu_count() * MESWISH_BLOCKS_PER_CU;
+    if (tiles < 1)
+        tiles = 1;
+    return tiles < cap ? tiles : cap;
+}
+
+static size_t elem_size(int dtype) { return dtype == MESWISH_F32 ? 4 : 2; }
+
+static bool dtype_ok(int dtype) { return dtype == MESWISH_F32 || dtype == MESWISH_BF16; }
+
+// Ranges [a, a+na) and [b, b+nb) overlap.
+static bool overlaps(const void* a, size_t na, const void* b, size_t nb)
+{
+    uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+    return na && nb && pa < pb + nb && pb < pa + na;
+}
+
+// An output range may coincide exactly with an input range of the same
+// tensor, or be disjoint from it.
+static bool alias_ok(const void* out, const void* in, size_t bytes)
+{
+    return out == in || !overlaps(out, bytes, in, bytes);
+}
+
+static int launch(const void* fn, int64_t grid, void** args, hipStream_t stream)
+{
+    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kBlock), args, 0, stream);
+    return e == hipSuccess ? MESWISH_OK : MESWISH_EHIP;
+}
+
+// Elements before the first 16-byte boundary of p (p element-aligned).
+static int64_t head_elems(const void* p, size_t esize)
+{
+    uintptr_t mis = (uintptr_t)p & 15u;
+    return mis ? (int64_t)((16u - mis) / esize) : 0;
+}
+
+template <typename IO, bool kBwd>
+static int run_single(const void* x, const void* dy, void* out, size_t n, Coef k,
+                      hipStream_t stream)
+{
+    constexpr int E = Io<IO>::kPerVec;
+    uintptr_t mx = (uintptr_t)x & 15u, mo = (uintptr_t)out & 15u;
+    uintptr_t md = kBwd ? ((uintptr_t)dy & 15u) : mx;
+    const IO* xp = static_cast<const IO*>(x);
+    const IO* dp = static_cast<const IO*>(dy);
+    IO* op = static_cast<IO*>(out);
+    if (mx == mo && mx == md) {
+        int64_t head = head_elems(x, sizeof(IO));
+        if (head > (int64_t)n)
+            head = (int64_t)n;
+        int64_t nvec = ((int64_t)n - head) / E;
+        int64_t tail = (int64_t)n - head - nvec * E;
+        int64_t grid = grid_for_tiles((nvec + kTileVecs - 1) / kTileVecs);
+        void* args[] = {&xp, &dp, &op, &head, &nvec, &tail, &k};
+        return launch(reinterpret_cast<const void*>(&swish_vec_kernel<IO, kBwd>), grid, args,
+                      stream);
+    }
+    int64_t nn = (int64_t)n;
+    int64_t grid = grid_for_tiles((nn + kBlock * kUnroll - 1) / (kBlock * kUnroll));
+    void* args[] = {&xp, &dp, &op, &nn, &k};
+    return launch(reinterpret_cast<const void*>(&swish_elem_kernel<IO, kBwd>), grid, args, stream);
+}
+
+template <typename IO, bool kBwd>
+static int run_group(GroupArgs& g, Coef k, hipStream_t stream)
+{
+    constexpr int E = Io<IO>::kPerVec;
+    int64_t tiles = 0;
+    for (int j = 0; j < g.count; ++j) {
+        g.tile_begin[j] = tiles;
+        const int64_t n = g.n[j];
+        uintptr_t mx = (uintptr_t)g.x[j] & 15u, mo = (uintptr_t)g.out[j] & 15u;
+        uintptr_t md = kBwd ? ((uintptr_t)g.dy[j] & 15u) : mx;
+        int64_t t;
+        if (n == 0) {
+            g.head[j] = 0;
+            t = 0;
+        } else if (mx == mo && mx == md) {
+            int64_t head = head_elems(g.x[j], sizeof(IO));
+            if (head > n)
+                head = n;
+            g.head[j] = (int32_t)head;
+            int64_t nvec = (n - head) / E;
+            t = (nvec + kTileVecs - 1) / kTileVecs;
+            if (t == 0)
+                t = 1;  // a tensor shorter than one vector still needs its scalar tile
+        } else {
+            g.head[j] = -1;
+            t = (n + kTileVecs - 1) / kTileVecs;
+        }
+        tiles += t;
+    }
+    g.tile_begin[g.count] = tiles;
+    if (tiles == 0)
+        return MESWISH_OK;
+    int64_t grid = grid_for_tiles(tiles);
+    void* args[] = {&g, &k};
+    return launch(reinterpret_cast<const void*>(&swish_group_kernel<IO, kBwd>), grid, args,
+                  stream);
+}
+
+// Common argument checks.  Returns MESWISH_OK or an error code.
+static int check_common(float alpha, int dtype)
+{
+    if (!dtype_ok(dtype))
+        return MESWISH_EINVAL;
+    if (!isfinite(alpha))
+        return MESWISH_EINVAL;
+    return MESWISH_OK;
+}
+
+static int check_tensor(const void* p, size_t n, size_t esize)
+{
+    if (p == nullptr)
+        return MESWISH_EINVAL;
+    if ((uintptr_t)p % esize)
+        return MESWISH_EINVAL;
+    if (n > (size_t)INT64_MAX / 16)
+        return MESWISH_EINVAL;
+    return MESWISH_OK;
+}
+
+}  // namespace meswish
+
+using namespace meswish;
+
+extern "C" int swish_fwd(const void* x, void* y, size_t n, float alpha, int dtype, void* stream)
+{
+    int rc = check_common(alpha, dtype);
+    if (rc != MESWISH_OK || n == 0)
+        return rc;
+    size_t es = elem_size(dtype);
+    if ((rc = check_tensor(x, n, es)) != MESWISH_OK || (rc = check_tensor(y, n, es)) != MESWISH_OK)
+        return rc;
+    if (!alias_ok(y, x, n * es))
+        return MESWISH_EALIAS;
+    Coef k = make_coef(alpha);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == MESWISH_F32)
+        return run_single<float, false>(x, nullptr, y, n, k, s);
+    return run_single<bf16_t, false>(x, nullptr, y, n, k, s);
+}
+
+extern "C" int swish_bwd(const void* x, const void* dy, void* dx, size_t n, float alpha, int dtype,
+                         void* stream)
+{
+    int rc = check_common(alpha, dtype);
+    if (rc != MESWISH_OK || n == 0)
+        return rc;
+    size_t es = elem_size(dtype);
+    if ((rc = check_tensor(x, n, es)) != MESWISH_OK || (rc = check_tensor(dy, n, es)) != MESWISH_OK ||
+        (rc = check_tensor(dx, n, es)) != MESWISH_OK)
+        return rc;
+    if (!alias_ok(dx, x, n * es) || !alias_ok(dx, dy, n * es))
+        return MESWISH_EALIAS;
+    Coef k = make_coef(alpha);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == MESWISH_F32)
+        return run_single<float, true>(x, dy, dx, n, k, s);
+    return run_single<bf16_t, true>(x, dy, dx, n, k, s);
+}
+
+namespace meswish {
+
+// Validates a group and fills the kernel arguments.  in2 is NULL for the
+// forward.  Outputs may coincide exactly with their own tensor's inputs;
+// every other overlap involving an output is rejected.
+static int fill_group(GroupArgs& g, int count, const void* const* in1, const void* const* in2,
+                      void* const* out, const size_t* n, int dtype)
+{
+    size_t es = elem_size(dtype);
+    g.count = count;
+    for (int j = 0; j < count; ++j) {
+        int rc;
+        if (n[j] == 0) {
+            g.x[j] = in1[j];
+            g.dy[j] = in2 ? in2[j] : nullptr;
+            g.out[j] = out[j];
+            g.n[j] = 0;
+            continue;
+        }
+        if ((rc = check_tensor(in1[j], n[j], es)) != MESWISH_OK ||
+            (rc = check_tensor(out[j], n[j], es)) != MESWISH_OK)
+            return rc;
+        if (in2 && (rc = check_tensor(in2[j], n[j], es)) != MESWISH_OK)
+            return rc;
+        g.x[j] = in1[j];
+        g.dy[j] = in2 ? in2[j] : nullptr;
+        g.out[j] = out[j];
+        g.n[j] = (int64_t)n[j];
+    }
+    for (int j = 0; j < count; ++j) {
+        size_t bj = n[j] * es;
+        if (!bj)
+            continue;
+        if (!alias_ok(out[j], in1[j], bj) || (in2 && !alias_ok(out[j], in2[j], bj)))
+            return MESWISH_EALIAS;
+        for (int i = 0; i < count; ++i) {
+            size_t bi = n[i] * es;
+            if (i == j || !bi)
+                continue;
+            if (overlaps(out[j], bj, out[i], bi) || overlaps(out[j], bj, in1[i], bi) ||
+                (in2 && overlaps(out[j], bj, in2[i], bi)))
+                return MESWISH_EALIAS;
+        }
+    }
+    return MESWISH_OK;
+}
+
+}  // namespace meswish
+
+extern "C" int swish_fwd_grouped(const meswish_fwd_desc* desc, int count, float alpha, int dtype,
+                                 void* stream)
+{
+    int rc = check_common(alpha, dtype);
+    if (rc != MESWISH_OK)
+        return rc;
+    if (count < 0 || (count > 0 && desc == nullptr))
+        return MESWISH_EINVAL;
+    if (count > MESWISH_MAX_GROUP)
+        return MESWISH_ETOOMANY;
+    if (count == 0)
+        return MESWISH_OK;
+    const void* in1[MESWISH_MAX_GROUP];
+    void* out[MESWISH_MAX_GROUP];
+    size_t n[MESWISH_MAX_GROUP];
+    for (int j = 0; j < count; ++j) {
+        in1[j] = desc[j].x;
+        out[j] = desc[j].y;
+        n[j] = desc[j].n;
+    }
+    GroupArgs g;
+    memset(&g, 0, sizeof g);
+    if ((rc = fill_group(g, count, in1, nullptr, out, n, dtype)) != MESWISH_OK)
+        return rc;
+    Coef k = make_coef(alpha);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == MESWISH_F32)
+        return run_group<float, false>(g, k, s);
+    return run_group<bf16_t, false>(g, k, s);
+}
+
+extern "C" int swish_bwd_grouped(const meswish_bwd_desc* desc, int count, float alpha, int dtype,
+                                 void* stream)
+{
+    int rc = check_common(alpha, dtype);
+    if (rc != MESWISH_OK)
+        return rc;
+    if (count < 0 || (count > 0 && desc == nullptr))
+        return MESWISH_EINVAL;
+    if (count > MESWISH_MAX_GROUP)
+        return MESWISH_ETOOMANY;
+    if (count == 0)
+        return MESWISH_OK;
+    const void* in1[MESWISH_MAX_GROUP];
+    const void* in2[MESWISH_MAX_GROUP];
+    void* out[MESWISH_MAX_GROUP];
+    size_t n[MESWISH_MAX_GROUP];
+    for (int j = 0; j < count; ++j) {
+        in1[j] = desc[j].x;
+        in2[j] = desc[j].dy;
+        out[j] = desc[j].dx;
+        n[j] = desc[j].n;
+    }
+    GroupArgs g;
+    memset(&g, 0, sizeof g);
+    if ((rc = fill_group(g, count, in1, in2, out, n, dtype)) != MESWISH_OK)
+        return rc;
+    Coef k = make_coef(alpha);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == MESWISH_F32)
+        return run_group<float, true>(g, k, s);
+    return run_group<bf16_t, true>(g, k, s);
+}
+
+extern "C" int meswish_copy(const void* src, void* dst, size_t bytes, void* stream)
+{
+    if (bytes == 0)
+        return MESWISH_OK;
+    if (!src || !dst || ((uintptr_t)src & 15u) || ((uintptr_t)dst & 15u) || (bytes & 15u))
+        return MESWISH_EINVAL;
+    if (overlaps(src, bytes, dst, bytes))
+        return MESWISH_EALIAS;
+    const uint4* s = static_cast<const uint4*>(src);
+    uint4* d = static_cast<uint4*>(dst);
+    int64_t nvec = (int64_t)(bytes / 16);
+    int64_t grid = grid_for_tiles((nvec + kTileVecs - 1) / kTileVecs);
+    void* args[] = {&s, &d, &nvec};
+    return launch(reinterpret_cast<const void*>(&copy16_kernel), grid, args,
+                  static_cast<hipStream_t>(stream));
+}
+
+extern "C" const char* meswish_strerror(int status)
+{
+    switch (status) {
+    case MESWISH_OK:
+        return "success";
+    case MESWISH_EINVAL:
+        return "invalid argument (null or misaligned pointer, unknown dtype, non-finite alpha, "
+               "bad count or size)";
+    case MESWISH_EALIAS:
+        return "an output partially overlaps an input or another output";
+    case MESWISH_EHIP:
+        return "the HIP runtime reported an error at kernel launch";
+    case MESWISH_ETOOMANY:
+        return "grouped call with more tensors than MESWISH_MAX_GROUP";
+    default:
+        return "unknown status";
+    }
+}
+
+extern "C" int meswish_version(void) { return 100; }

@@ -1,0 +1,54 @@
+"""Autograd function and module of the memory-efficient Swish.
+
+Blog post "Memory efficient Swish" (adeeplearner.github.io, 2021-05-17):
+
+* "How is the memory efficient version Swish implemented?": one autograd
+  function whose forward keeps only its input and whose backward recomputes
+  the sigmoid from it, wrapped in a module.
+* "How is Swish implemented?": the module carries a slope ``alpha`` (a plain
+  float, default 1.0) applied inside the sigmoid.
+
+Both passes run in libmeswish's gfx950 kernels (``functional``); the only
+tensor kept between forward and backward is x.
+"""
+
+from __future__ import annotations
+
+import torch
+from torch import nn
+
+from .functional import swish_bwd, swish_fwd
+
+
+class SwishFn(torch.autograd.Function):
+    """y = x * sigmoid(alpha x); backward from the saved input alone."""
+
+    @staticmethod
+    def forward(ctx, x: torch.Tensor, alpha: float = 1.0) -> torch.Tensor:
+        y = swish_fwd(x, alpha)
+        ctx.save_for_backward(x)
+        ctx.alpha = float(alpha)
+        return y
+
+    @staticmethod
+    def backward(ctx, dy: torch.Tensor):
+        (x,) = ctx.saved_tensors
+        return swish_bwd(x, dy, ctx.alpha), None
+
+
+def swish(x: torch.Tensor, alpha: float = 1.0) -> torch.Tensor:
+    return SwishFn.apply(x, alpha)
+
+
+class MemoryEfficientSwish(nn.Module):
+    """Drop-in Swish module that keeps one tensor (its input) for backward."""
+
+    def __init__(self, alpha: float = 1.0):
+        super().__init__()
+        self.alpha = float(alpha)
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        return SwishFn.apply(x, self.alpha)
+
+    def extra_repr(self) -> str:
+        return f"alpha={self.alpha}"

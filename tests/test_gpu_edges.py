@@ -1,0 +1,240 @@
+"""GPU edge cases through the C ABI, each against the CPU oracle.
+
+* every finite bfloat16 input (65,280 patterns) at alpha 1 and 1.5 with
+  dy in {1, -1, 0.01}, forward and backward;
+* a stride sample of all binary32 bit patterns (about a million values,
+  every exponent), forward and backward, alpha 1 and 1.5;
+* the out-of-range exponent branch: x between -200 and -50 at alpha 1.5
+  (subnormal and underflowing results), tiny and huge alpha;
+* lengths 0..67 and misaligned pointers (vector, head/tail and element-wise
+  paths), in-place calls, NaN propagation, bitwise determinism, the alias
+  and limit checks, and grouped == single bit for bit.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import memory_efficient_activation_amd as mea
+from memory_efficient_activation_amd import _lib, inputs
+from oracle.compare import bf16_report, f32_report
+
+from gpu_util import ORACLE_THREADS, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(x_host, dy_host, alpha, oracle, x_dev=None, dy_dev=None):
+    x = to_dev(x_host) if x_dev is None else x_dev
+    dy = to_dev(dy_host) if dy_dev is None else dy_dev
+    y = mea.swish_fwd(x, alpha)
+    dx = mea.swish_bwd(x, dy, alpha)
+    torch.cuda.synchronize()
+    oy = oracle.fwd(x_host, alpha, threads=ORACLE_THREADS)
+    odx, m = oracle.bwd(x_host, dy_host, alpha, threads=ORACLE_THREADS)
+    if x_host.dtype == np.uint16:
+        return bf16_report(to_host(y), oy), bf16_report(to_host(dx), odx)
+    return f32_report(to_host(y), oy), f32_report(to_host(dx), odx, m)
+
+
+@pytest.mark.parametrize("alpha", [1.0, 1.5])
+@pytest.mark.parametrize("dyv", [1.0, -1.0, 0.01])
+def test_exhaustive_bf16(alpha, dyv, oracle):
+    xb = inputs.exhaustive_bf16_finite()
+    dyb = inputs.encode(np.full(xb.size, dyv), "bf16")
+    rf, rb = _check(xb, dyb, alpha, oracle)
+    say(f"[edges] exhaustive bf16 alpha={alpha} dy={dyv}: fwd {rf} bwd {rb}")
+    assert rf["ok"], rf
+    assert rb["ok"], rb
+
+
+@pytest.mark.parametrize("alpha", [1.0, 1.5])
+def test_fp32_bit_pattern_sample(alpha, oracle):
+    x = inputs.fp32_pattern_sample(4099)
+    rng = np.random.default_rng(3)
+    for dy in (np.ones(x.size, np.float32), rng.standard_normal(x.size).astype(np.float32)):
+        rf, rb = _check(x, dy, alpha, oracle)
+        say(f"[edges] fp32 pattern sample alpha={alpha}: fwd {rf} bwd {rb}")
+        assert rf["ok"], rf
+        assert rb["ok"], rb
+
+
+@pytest.mark.parametrize("alpha", [1.5, 1.0, 0.01, 1e-20, 40.0, -1.5])
+def test_scaled_exponent_branch(alpha, oracle):
+    rng = np.random.default_rng(11)
+    lim = 200.0 / abs(alpha)
+    x = np.concatenate([rng.uniform(-lim, lim, 200000),
+                        -np.geomspace(50 / abs(alpha), 400 / abs(alpha), 100000),
+                        np.geomspace(50 / abs(alpha), 400 / abs(alpha), 100000)]).astype(np.float32)
+    x = x[np.isfinite(x)]
+    dy = np.concatenate([rng.standard_normal(x.size - 8),
+                         [3e38, -3e38, 1e-30, -1e-40, 0.0, -0.0, 1e20, -7.0]]).astype(np.float32)
+    rf, rb = _check(x, dy, alpha, oracle)
+    say(f"[edges] scaled branch alpha={alpha}: fwd {rf} bwd {rb}")
+    assert rf["ok"], rf
+    assert rb["ok"], rb
+    xb = inputs.encode(x, "bf16")
+    dyb = inputs.encode(dy, "bf16")
+    rf, rb = _check(xb, dyb, alpha, oracle)
+    assert rf["ok"], rf
+    assert rb["ok"], rb
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_lengths_and_misalignment(dtype, oracle):
+    rng = np.random.default_rng(5)
+    base_x = inputs.encode(rng.standard_normal(4096) * 4, dtype)
+    base_dy = inputs.encode(rng.standard_normal(4096), dtype)
+    xd, dyd = to_dev(base_x), to_dev(base_dy)
+    outbuf = torch.empty_like(xd)
+    checked = 0
+    for n in list(range(0, 68)) + [1023, 2049]:
+        for ox in (0, 1, 3, 5):
+            for oo in (0, 1, 3):
+                if ox + n > 4096 or oo + n > 4096:
+                    continue
+                x = xd[ox:ox + n]
+                dy = dyd[oo:oo + n]  # dy shares dx's misalignment or not
+                y = outbuf[oo:oo + n]
+                mea.swish_fwd(x, 1.25, out=y)
+                torch.cuda.synchronize()
+                oy = oracle.fwd(base_x[ox:ox + n], 1.25)
+                got = to_host(y)
+                r = bf16_report(got, oy) if dtype == "bf16" else f32_report(got, oy)
+                assert r["ok"], (n, ox, oo, r)
+                dx = mea.swish_bwd(x, dy, 1.25, out=y)
+                torch.cuda.synchronize()
+                odx, m = oracle.bwd(base_x[ox:ox + n], base_dy[oo:oo + n], 1.25)
+                got = to_host(dx)
+                r = bf16_report(got, odx) if dtype == "bf16" else f32_report(got, odx, m)
+                assert r["ok"], (n, ox, oo, r)
+                checked += 1
+    say(f"[edges] {dtype}: {checked} (length, offset) cases")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_in_place(dtype, oracle):
+    w = inputs.make(3 if dtype == "bf16" else 2, n=100003)
+    x0, dy0 = to_dev(w.xs[0]), to_dev(w.dys[0])
+    y_ref = mea.swish_fwd(x0, w.alpha)
+    dx_ref = mea.swish_bwd(x0, dy0, w.alpha)
+    x = x0.clone()
+    mea.swish_fwd(x, w.alpha, out=x)
+    dy = dy0.clone()
+    mea.swish_bwd(x0, dy, w.alpha, out=dy)          # dx == dy
+    x2 = x0.clone()
+    mea.swish_bwd(x2, dy0, w.alpha, out=x2)         # dx == x
+    torch.cuda.synchronize()
+    iv = torch.int16 if dtype == "bf16" else torch.int32
+    assert torch.equal(x.view(iv), y_ref.view(iv))
+    assert torch.equal(dy.view(iv), dx_ref.view(iv))
+    assert torch.equal(x2.view(iv), dx_ref.view(iv))
+
+
+def test_nan_propagation():
+    for dtype in (torch.float32, torch.bfloat16):
+        x = torch.tensor([float("nan"), 1.0, -2.0, 0.5] * 8, device="cuda", dtype=dtype)
+        dy = torch.tensor([1.0, float("nan"), 1.0, 1.0] * 8, device="cuda", dtype=dtype)
+        y = mea.swish_fwd(x, 1.0)
+        dx = mea.swish_bwd(x, dy, 1.0)
+        torch.cuda.synchronize()
+        assert torch.isnan(y[0::4]).all() and not torch.isnan(y[1::4]).any()
+        assert torch.isnan(dx[0::4]).all() and torch.isnan(dx[1::4]).all()
+        assert not torch.isnan(dx[2::4]).any() and not torch.isnan(dx[3::4]).any()
+
+
+def test_bitwise_deterministic():
+    w = inputs.make(4, n=3_000_001)
+    x, dy = to_dev(w.xs[0]), to_dev(w.dys[0])
+    a = [mea.swish_fwd(x, w.alpha) for _ in range(3)]
+    b = [mea.swish_bwd(x, dy, w.alpha) for _ in range(3)]
+    torch.cuda.synchronize()
+    for t in a[1:]:
+        assert torch.equal(t.view(torch.int32), a[0].view(torch.int32))
+    for t in b[1:]:
+        assert torch.equal(t.view(torch.int32), b[0].view(torch.int32))
+
+
+def test_alias_rejected_with_real_buffers():
+    buf = torch.zeros(8192, device="cuda", dtype=torch.float32)
+    x = buf[0:4096]
+    with pytest.raises(mea.MeswishError) as e:
+        mea.swish_fwd(x, 1.0, out=buf[16:4112])
+    assert e.value.status == _lib.EALIAS
+    with pytest.raises(mea.MeswishError) as e:
+        mea.swish_bwd(x, buf[4096:8192], 1.0, out=buf[4000:8096])
+    assert e.value.status == _lib.EALIAS
+    # Group: output of tensor 0 is the input of tensor 1.
+    with pytest.raises(mea.MeswishError) as e:
+        mea.swish_fwd_grouped([buf[0:1024], buf[1024:2048]], 1.0,
+                              outs=[buf[1024:2048], buf[4096:5120]])
+    assert e.value.status == _lib.EALIAS
+    torch.cuda.synchronize()
+    assert float(buf.abs().sum()) == 0.0  # nothing was launched
+
+
+def test_grouped_limits_and_chunking(oracle):
+    lib = _lib.library()
+    d = (_lib.FwdDesc * 65)()
+    assert lib.swish_fwd_grouped(d, 65, 1.0, _lib.F32, None) == _lib.ETOOMANY
+    rng = np.random.default_rng(9)
+    host = [inputs.encode(rng.standard_normal(int(n)) * 3, "bf16")
+            for n in rng.integers(0, 3000, 150)]
+    xs = [to_dev(h) for h in host]
+    ys = mea.swish_fwd_grouped(xs, 0.75)       # three launches of <= 64 tensors
+    torch.cuda.synchronize()
+    for h, y in zip(host, ys):
+        r = bf16_report(to_host(y), oracle.fwd(h, 0.75))
+        assert r["ok"], r
+
+
+def test_grouped_equals_single_mixed(oracle):
+    """Aligned, misaligned and empty tensors in one group, both dtypes."""
+    rng = np.random.default_rng(21)
+    for dtype in ("f32", "bf16"):
+        big = to_dev(inputs.encode(rng.standard_normal(300000) * 5, dtype))
+        dbig = to_dev(inputs.encode(rng.standard_normal(300000), dtype))
+        cuts = [(0, 100000), (100001, 100001), (100003, 170000), (170000, 170005),
+                (170007, 299999)]
+        xs = [big[a:b] for a, b in cuts]
+        dys = [dbig[a:b] for a, b in cuts]
+        ys = mea.swish_fwd_grouped(xs, -0.6)
+        dxs = mea.swish_bwd_grouped(xs, dys, -0.6)
+        y1 = [mea.swish_fwd(x, -0.6) for x in xs]
+        d1 = [mea.swish_bwd(x, d, -0.6) for x, d in zip(xs, dys)]
+        torch.cuda.synchronize()
+        iv = torch.int16 if dtype == "bf16" else torch.int32
+        for a, b in zip(ys + dxs, y1 + d1):
+            assert torch.equal(a.view(iv), b.view(iv))
+        for (a, b), y in zip(cuts, ys):
+            xh = to_host(big[a:b])
+            r = (bf16_report if dtype == "bf16" else f32_report)(to_host(y), oracle.fwd(xh, -0.6))
+            assert r["ok"], r
+
+
+def test_runs_on_a_side_stream(oracle):
+    w = inputs.make(3, n=1 << 21)
+    x, dy = to_dev(w.xs[0]), to_dev(w.dys[0])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        y = mea.swish_fwd(x, 1.0)
+        dx = mea.swish_bwd(x, dy, 1.0)
+    s.synchronize()
+    assert bf16_report(to_host(y), oracle.fwd(w.xs[0], 1.0, threads=ORACLE_THREADS))["ok"]
+    assert bf16_report(to_host(dx), oracle.bwd(w.xs[0], w.dys[0], 1.0, threads=ORACLE_THREADS,
+                                               want_scale=False)[0])["ok"]
+
+
+def test_one_hip_runtime_and_in_tree_library():
+    mea.swish_fwd(torch.ones(8, device="cuda"), 1.0)
+    torch.cuda.synchronize()
+    with open("/proc/self/maps") as f:
+        maps = f.read()
+    hip = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(hip) == 1, hip
+    libs = {os.path.realpath(line.split()[-1]) for line in maps.splitlines()
+            if "libmeswish" in line}
+    assert libs == {os.path.realpath(_lib.LIBRARY)}, libs
