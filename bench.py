@@ -10,19 +10,20 @@ One step = one forward launch (read x, write y) + one backward launch (read
 x and dy, write dx) through the C ABI of libmeswish.  Algorithmic bytes per
 step = 2 b n + 3 b n = 671,088,640 B (b = 2).  The timed region is K steps
 back to back between two device synchronisations; ``value`` is algorithmic
-bytes over wall time, in decimal GB/s.
+bytes over wall time, in decimal GB/s.  Four copies of the buffers are used
+in rotation so that no kernel can read its inputs from the 256 MB Infinity
+Cache: every counted byte crosses the HBM interface.
 
 Also reported (one JSON line on stdout):
   roofline      the dominant kernel (the backward): algorithmic bytes per
-                launch / mean launch time from HIP events recorded on the
-                launch stream inside the timed region, against 8 TB/s;
+                launch / mean launch time, from HIP events on the launch
+                stream around K back-to-back backward launches (same
+                rotation), against 8 TB/s;
                 ``traffic`` = HBM bytes per launch from rocprofv3 counters
                 (profiles/), or null if the kernel source changed since.
   cpu_baseline  the CPU oracle (binary64 C, all host cores) on the same
                 workload, same algorithmic bytes.
-  copy_ceiling  a plain 16-byte copy kernel over the same bytes.
-  cold_cache    forward and backward timed one by one after writing 1 GiB
-                (4x the 256 MB Infinity Cache), per launch.
+  copy_ceiling  a plain 16-byte copy kernel (read one tensor, write one).
   bytes_retained  bytes kept for the backward: x only, vs 3 maps (naive).
 """
 
@@ -44,6 +45,7 @@ if ROOT not in sys.path:
 METRIC = "HBM GB/s + fraction of peak, Swish fwd+bwd, 67M-elem bf16, 1 MI355X"
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD public specification
 KERNEL_SOURCE = os.path.join(ROOT, "memory_efficient_activation_amd", "csrc", "meswish.hip")
+SETS = 4
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "swish_bwd_bf16_8x2048x4096_traffic.md")
 
 
@@ -59,7 +61,7 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the CPU oracle timing (profiling runs)")
     p.add_argument("--no-extras", action="store_true",
-                   help="skip the copy ceiling and cold-cache measurements (profiling runs)")
+                   help="skip the copy-ceiling measurement")
     p.add_argument("--cpu-reps", type=int, default=3)
     return p.parse_args()
 
@@ -113,57 +115,70 @@ def main():
     def to_dev(a):
         return torch.from_numpy(a).view(torch.int16).view(torch.bfloat16).to(dev)
 
-    x = to_dev(w.xs[0])
-    dy = to_dev(w.dys[0])
-    y = torch.empty_like(x)
-    dx = torch.empty_like(x)
+    # SETS copies of (x, dy, y, dx).  Kernel number k (forward and backward
+    # alternate) uses set k % SETS, so no kernel reads memory that any of
+    # the previous SETS - 1 kernels touched (>= 800 MB of traffic, three
+    # times the 256 MB Infinity Cache): every input byte comes from HBM.
+    x0, dy0 = to_dev(w.xs[0]), to_dev(w.dys[0])
+    bufs = []
+    for _ in range(SETS):
+        xs, dys = x0.clone(), dy0.clone()
+        bufs.append((xs, dys, torch.empty_like(xs), torch.empty_like(xs)))
+    del x0, dy0
+    ptrs = [tuple(t.data_ptr() for t in b) for b in bufs]
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
-    xp, dyp, yp, dxp = x.data_ptr(), dy.data_ptr(), y.data_ptr(), dx.data_ptr()
     code = _lib.BF16
 
     fwd_b = accounting.fwd_bytes(n, dtype)
     bwd_b = accounting.bwd_bytes(n, dtype)
     step_b = fwd_b + bwd_b
 
-    def fwd():
+    def fwd(j):
+        xp, _, yp, _ = ptrs[j % SETS]
         _lib.check(lib.swish_fwd(xp, yp, n, alpha, code, sh), "swish_fwd")
 
-    def bwd():
+    def bwd(j):
+        xp, dyp, _, dxp = ptrs[j % SETS]
         _lib.check(lib.swish_bwd(xp, dyp, dxp, n, alpha, code, sh), "swish_bwd")
 
-    for _ in range(args.warmup):
-        fwd()
-        bwd()
+    def step(i):
+        fwd(2 * i)
+        bwd(2 * i + 1)
+
+    def region(fn, count):
+        """count calls of fn(i) between two events on the launch stream."""
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        a.record(stream)
+        for i in range(count):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, a.elapsed_time(b)
+
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for i in range(K):
-        ev[i][0].record(stream)
-        fwd()
-        ev[i][1].record(stream)
-        bwd()
-        ev[i][2].record(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = start.elapsed_time(end)
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    bwd_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    wall, gpu_ms = region(step, K)
     log(f"[bench] timed {K} steps: wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms")
+
+    # Per-kernel launch durations: each kernel alone, back to back on the
+    # rotating sets, between two events on the launch stream.
+    _, bwd_total = region(bwd, K)
+    _, fwd_total = region(fwd, K)
+    bwd_us = bwd_total * 1e3 / K
+    fwd_us = fwd_total * 1e3 / K
+    bwd_gbps = bwd_b / (bwd_us * 1e-6) / 1e9
+    fwd_gbps = fwd_b / (fwd_us * 1e-6) / 1e9
 
     ms_per_step = wall * 1e3 / K
     value = step_b * K / wall / 1e9
-    fwd_mean, bwd_mean = statistics.fmean(fwd_ms), statistics.fmean(bwd_ms)
-    fwd_gbps = fwd_b / (fwd_mean * 1e-3) / 1e9
-    bwd_gbps = bwd_b / (bwd_mean * 1e-3) / 1e9
     traffic, traffic_note = traffic_from_profile()
 
     result = {
@@ -182,58 +197,37 @@ def main():
         "data": "synthetic",
         "config": {"workload": "swish fwd+bwd, bf16 [8,2048,4096] (67,108,864 elements), alpha=1.0",
                    "n": n, "alpha": alpha, "bytes_per_step": step_b,
-                   "x": "N(0,1) seed 0", "dy": "0.01*N(0,1) seed 1"},
+                   "x": "N(0,1) seed 0", "dy": "0.01*N(0,1) seed 1",
+                   "buffer_sets": SETS},
         "frac_peak": round(value / PEAK_HBM_GBPS, 4),
         "elements_per_s": round(n * K / wall, 1),
         "gpu_ms_per_step_events": round(gpu_ms / K, 5),
-        "fwd": {"bytes": fwd_b, "mean_us": round(fwd_mean * 1e3, 2),
-                "median_us": round(statistics.median(fwd_ms) * 1e3, 2), "GBps": round(fwd_gbps, 1)},
-        "bwd": {"bytes": bwd_b, "mean_us": round(bwd_mean * 1e3, 2),
-                "median_us": round(statistics.median(bwd_ms) * 1e3, 2), "GBps": round(bwd_gbps, 1)},
+        "fwd": {"bytes": fwd_b, "mean_us": round(fwd_us, 2), "GBps": round(fwd_gbps, 1)},
+        "bwd": {"bytes": bwd_b, "mean_us": round(bwd_us, 2), "GBps": round(bwd_gbps, 1)},
         "roofline": {"kernel": "swish_vec_kernel<bf16, bwd>", "bound": "hbm",
                      "achieved": round(bwd_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(bwd_gbps / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "traffic_note": traffic_note,
-                     "bytes_per_launch": bwd_b, "mean_launch_us": round(bwd_mean * 1e3, 2)},
+                     "bytes_per_launch": bwd_b, "mean_launch_us": round(bwd_us, 2)},
         "bytes_retained": {"memory_efficient": accounting.retained_bytes(n, dtype),
                            "naive_3_maps": accounting.retained_bytes(n, dtype, naive=True)},
     }
 
     if not args.no_extras:
-        # Plain copy over the same bytes as one x -> y pass.
-        for _ in range(5):
+        # Plain 16-byte copy of one tensor (read b n, write b n), same rotation.
+        def copy(j):
+            xp, _, yp, _ = ptrs[j % SETS]
             _lib.check(lib.meswish_copy(xp, yp, 2 * n, sh), "meswish_copy")
-        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(50)]
-        for e in cev:
-            e[0].record(stream)
-            _lib.check(lib.meswish_copy(xp, yp, 2 * n, sh), "meswish_copy")
-            e[1].record(stream)
-        torch.cuda.synchronize()
-        cms = statistics.fmean(e[0].elapsed_time(e[1]) for e in cev)
-        copy_gbps = 2 * (2 * n) / (cms * 1e-3) / 1e9
-        result["copy_ceiling"] = {"bytes": 4 * n, "mean_us": round(cms * 1e3, 2),
+        for i in range(5):
+            copy(i)
+        _, cms = region(copy, K)
+        copy_us = cms * 1e3 / K
+        copy_gbps = 2 * (2 * n) / (copy_us * 1e-6) / 1e9
+        result["copy_ceiling"] = {"bytes": 4 * n, "mean_us": round(copy_us, 2),
                                   "GBps": round(copy_gbps, 1),
                                   "bwd_frac_of_copy": round(bwd_gbps / copy_gbps, 4),
                                   "value_frac_of_copy": round(value / copy_gbps, 4)}
-        # Cold cache: each launch after writing 1 GiB.
-        scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        cold = {"fwd": [], "bwd": []}
-        for _ in range(20):
-            for name, fn in (("fwd", fwd), ("bwd", bwd)):
-                scrub.fill_(1)
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                fn()
-                b.record(stream)
-                torch.cuda.synchronize()
-                cold[name].append(a.elapsed_time(b))
-        del scrub
-        cf, cb = statistics.median(cold["fwd"]), statistics.median(cold["bwd"])
-        result["cold_cache"] = {"fwd_median_us": round(cf * 1e3, 2), "bwd_median_us": round(cb * 1e3, 2),
-                                "fwd_GBps": round(fwd_b / (cf * 1e-3) / 1e9, 1),
-                                "bwd_GBps": round(bwd_b / (cb * 1e-3) / 1e9, 1),
-                                "step_GBps": round(step_b / ((cf + cb) * 1e-3) / 1e9, 1)}
-        log(f"[bench] extras done: copy {copy_gbps:.0f} GB/s")
+        log(f"[bench] copy ceiling {copy_gbps:.0f} GB/s")
 
     if not args.no_cpu_baseline:
         import oracle

@@ -17,17 +17,22 @@
 //     atomics, no barriers.  Each lane moves 16-byte vectors (4 binary32 or
 //     8 bfloat16), a wave touches 1 KiB contiguous per access, and a thread
 //     issues all its loads of an iteration before any arithmetic.
-//   * Grid-stride over tiles of kBlock * kUnroll vectors; the grid is sized
-//     to the device's compute units (256 on MI355X, 8 XCDs).
+//   * One tile of kBlock x kUnroll vectors per block, one block
+//     per tile (the dispatcher keeps all 256 CUs of the 8 XCDs busy and
+//     balances the tail); the loop over tiles only matters when the grid
+//     is capped.  Tile shape and cache policy (non-temporal loads/stores
+//     per stream) were chosen by measurement on MI355X.
 //   * Arithmetic is binary32 with the hardware exp2 and reciprocal
-//     (v_exp_f32, v_rcp_f32).  The sigmoid is evaluated as
-//     e = 2^(-|t| log2 e) <= 1, p = 1/(1+e), q = e p, s = p (t >= 0) or q,
-//     1 - s = q (t >= 0) or p, so nothing overflows and 1 - s never cancels.
-//   * binary32 I/O: the exponent -|alpha x| log2 e is carried as a hi+lo
-//     pair so the exponential keeps binary32 accuracy at |alpha x| ~ 90.
-//   * e below the binary32 normal range (|alpha x| > 87.3) takes a rare
-//     branch that scales by powers of two (frexp/ldexp) so that subnormal
-//     results round once and keep gradual underflow (the hardware
+//     (v_exp_f32, v_rcp_f32): E = e^-t = 2^(-t log2 e), s = 1 / (1 + E),
+//     1 - s = E s.  Both s and 1 - s come out with small relative error for
+//     every t (no cancellation), the forward costs one exp, one reciprocal
+//     and three multiply/adds per element, and the backward four more.
+//   * binary32 I/O: the exponent -alpha x log2 e is carried as a hi+lo pair
+//     so that E keeps binary32 accuracy up to |alpha x| ~ 87.
+//   * |alpha x| > 86.6 (E outside [2^-125, 2^125]) takes a rare branch:
+//     there s or 1 - s rounds to exactly 1, and the small factor
+//     e^-|alpha x| is applied by powers of two (frexp/ldexp) so that
+//     subnormal results round once and keep gradual underflow (the hardware
 //     transcendentals flush subnormals).
 //   * bfloat16 I/O: widening is a 16-bit shift; narrowing is the gfx950
 //     v_cvt_pk_bf16_f32 (round to nearest even), two elements per op.
@@ -42,27 +47,68 @@
 
 #include "meswish.h"
 
-#ifndef MESWISH_BLOCK
-#define MESWISH_BLOCK 256
+// Threads per block, per element type.
+#ifndef MESWISH_BLOCK_BF16
+#define MESWISH_BLOCK_BF16 256
 #endif
-#ifndef MESWISH_UNROLL
-#define MESWISH_UNROLL 4
+#ifndef MESWISH_BLOCK_F32
+#define MESWISH_BLOCK_F32 64
+#endif
+// 16-byte vectors per thread and stream, per element type.
+#ifndef MESWISH_UNROLL_BF16
+#define MESWISH_UNROLL_BF16 1
+#endif
+#ifndef MESWISH_UNROLL_F32
+#define MESWISH_UNROLL_F32 1
 #endif
 #ifndef MESWISH_BLOCKS_PER_CU
-#define MESWISH_BLOCKS_PER_CU 8
+#define MESWISH_BLOCKS_PER_CU 100000
 #endif
-#ifndef MESWISH_NT_LOAD
-#define MESWISH_NT_LOAD 0
+// Remap block ids so that the blocks one XCD receives (the dispatcher deals
+// blocks to the 8 XCDs round-robin) work on adjacent tiles.
+#ifndef MESWISH_XCD_SWIZZLE
+#define MESWISH_XCD_SWIZZLE 0
 #endif
-#ifndef MESWISH_NT_STORE
-#define MESWISH_NT_STORE 0
+// Minimum waves per SIMD the compiler must allow (caps VGPRs); 0 = no cap.
+#ifndef MESWISH_MIN_WAVES
+#define MESWISH_MIN_WAVES 0
+#endif
+#if MESWISH_MIN_WAVES > 0
+#define MESWISH_BOUNDS __launch_bounds__(Io<IO>::kBlock, MESWISH_MIN_WAVES)
+#else
+#define MESWISH_BOUNDS __launch_bounds__(Io<IO>::kBlock)
+#endif
+#define MESWISH_COPY_BOUNDS __launch_bounds__(MESWISH_COPY_BLOCK)
+// Non-temporal (streaming) cache policy per stream, as bit masks:
+// 1 = loads of x, 2 = loads of dy, 4 = stores of the result; chosen per
+// direction and element type by measurement.
+#ifndef MESWISH_NT_FWD_BF16
+#define MESWISH_NT_FWD_BF16 5
+#endif
+#ifndef MESWISH_NT_BWD_BF16
+#define MESWISH_NT_BWD_BF16 6
+#endif
+#ifndef MESWISH_NT_FWD_F32
+#define MESWISH_NT_FWD_F32 5
+#endif
+#ifndef MESWISH_NT_BWD_F32
+#define MESWISH_NT_BWD_F32 7
+#endif
+#ifndef MESWISH_NT_COPY
+#define MESWISH_NT_COPY 5
+#endif
+#ifndef MESWISH_COPY_BLOCK
+#define MESWISH_COPY_BLOCK 64
+#endif
+#ifndef MESWISH_COPY_UNROLL
+#define MESWISH_COPY_UNROLL 1
 #endif
 
 namespace meswish {
 
-constexpr int kBlock = MESWISH_BLOCK;
-constexpr int kUnroll = MESWISH_UNROLL;
-constexpr int kTileVecs = kBlock * kUnroll;  // 16-byte vectors per tile
+constexpr int kCopyBlock = MESWISH_COPY_BLOCK;
+constexpr int kCopyUnroll = MESWISH_COPY_UNROLL;
+constexpr int kCopyTileVecs = kCopyBlock * kCopyUnroll;
 
 // ---------------------------------------------------------------------------
 // Coefficients prepared on the host.
@@ -70,20 +116,20 @@ constexpr int kTileVecs = kBlock * kUnroll;  // 16-byte vectors per tile
 
 struct Coef {
     float alpha;      // alpha
-    float cn_hi;      // binary32 nearest to -|alpha| log2(e)
-    float cn_lo_ln2;  // (-|alpha| log2(e) - cn_hi) * ln 2
+    float c_hi;       // binary32 nearest to -alpha log2(e)
+    float c_lo_ln2;   // (-alpha log2(e) - c_hi) * ln 2
 };
 
 static Coef make_coef(float alpha)
 {
     const double log2e = 1.44269504088896340735992468100189214;
     const double ln2 = 0.693147180559945309417232121458176568;
-    double c = -fabs((double)alpha) * log2e;
+    double c = -(double)alpha * log2e;
     float hi = (float)c;
     Coef k;
     k.alpha = alpha;
-    k.cn_hi = hi;
-    k.cn_lo_ln2 = (float)((c - (double)hi) * ln2);
+    k.c_hi = hi;
+    k.c_lo_ln2 = (float)((c - (double)hi) * ln2);
     return k;
 }
 
@@ -92,106 +138,105 @@ static Coef make_coef(float alpha)
 // ---------------------------------------------------------------------------
 
 constexpr float kLn2f = 0.693147180559945309f;
-// Below this exponent 2^v is no longer a binary32 normal number.
-constexpr float kMinNormalExp = -126.0f;
-// Below this exponent every result of the scaled branch rounds to zero:
-// |x| < 2^128 and 2^-300 * 2^128 < 2^-150.
+// |exponent| above which E = 2^v leaves [2^-125, 2^125]: then the rare
+// branch takes over (|alpha x| > 86.6).
+constexpr float kMaxExp = 125.0f;
+// Below this base-2 exponent every result of the rare branch rounds to zero:
+// |x|, |dy| < 2^128, |1 + t| < 2^9 and 2^(128 + 9 + 1 - 300) < 2^-150.
 constexpr float kZeroExp = -300.0f;
 
 __device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2f(v); }
 __device__ __forceinline__ float rcp_hw(float v) { return __builtin_amdgcn_rcpf(v); }
 
-// e = exp(-|alpha x|) for exponents in the normal range.  vh receives the
-// (hi part of the) base-2 exponent, used to detect the out-of-range case.
+// E = e^(-alpha x) = 2^v, v = x * (-alpha log2 e).  With kPrecise the
+// rounding error of v (and of the binary32 coefficient) is carried as
+// w = (exact v - v) ln 2 and applied as E (1 + w).  The caller flags
+// |v| > kMaxExp for the rare branch.
 template <bool kPrecise>
-__device__ __forceinline__ float neg_exp(float x, const Coef& k, float& vh)
+__device__ __forceinline__ float exp_neg_t(float x, const Coef& k, float& v)
 {
-    float ax = fabsf(x);
-    vh = ax * k.cn_hi;
-    float e = exp2_hw(vh);
+    v = x * k.c_hi;
+    float e = exp2_hw(v);
     if (kPrecise) {
-        float err = fmaf(ax, k.cn_hi, -vh);           // exact error of vh
-        float w = fmaf(ax, k.cn_lo_ln2, err * kLn2f);  // rest of exponent, times ln 2
-        e = fmaf(e, w, e);                             // 2^vh * (1 + w)
+        float err = fmaf(x, k.c_hi, -v);               // exact error of v
+        float w = fmaf(x, k.c_lo_ln2, err * kLn2f);     // rest of the exponent, times ln 2
+        e = fmaf(e, w, e);
     }
     return e;
 }
 
 template <bool kPrecise>
-__device__ __forceinline__ float fwd_fast(float x, const Coef& k, bool& scaled)
+__device__ __forceinline__ float fwd_fast(float x, const Coef& k, bool& rare)
 {
-    float vh;
-    float e = neg_exp<kPrecise>(x, k, vh);
-    float p = rcp_hw(1.0f + e);
-    float q = e * p;
-    float s = (k.alpha * x >= 0.0f) ? p : q;
-    scaled |= vh < kMinNormalExp;
+    float v;
+    float e = exp_neg_t<kPrecise>(x, k, v);
+    float s = rcp_hw(1.0f + e);  // Sigmoid(alpha x)
+    rare |= fabsf(v) > kMaxExp;
     return x * s;
 }
 
 template <bool kPrecise>
-__device__ __forceinline__ float bwd_fast(float x, float dy, const Coef& k, bool& scaled)
+__device__ __forceinline__ float bwd_fast(float x, float dy, const Coef& k, bool& rare)
 {
-    float vh;
-    float e = neg_exp<kPrecise>(x, k, vh);
-    float p = rcp_hw(1.0f + e);
-    float q = e * p;
-    float t = k.alpha * x;
-    bool pos = t >= 0.0f;
-    float s = pos ? p : q;
-    float c = pos ? q : p;  // 1 - s
-    float g = fmaf(t, c, 1.0f);
-    scaled |= vh < kMinNormalExp;
+    float v;
+    float e = exp_neg_t<kPrecise>(x, k, v);
+    float s = rcp_hw(1.0f + e);  // Sigmoid(t)
+    float c = e * s;             // 1 - Sigmoid(t), without cancellation
+    float g = fmaf(k.alpha * x, c, 1.0f);
+    rare |= fabsf(v) > kMaxExp;
     return dy * (s * g);
 }
 
-__device__ __forceinline__ bool needs_scaling(float x, const Coef& k)
+__device__ __forceinline__ bool is_rare(float x, const Coef& k)
 {
-    return fabsf(x) * k.cn_hi < kMinNormalExp;
+    return fabsf(x * k.c_hi) > kMaxExp;
 }
 
-// The branch for e = exp(-|t|) < 2^-126.  There p = 1/(1+e) rounds to 1.
-// For t >= 0, s rounds to 1 and y = x.  For t < 0, s = e = ef * 2^kf with
-// ef in [1, 2], and the result is assembled as mantissa * 2^exponent so that
-// it is rounded once, at the end, even when it is subnormal.
-__device__ __forceinline__ float fwd_scaled(float x, Coef k)
+// The rare branch, |t| > 86.6 with t = alpha x.  For t > 0, Sigmoid(t)
+// rounds to 1 and t (1 - Sigmoid(t)) to 0: y = x and dx = dy.  For t < 0,
+// 1 - Sigmoid(t) rounds to 1 and Sigmoid(t) = e^t = ef * 2^kf with ef in
+// [1, 2]: the result is assembled as (mantissa product) * 2^(exponents) so
+// that it is rounded once, at the end, even when it is subnormal.
+__device__ __forceinline__ void small_sigmoid(float x, const Coef& k, float& ef, int& kf)
+{
+    float v = x * k.c_hi;                          // = |t| log2 e here
+    float err = fmaf(x, k.c_hi, -v);
+    float w = fmaf(x, k.c_lo_ln2, err * kLn2f);    // e^t = 2^(-v) (1 - w)
+    float vh = -v;
+    float f = floorf(vh);
+    ef = exp2_hw(vh - f);
+    ef = fmaf(ef, -w, ef);
+    kf = (int)f;
+}
+
+__device__ __forceinline__ float fwd_rare(float x, const Coef& k)
 {
     if (k.alpha * x >= 0.0f)
         return x;
-    float ax = fabsf(x);
-    float vh = ax * k.cn_hi;
-    if (vh < kZeroExp)
+    if (-(x * k.c_hi) < kZeroExp)
         return x * 0.0f;
-    float err = fmaf(ax, k.cn_hi, -vh);
-    float w = fmaf(ax, k.cn_lo_ln2, err * kLn2f);
-    float kf = floorf(vh);
-    float ef = exp2_hw(vh - kf);
-    ef = fmaf(ef, w, ef);
+    float ef;
+    int kf;
+    small_sigmoid(x, k, ef, kf);
     int ex;
     float mx = frexpf(x, &ex);
-    return ldexpf(mx * ef, ex + (int)kf);
+    return ldexpf(mx * ef, ex + kf);
 }
 
-// Same branch for the backward: for t >= 0, dx = dy; for t < 0,
-// 1 - s rounds to 1 and dx = dy * e * (1 + t).
-__device__ __forceinline__ float bwd_scaled(float x, float dy, Coef k)
+__device__ __forceinline__ float bwd_rare(float x, float dy, const Coef& k)
 {
     float t = k.alpha * x;
     if (t >= 0.0f)
         return dy;
-    float ax = fabsf(x);
-    float vh = ax * k.cn_hi;
-    if (vh < kZeroExp)
+    if (-(x * k.c_hi) < kZeroExp)
         return dy * -0.0f;
-    float err = fmaf(ax, k.cn_hi, -vh);
-    float w = fmaf(ax, k.cn_lo_ln2, err * kLn2f);
-    float kf = floorf(vh);
-    float ef = exp2_hw(vh - kf);
-    ef = fmaf(ef, w, ef);
-    float g = 1.0f + t;
+    float ef;
+    int kf;
+    small_sigmoid(x, k, ef, kf);
+    float g = 1.0f + t;  // 1 + t (1 - s) with 1 - s rounding to 1
     int ed;
     float md = frexpf(dy, &ed);
-    return ldexpf(md * ef * g, ed + (int)kf);
+    return ldexpf(md * ef * g, ed + kf);
 }
 
 // ---------------------------------------------------------------------------
@@ -221,6 +266,8 @@ template <typename IO> struct Io;
 
 template <> struct Io<float> {
     static constexpr int kPerVec = 4;
+    static constexpr int kUnroll = MESWISH_UNROLL_F32;
+    static constexpr int kBlock = MESWISH_BLOCK_F32;
     static constexpr bool kPrecise = true;
     __device__ static void unpack(const uint4& v, float (&f)[4])
     {
@@ -240,6 +287,8 @@ template <> struct Io<float> {
 
 template <> struct Io<bf16_t> {
     static constexpr int kPerVec = 8;
+    static constexpr int kUnroll = MESWISH_UNROLL_BF16;
+    static constexpr int kBlock = MESWISH_BLOCK_BF16;
     static constexpr bool kPrecise = false;
     __device__ static void unpack(const uint4& v, float (&f)[8])
     {
@@ -263,23 +312,42 @@ template <> struct Io<bf16_t> {
     }
 };
 
+template <typename IO, bool kBwd> struct NtPolicy;
+template <> struct NtPolicy<float, false> { static constexpr int kMask = MESWISH_NT_FWD_F32; };
+template <> struct NtPolicy<float, true> { static constexpr int kMask = MESWISH_NT_BWD_F32; };
+template <> struct NtPolicy<bf16_t, false> { static constexpr int kMask = MESWISH_NT_FWD_BF16; };
+template <> struct NtPolicy<bf16_t, true> { static constexpr int kMask = MESWISH_NT_BWD_BF16; };
+
+// 16-byte vectors per tile (one block's share of work).
+template <typename IO>
+constexpr int tile_vecs() { return Io<IO>::kBlock * Io<IO>::kUnroll; }
+
+typedef uint32_t u32x4_v __attribute__((ext_vector_type(4)));
+
+// 16-byte global load / store; kNT selects the non-temporal (streaming)
+// cache policy.
+template <bool kNT>
 __device__ __forceinline__ uint4 ld16(const uint4* p)
 {
-#if MESWISH_NT_LOAD
-    return __builtin_nontemporal_load(p);
-#else
+    if (kNT) {
+        u32x4_v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_v*>(p));
+        return make_uint4(v.x, v.y, v.z, v.w);
+    }
     return *p;
-#endif
 }
 
+template <bool kNT>
 __device__ __forceinline__ void st16(uint4* p, const uint4& v)
 {
-#if MESWISH_NT_STORE
-    __builtin_nontemporal_store(v, p);
-#else
-    *p = v;
-#endif
+    if (kNT) {
+        u32x4_v w = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4_v*>(p));
+    } else {
+        *p = v;
+    }
 }
+
+constexpr int kNtCopy = MESWISH_NT_COPY;
 
 // One 16-byte vector of the forward / backward.
 template <typename IO>
@@ -288,15 +356,15 @@ __device__ __forceinline__ uint4 fwd_vec(const uint4& xv, const Coef& k)
     constexpr int E = Io<IO>::kPerVec;
     float xf[E], yf[E];
     Io<IO>::unpack(xv, xf);
-    bool scaled = false;
+    bool rare = false;
 #pragma unroll
     for (int j = 0; j < E; ++j)
-        yf[j] = fwd_fast<Io<IO>::kPrecise>(xf[j], k, scaled);
-    if (__builtin_expect(scaled, 0)) {
+        yf[j] = fwd_fast<Io<IO>::kPrecise>(xf[j], k, rare);
+    if (__builtin_expect(rare, 0)) {
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            if (needs_scaling(xf[j], k))
-                yf[j] = fwd_scaled(xf[j], k);
+            if (is_rare(xf[j], k))
+                yf[j] = fwd_rare(xf[j], k);
     }
     return Io<IO>::pack(yf);
 }
@@ -308,15 +376,15 @@ __device__ __forceinline__ uint4 bwd_vec(const uint4& xv, const uint4& dv, const
     float xf[E], df[E], gf[E];
     Io<IO>::unpack(xv, xf);
     Io<IO>::unpack(dv, df);
-    bool scaled = false;
+    bool rare = false;
 #pragma unroll
     for (int j = 0; j < E; ++j)
-        gf[j] = bwd_fast<Io<IO>::kPrecise>(xf[j], df[j], k, scaled);
-    if (__builtin_expect(scaled, 0)) {
+        gf[j] = bwd_fast<Io<IO>::kPrecise>(xf[j], df[j], k, rare);
+    if (__builtin_expect(rare, 0)) {
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            if (needs_scaling(xf[j], k))
-                gf[j] = bwd_scaled(xf[j], df[j], k);
+            if (is_rare(xf[j], k))
+                gf[j] = bwd_rare(xf[j], df[j], k);
     }
     return Io<IO>::pack(gf);
 }
@@ -327,57 +395,60 @@ __device__ __forceinline__ void one_element(const IO* x, const IO* dy, IO* out, 
                                             const Coef& k)
 {
     float xv = Io<IO>::load1(x, i);
-    bool scaled = false;
+    bool rare = false;
     float r;
     if (kBwd) {
         float dv = Io<IO>::load1(dy, i);
-        r = bwd_fast<Io<IO>::kPrecise>(xv, dv, k, scaled);
-        if (scaled)
-            r = bwd_scaled(xv, dv, k);
+        r = bwd_fast<Io<IO>::kPrecise>(xv, dv, k, rare);
+        if (rare)
+            r = bwd_rare(xv, dv, k);
     } else {
-        r = fwd_fast<Io<IO>::kPrecise>(xv, k, scaled);
-        if (scaled)
-            r = fwd_scaled(xv, k);
+        r = fwd_fast<Io<IO>::kPrecise>(xv, k, rare);
+        if (rare)
+            r = fwd_rare(xv, k);
     }
     Io<IO>::store1(out, i, r);
 }
 
 // Vectors [v_begin, v_end) of the 16-byte-aligned body starting at x, dy, out
 // (already offset past the head), processed by this block as tiles of
-// kTileVecs vectors with stride `tile_stride` tiles.
-template <typename IO, bool kBwd>
+// tile_vecs<IO>() vectors.
+template <typename IO, bool kBwd, int kNt = NtPolicy<IO, kBwd>::kMask>
 __device__ __forceinline__ void body_tile(const uint4* xv, const uint4* dv, uint4* ov,
                                           int64_t tile_first, int64_t nvec, const Coef& k)
 {
+    constexpr int kUnroll = Io<IO>::kUnroll;
+    constexpr int kBlock = Io<IO>::kBlock;
     int64_t i = tile_first + threadIdx.x;
-    if (tile_first + kTileVecs <= nvec) {
+    if (tile_first + tile_vecs<IO>() <= nvec) {
         uint4 a[kUnroll], b[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            a[u] = ld16(xv + i + u * kBlock);
+            a[u] = ld16<(kNt & 1) != 0>(xv + i + u * kBlock);
         if (kBwd) {
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u)
-                b[u] = ld16(dv + i + u * kBlock);
+                b[u] = ld16<(kNt & 2) != 0>(dv + i + u * kBlock);
         }
         // Keep every load of the tile ahead of the first use of its data, so
         // that a thread has all of them in flight at once.
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            st16(ov + i + u * kBlock, kBwd ? bwd_vec<IO>(a[u], b[u], k) : fwd_vec<IO>(a[u], k));
+            st16<(kNt & 4) != 0>(ov + i + u * kBlock,
+                                  kBwd ? bwd_vec<IO>(a[u], b[u], k) : fwd_vec<IO>(a[u], k));
     } else {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             int64_t j = i + u * kBlock;
             if (j < nvec) {
-                uint4 a = ld16(xv + j);
+                uint4 a = ld16<(kNt & 1) != 0>(xv + j);
                 uint4 r;
                 if (kBwd)
-                    r = bwd_vec<IO>(a, ld16(dv + j), k);
+                    r = bwd_vec<IO>(a, ld16<(kNt & 2) != 0>(dv + j), k);
                 else
                     r = fwd_vec<IO>(a, k);
-                st16(ov + j, r);
+                st16<(kNt & 4) != 0>(ov + j, r);
             }
         }
     }
@@ -390,7 +461,7 @@ __device__ __forceinline__ void body_tile(const uint4* xv, const uint4* dv, uint
 // Single tensor, all pointers congruent modulo 16 bytes: `head` scalar
 // elements, then nvec 16-byte vectors, then `tail` scalar elements.
 template <typename IO, bool kBwd>
-__global__ __launch_bounds__(kBlock) void swish_vec_kernel(const IO* x, const IO* dy, IO* out,
+__global__ MESWISH_BOUNDS void swish_vec_kernel(const IO* x, const IO* dy, IO* out,
                                                            int64_t head, int64_t nvec,
                                                            int64_t tail, Coef k)
 {
@@ -398,8 +469,14 @@ __global__ __launch_bounds__(kBlock) void swish_vec_kernel(const IO* x, const IO
     const uint4* xv = reinterpret_cast<const uint4*>(x + head);
     const uint4* dv = kBwd ? reinterpret_cast<const uint4*>(dy + head) : nullptr;
     uint4* ov = reinterpret_cast<uint4*>(out + head);
+    constexpr int64_t kTileVecs = tile_vecs<IO>();
     const int64_t stride = (int64_t)gridDim.x * kTileVecs;
-    for (int64_t t0 = (int64_t)blockIdx.x * kTileVecs; t0 < nvec; t0 += stride)
+    int64_t b = blockIdx.x;
+#if MESWISH_XCD_SWIZZLE
+    if ((gridDim.x & 7u) == 0)
+        b = (b & 7) * (gridDim.x >> 3) + (b >> 3);
+#endif
+    for (int64_t t0 = b * kTileVecs; t0 < nvec; t0 += stride)
         body_tile<IO, kBwd>(xv, dv, ov, t0, nvec, k);
     if (blockIdx.x == 0 && threadIdx.x < head + tail) {
         int64_t i = threadIdx.x < head ? (int64_t)threadIdx.x
@@ -410,9 +487,10 @@ __global__ __launch_bounds__(kBlock) void swish_vec_kernel(const IO* x, const IO
 
 // Single tensor, element by element (pointers not congruent modulo 16).
 template <typename IO, bool kBwd>
-__global__ __launch_bounds__(kBlock) void swish_elem_kernel(const IO* x, const IO* dy, IO* out,
+__global__ MESWISH_BOUNDS void swish_elem_kernel(const IO* x, const IO* dy, IO* out,
                                                             int64_t n, Coef k)
 {
+    constexpr int kBlock = Io<IO>::kBlock;
     const int64_t stride = (int64_t)gridDim.x * kBlock;
     for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride)
         one_element<IO, kBwd>(x, dy, out, i, k);
@@ -424,7 +502,7 @@ __global__ __launch_bounds__(kBlock) void swish_elem_kernel(const IO* x, const I
 // a forward scan (tiles of one block are increasing, so the scan is
 // amortised O(1)).  The first tile of a tensor also does its scalar head and
 // tail.  A tensor whose pointers are not congruent modulo 16 bytes (flag 0)
-// is processed element by element, kTileVecs elements per tile.
+// is processed element by element, tile_vecs<IO>() elements per tile.
 struct GroupArgs {
     const void* x[MESWISH_MAX_GROUP];
     const void* dy[MESWISH_MAX_GROUP];
@@ -436,9 +514,11 @@ struct GroupArgs {
 };
 
 template <typename IO, bool kBwd>
-__global__ __launch_bounds__(kBlock) void swish_group_kernel(GroupArgs g, Coef k)
+__global__ MESWISH_BOUNDS void swish_group_kernel(GroupArgs g, Coef k)
 {
     constexpr int E = Io<IO>::kPerVec;
+    constexpr int kUnroll = Io<IO>::kUnroll;
+    constexpr int64_t kTileVecs = tile_vecs<IO>();
     const int64_t total = g.tile_begin[g.count];
     int j = 0;
     for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
@@ -454,7 +534,7 @@ __global__ __launch_bounds__(kBlock) void swish_group_kernel(GroupArgs g, Coef k
             int64_t e0 = local * kTileVecs;
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                int64_t i = e0 + u * kBlock + threadIdx.x;
+                int64_t i = e0 + u * Io<IO>::kBlock + threadIdx.x;
                 if (i < n)
                     one_element<IO, kBwd>(x, dy, out, i, k);
             }
@@ -474,25 +554,26 @@ __global__ __launch_bounds__(kBlock) void swish_group_kernel(GroupArgs g, Coef k
 }
 
 // Plain 16-byte copy (measurement helper).
-__global__ __launch_bounds__(kBlock) void copy16_kernel(const uint4* src, uint4* dst, int64_t nvec)
+__global__ MESWISH_COPY_BOUNDS void copy16_kernel(const uint4* src, uint4* dst, int64_t nvec)
 {
-    const int64_t stride = (int64_t)gridDim.x * kTileVecs;
-    for (int64_t t0 = (int64_t)blockIdx.x * kTileVecs; t0 < nvec; t0 += stride) {
+    const int64_t stride = (int64_t)gridDim.x * kCopyTileVecs;
+    for (int64_t t0 = (int64_t)blockIdx.x * kCopyTileVecs; t0 < nvec; t0 += stride) {
         int64_t i = t0 + threadIdx.x;
-        if (t0 + kTileVecs <= nvec) {
-            uint4 a[kUnroll];
+        if (t0 + kCopyTileVecs <= nvec) {
+            uint4 a[kCopyUnroll];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
-                a[u] = ld16(src + i + u * kBlock);
+            for (int u = 0; u < kCopyUnroll; ++u)
+                a[u] = ld16<(kNtCopy & 1) != 0>(src + i + u * kCopyBlock);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
-                st16(dst + i + u * kBlock, a[u]);
+            for (int u = 0; u < kCopyUnroll; ++u)
+                st16<(kNtCopy & 4) != 0>(dst + i + u * kCopyBlock, a[u]);
         } else {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
-                if (i + u * kBlock < nvec)
-                    st16(dst + i + u * kBlock, ld16(src + i + u * kBlock));
+            for (int u = 0; u < kCopyUnroll; ++u)
+                if (i + u * kCopyBlock < nvec)
+                    st16<(kNtCopy & 4) != 0>(dst + i + u * kCopyBlock,
+                                               ld16<(kNtCopy & 1) != 0>(src + i + u * kCopyBlock));
         }
     }
 }
@@ -550,9 +631,9 @@ static bool alias_ok(const void* out, const void* in, size_t bytes)
     return out == in || !overlaps(out, bytes, in, bytes);
 }
 
-static int launch(const void* fn, int64_t grid, void** args, hipStream_t stream)
+static int launch(const void* fn, int64_t grid, void** args, hipStream_t stream, int block)
 {
-    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kBlock), args, 0, stream);
+    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(block), args, 0, stream);
     return e == hipSuccess ? MESWISH_OK : MESWISH_EHIP;
 }
 
@@ -579,21 +660,25 @@ static int run_single(const void* x, const void* dy, void* out, size_t n, Coef k
             head = (int64_t)n;
         int64_t nvec = ((int64_t)n - head) / E;
         int64_t tail = (int64_t)n - head - nvec * E;
+        constexpr int64_t kTileVecs = tile_vecs<IO>();
         int64_t grid = grid_for_tiles((nvec + kTileVecs - 1) / kTileVecs);
         void* args[] = {&xp, &dp, &op, &head, &nvec, &tail, &k};
         return launch(reinterpret_cast<const void*>(&swish_vec_kernel<IO, kBwd>), grid, args,
-                      stream);
+                      stream, Io<IO>::kBlock);
     }
     int64_t nn = (int64_t)n;
-    int64_t grid = grid_for_tiles((nn + kBlock * kUnroll - 1) / (kBlock * kUnroll));
+    constexpr int64_t kTile = tile_vecs<IO>();
+    int64_t grid = grid_for_tiles((nn + kTile - 1) / kTile);
     void* args[] = {&xp, &dp, &op, &nn, &k};
-    return launch(reinterpret_cast<const void*>(&swish_elem_kernel<IO, kBwd>), grid, args, stream);
+    return launch(reinterpret_cast<const void*>(&swish_elem_kernel<IO, kBwd>), grid, args, stream,
+                  Io<IO>::kBlock);
 }
 
 template <typename IO, bool kBwd>
 static int run_group(GroupArgs& g, Coef k, hipStream_t stream)
 {
     constexpr int E = Io<IO>::kPerVec;
+    constexpr int64_t kTileVecs = tile_vecs<IO>();
     int64_t tiles = 0;
     for (int j = 0; j < g.count; ++j) {
         g.tile_begin[j] = tiles;
@@ -625,7 +710,7 @@ static int run_group(GroupArgs& g, Coef k, hipStream_t stream)
     int64_t grid = grid_for_tiles(tiles);
     void* args[] = {&g, &k};
     return launch(reinterpret_cast<const void*>(&swish_group_kernel<IO, kBwd>), grid, args,
-                  stream);
+                  stream, Io<IO>::kBlock);
 }
 
 // Common argument checks.  Returns MESWISH_OK or an error code.
@@ -813,10 +898,10 @@ extern "C" int meswish_copy(const void* src, void* dst, size_t bytes, void* stre
     const uint4* s = static_cast<const uint4*>(src);
     uint4* d = static_cast<uint4*>(dst);
     int64_t nvec = (int64_t)(bytes / 16);
-    int64_t grid = grid_for_tiles((nvec + kTileVecs - 1) / kTileVecs);
+    int64_t grid = grid_for_tiles((nvec + kCopyTileVecs - 1) / kCopyTileVecs);
     void* args[] = {&s, &d, &nvec};
     return launch(reinterpret_cast<const void*>(&copy16_kernel), grid, args,
-                  static_cast<hipStream_t>(stream));
+                  static_cast<hipStream_t>(stream), kCopyBlock);
 }
 
 extern "C" const char* meswish_strerror(int status)

@@ -1,0 +1,139 @@
+"""Summarise rocprofv3 CSV output of bench.py into short markdown tables.
+
+Usage (after the rocprofv3 runs listed in each summary's header):
+
+    python -m memory_efficient_activation_amd.rocprof_summary trace DIR
+    python -m memory_efficient_activation_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR
+
+``trace``   reads ``*_kernel_stats.csv`` and ``*_kernel_trace.csv`` from a
+            ``--kernel-trace --stats --output-format csv`` run and prints the
+            per-kernel averages, plus the per-region averages of bench.py's
+            three timed regions (alternating steps, backward only, forward
+            only).
+``traffic`` reads ``*_counter_collection.csv`` of one ``--pmc FETCH_SIZE``
+            run and one ``--pmc WRITE_SIZE`` run, calibrates each counter on
+            the plain copy kernel (which reads and writes exactly
+            ``bytes`` = 2 b n per launch), and prints the HBM bytes per
+            launch of the forward and backward kernels next to their
+            algorithmic bytes, with the sha256 of the kernel source.
+"""
+
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import os
+import statistics
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "csrc", "meswish.hip")
+
+N = 8 * 2048 * 4096          # elements of the benchmark tensor
+BF16 = 2                     # bytes per element
+COPY_BYTES = BF16 * N        # bytes the copy kernel reads (and writes) per launch
+ALGO = {"fwd": 2 * BF16 * N, "bwd": 3 * BF16 * N, "copy": 2 * BF16 * N}
+
+
+def kind(name: str) -> str:
+    if "swish_vec_kernel" in name:
+        return "bwd" if ", true>" in name else "fwd"
+    if "copy16_kernel" in name:
+        return "copy"
+    return "other"
+
+
+def _one(pattern: str) -> str:
+    hits = glob.glob(pattern)
+    if len(hits) != 1:
+        raise SystemExit(f"expected one file matching {pattern}, found {hits}")
+    return hits[0]
+
+
+def trace(d: str) -> str:
+    stats = list(csv.DictReader(open(_one(os.path.join(d, "*_kernel_stats.csv")))))
+    rows = list(csv.DictReader(open(_one(os.path.join(d, "*_kernel_trace.csv")))))
+    out = ["| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+    for r in stats:
+        out.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    seq = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), kind(r["Kernel_Name"]))
+                 for r in rows)
+    runs, cur = [], None
+    for i, (_, _, k) in enumerate(seq):
+        if cur and cur[0] == k:
+            cur[2] = i
+        else:
+            if cur:
+                runs.append(cur)
+            cur = [k, i, i]
+    if cur:
+        runs.append(cur)
+    out += ["", "| region (consecutive launches) | launches | mean kernel time (us) | "
+                "algorithmic GB/s |", "|---|---|---|---|"]
+    alt = [r for r in seq if r[2] in ("fwd", "bwd")]
+    # The alternating region is the longest run of fwd/bwd pairs.
+    best, start = (0, 0), None
+    for i in range(len(alt)):
+        if i and alt[i][2] != alt[i - 1][2]:
+            start = i - 1 if start is None else start
+            if i - start + 1 > best[0]:
+                best = (i - start + 1, start)
+        else:
+            start = None
+    if best[0] > 4:
+        seg = alt[best[1]:best[1] + best[0]]
+        for k in ("fwd", "bwd"):
+            d_ = [e - s for s, e, kk in seg if kk == k]
+            t = statistics.fmean(d_)
+            out.append(f"| alternating fwd/bwd steps: {k} | {len(d_)} | {t / 1e3:.2f} | "
+                       f"{ALGO[k] / t:.0f} |")
+    for k, a, b in runs:
+        if b - a >= 4 and k in ALGO:
+            d_ = [seq[i][1] - seq[i][0] for i in range(a, b + 1)]
+            t = statistics.fmean(d_)
+            out.append(f"| {k} only, back to back | {len(d_)} | {t / 1e3:.2f} | {ALGO[k] / t:.0f} |")
+    return "\n".join(out)
+
+
+def _counter(d: str, name: str) -> dict:
+    rows = list(csv.DictReader(open(_one(os.path.join(d, "*_counter_collection.csv")))))
+    acc: dict = {}
+    for r in rows:
+        if r["Counter_Name"] == name:
+            acc.setdefault(kind(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return {k: statistics.fmean(v) for k, v in acc.items()}
+
+
+def traffic(fetch_dir: str, write_dir: str) -> str:
+    f = _counter(fetch_dir, "FETCH_SIZE")
+    w = _counter(write_dir, "WRITE_SIZE")
+    kib = COPY_BYTES / 1024
+    cf, cw = kib / f["copy"], kib / w["copy"]
+    sha = hashlib.sha256(open(SOURCE, "rb").read()).hexdigest()
+    out = [f"calibration (copy kernel, {COPY_BYTES} B read and written per launch): "
+           f"FETCH_SIZE reads {f['copy']:.1f} KiB -> factor {cf:.5f}; "
+           f"WRITE_SIZE reads {w['copy']:.1f} KiB -> factor {cw:.5f}", "",
+           "| kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM bytes (calibrated) | "
+           "algorithmic bytes | ratio |", "|---|---|---|---|---|---|"]
+    per = {}
+    for k in ("fwd", "bwd", "copy"):
+        b = (f[k] * cf + w[k] * cw) * 1024
+        per[k] = b
+        out.append(f"| {k} | {f[k]:.1f} | {w[k]:.1f} | {b:.0f} | {ALGO[k]} | {b / ALGO[k]:.5f} |")
+    out += ["", f"traffic_bytes_per_launch: {per['bwd']:.0f}", f"kernel_source_sha256: {sha}"]
+    return "\n".join(out)
+
+
+def main(argv):
+    if len(argv) >= 2 and argv[0] == "trace":
+        print(trace(argv[1]))
+    elif len(argv) >= 3 and argv[0] == "traffic":
+        print(traffic(argv[1], argv[2]))
+    else:
+        raise SystemExit(__doc__)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
