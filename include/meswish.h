@@ -134,6 +134,39 @@ const char *meswish_strerror(int status);
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int meswish_version(void);
 
+/* Kernel path a single-tensor call takes (see meswish_plan). */
+typedef enum {
+    MESWISH_PATH_NONE = -1,   /* nothing to launch (n == 0 or an error) */
+    MESWISH_PATH_VECTOR = 0,  /* 16-byte vectors; scalar head and tail */
+    MESWISH_PATH_ELEMENT = 1  /* pointers not congruent modulo 16 bytes */
+} meswish_path;
+
+/* Launch plan of a single-tensor call. */
+typedef struct {
+    int path;                   /* meswish_path */
+    long long head;             /* elements before the first 16-byte boundary */
+    long long nvec;             /* 16-byte vectors of the body */
+    long long tail;             /* elements after the body (all n on the element path) */
+    long long tiles;            /* work tiles (one block each) */
+    long long grid;             /* blocks launched */
+    long long block;            /* threads per block */
+    long long elems_per_vector; /* 4 (binary32) or 8 (bfloat16) */
+    long long vectors_per_tile; /* 16-byte vectors per tile */
+} meswish_plan_t;
+
+/*
+ * Introspection of the host logic, for tests and tools: runs exactly the
+ * argument checks of swish_fwd (bwd == 0; dy ignored) or swish_bwd
+ * (bwd != 0) and, on success, fills *plan with the split those calls would
+ * launch.  Launches nothing and never dereferences x, dy or out (it may
+ * query the current device's compute-unit count).
+ * Returns the status the call would return (MESWISH_EHIP excepted);
+ * MESWISH_EINVAL if plan is NULL.  n == 0 gives MESWISH_OK with
+ * path MESWISH_PATH_NONE.
+ */
+int meswish_plan(const void *x, const void *dy, const void *out, size_t n,
+                 float alpha, int dtype, int bwd, meswish_plan_t *plan);
+
 /*
  * Measurement helper (not part of the operation): a plain 16-byte-vector
  * device copy of `bytes` bytes from src to dst on `stream`, used to measure

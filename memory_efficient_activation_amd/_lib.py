@@ -20,7 +20,8 @@ F32, BF16 = 0, 1
 MAX_GROUP = 64
 
 EXPORTED = ("swish_fwd", "swish_bwd", "swish_fwd_grouped", "swish_bwd_grouped",
-            "meswish_strerror", "meswish_version", "meswish_copy")
+            "meswish_strerror", "meswish_version", "meswish_copy", "meswish_plan")
+PATH_NONE, PATH_VECTOR, PATH_ELEMENT = -1, 0, 1
 
 
 class FwdDesc(ctypes.Structure):
@@ -30,6 +31,13 @@ class FwdDesc(ctypes.Structure):
 class BwdDesc(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("dy", ctypes.c_void_p), ("dx", ctypes.c_void_p),
                 ("n", ctypes.c_size_t)]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int), ("head", ctypes.c_longlong), ("nvec", ctypes.c_longlong),
+                ("tail", ctypes.c_longlong), ("tiles", ctypes.c_longlong),
+                ("grid", ctypes.c_longlong), ("block", ctypes.c_longlong),
+                ("elems_per_vector", ctypes.c_longlong), ("vectors_per_tile", ctypes.c_longlong)]
 
 
 class MeswishError(RuntimeError):
@@ -56,6 +64,8 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.meswish_version.restype = i
     lib.meswish_copy.argtypes = [vp, vp, sz, vp]
     lib.meswish_copy.restype = i
+    lib.meswish_plan.argtypes = [vp, vp, vp, sz, f, i, i, ctypes.POINTER(Plan)]
+    lib.meswish_plan.restype = i
     return lib
 
 

@@ -644,63 +644,76 @@ static int64_t head_elems(const void* p, size_t esize)
     return mis ? (int64_t)((16u - mis) / esize) : 0;
 }
 
+// How one tensor is split between the kernels' paths (see meswish_plan_t).
+template <typename IO, bool kBwd>
+static meswish_plan_t make_plan(const void* x, const void* dy, const void* out, size_t n)
+{
+    constexpr int E = Io<IO>::kPerVec;
+    constexpr int64_t kTileVecs = tile_vecs<IO>();
+    meswish_plan_t p;
+    memset(&p, 0, sizeof p);
+    uintptr_t mx = (uintptr_t)x & 15u, mo = (uintptr_t)out & 15u;
+    uintptr_t md = kBwd ? ((uintptr_t)dy & 15u) : mx;
+    const int64_t nn = (int64_t)n;
+    if (mx == mo && mx == md) {
+        int64_t head = head_elems(x, sizeof(IO));
+        if (head > nn)
+            head = nn;
+        p.path = MESWISH_PATH_VECTOR;
+        p.head = head;
+        p.nvec = (nn - head) / E;
+        p.tail = nn - head - p.nvec * E;
+        p.tiles = (p.nvec + kTileVecs - 1) / kTileVecs;
+    } else {
+        p.path = MESWISH_PATH_ELEMENT;
+        p.tail = nn;
+        p.tiles = (nn + kTileVecs - 1) / kTileVecs;
+    }
+    p.grid = grid_for_tiles(p.tiles);
+    p.block = Io<IO>::kBlock;
+    p.elems_per_vector = E;
+    p.vectors_per_tile = kTileVecs;
+    return p;
+}
+
 template <typename IO, bool kBwd>
 static int run_single(const void* x, const void* dy, void* out, size_t n, Coef k,
                       hipStream_t stream)
 {
-    constexpr int E = Io<IO>::kPerVec;
-    uintptr_t mx = (uintptr_t)x & 15u, mo = (uintptr_t)out & 15u;
-    uintptr_t md = kBwd ? ((uintptr_t)dy & 15u) : mx;
+    const meswish_plan_t p = make_plan<IO, kBwd>(x, dy, out, n);
     const IO* xp = static_cast<const IO*>(x);
     const IO* dp = static_cast<const IO*>(dy);
     IO* op = static_cast<IO*>(out);
-    if (mx == mo && mx == md) {
-        int64_t head = head_elems(x, sizeof(IO));
-        if (head > (int64_t)n)
-            head = (int64_t)n;
-        int64_t nvec = ((int64_t)n - head) / E;
-        int64_t tail = (int64_t)n - head - nvec * E;
-        constexpr int64_t kTileVecs = tile_vecs<IO>();
-        int64_t grid = grid_for_tiles((nvec + kTileVecs - 1) / kTileVecs);
+    int64_t head = p.head, nvec = p.nvec, tail = p.tail;
+    if (p.path == MESWISH_PATH_VECTOR) {
         void* args[] = {&xp, &dp, &op, &head, &nvec, &tail, &k};
-        return launch(reinterpret_cast<const void*>(&swish_vec_kernel<IO, kBwd>), grid, args,
-                      stream, Io<IO>::kBlock);
+        return launch(reinterpret_cast<const void*>(&swish_vec_kernel<IO, kBwd>), p.grid, args,
+                      stream, (int)p.block);
     }
     int64_t nn = (int64_t)n;
-    constexpr int64_t kTile = tile_vecs<IO>();
-    int64_t grid = grid_for_tiles((nn + kTile - 1) / kTile);
     void* args[] = {&xp, &dp, &op, &nn, &k};
-    return launch(reinterpret_cast<const void*>(&swish_elem_kernel<IO, kBwd>), grid, args, stream,
-                  Io<IO>::kBlock);
+    return launch(reinterpret_cast<const void*>(&swish_elem_kernel<IO, kBwd>), p.grid, args,
+                  stream, (int)p.block);
 }
 
 template <typename IO, bool kBwd>
 static int run_group(GroupArgs& g, Coef k, hipStream_t stream)
 {
-    constexpr int E = Io<IO>::kPerVec;
-    constexpr int64_t kTileVecs = tile_vecs<IO>();
     int64_t tiles = 0;
     for (int j = 0; j < g.count; ++j) {
         g.tile_begin[j] = tiles;
-        const int64_t n = g.n[j];
-        uintptr_t mx = (uintptr_t)g.x[j] & 15u, mo = (uintptr_t)g.out[j] & 15u;
-        uintptr_t md = kBwd ? ((uintptr_t)g.dy[j] & 15u) : mx;
-        int64_t t;
-        if (n == 0) {
-            g.head[j] = 0;
-            t = 0;
-        } else if (mx == mo && mx == md) {
-            int64_t head = head_elems(g.x[j], sizeof(IO));
-            if (head > n)
-                head = n;
-            g.head[j] = (int32_t)head;
-            int64_t nvec = (n - head) / E;
-            t = (nvec + kTileVecs - 1) / kTileVecs;
-            if (t == 0)
-                t = 1;  // a tensor shorter than one vector still needs its scalar tile
-        } else {
-            g.head[j] = -1;
-            t = (n + kTileVecs - 1) / kTileVecs;
+        int64_t t = 0;
+        g.head[j] = 0;
+        if (g.n[j] > 0) {
+            const meswish_plan_t p = make_plan<IO, kBwd>(g.x[j], g.dy[j], g.out[j], (size_t)g.n[j]);
+            if (p.path == MESWISH_PATH_VECTOR) {
+                g.head[j] = (int32_t)p.head;
+                // A tensor shorter than one vector still needs its scalar tile.
+                t = p.tiles > 0 ? p.tiles : 1;
+            } else {
+                g.head[j] = -1;
+                t = p.tiles;
+            }
         }
         tiles += t;
     }
@@ -738,16 +751,32 @@ static int check_tensor(const void* p, size_t n, size_t esize)
 
 using namespace meswish;
 
-extern "C" int swish_fwd(const void* x, void* y, size_t n, float alpha, int dtype, void* stream)
+namespace meswish {
+
+// Argument checks of one single-tensor call (dy is NULL for the forward).
+static int check_single(const void* x, const void* dy, const void* out, size_t n, float alpha,
+                        int dtype, bool bwd)
 {
     int rc = check_common(alpha, dtype);
     if (rc != MESWISH_OK || n == 0)
         return rc;
     size_t es = elem_size(dtype);
-    if ((rc = check_tensor(x, n, es)) != MESWISH_OK || (rc = check_tensor(y, n, es)) != MESWISH_OK)
+    if ((rc = check_tensor(x, n, es)) != MESWISH_OK || (rc = check_tensor(out, n, es)) != MESWISH_OK)
         return rc;
-    if (!alias_ok(y, x, n * es))
+    if (bwd && (rc = check_tensor(dy, n, es)) != MESWISH_OK)
+        return rc;
+    if (!alias_ok(out, x, n * es) || (bwd && !alias_ok(out, dy, n * es)))
         return MESWISH_EALIAS;
+    return MESWISH_OK;
+}
+
+}  // namespace meswish
+
+extern "C" int swish_fwd(const void* x, void* y, size_t n, float alpha, int dtype, void* stream)
+{
+    int rc = check_single(x, nullptr, y, n, alpha, dtype, false);
+    if (rc != MESWISH_OK || n == 0)
+        return rc;
     Coef k = make_coef(alpha);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == MESWISH_F32)
@@ -758,20 +787,31 @@ extern "C" int swish_fwd(const void* x, void* y, size_t n, float alpha, int dtyp
 extern "C" int swish_bwd(const void* x, const void* dy, void* dx, size_t n, float alpha, int dtype,
                          void* stream)
 {
-    int rc = check_common(alpha, dtype);
+    int rc = check_single(x, dy, dx, n, alpha, dtype, true);
     if (rc != MESWISH_OK || n == 0)
         return rc;
-    size_t es = elem_size(dtype);
-    if ((rc = check_tensor(x, n, es)) != MESWISH_OK || (rc = check_tensor(dy, n, es)) != MESWISH_OK ||
-        (rc = check_tensor(dx, n, es)) != MESWISH_OK)
-        return rc;
-    if (!alias_ok(dx, x, n * es) || !alias_ok(dx, dy, n * es))
-        return MESWISH_EALIAS;
     Coef k = make_coef(alpha);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == MESWISH_F32)
         return run_single<float, true>(x, dy, dx, n, k, s);
     return run_single<bf16_t, true>(x, dy, dx, n, k, s);
+}
+
+extern "C" int meswish_plan(const void* x, const void* dy, const void* out, size_t n, float alpha,
+                            int dtype, int bwd, meswish_plan_t* plan)
+{
+    if (plan == nullptr)
+        return MESWISH_EINVAL;
+    memset(plan, 0, sizeof *plan);
+    plan->path = MESWISH_PATH_NONE;
+    int rc = check_single(x, dy, out, n, alpha, dtype, bwd != 0);
+    if (rc != MESWISH_OK || n == 0)
+        return rc;
+    if (dtype == MESWISH_F32)
+        *plan = bwd ? make_plan<float, true>(x, dy, out, n) : make_plan<float, false>(x, dy, out, n);
+    else
+        *plan = bwd ? make_plan<bf16_t, true>(x, dy, out, n) : make_plan<bf16_t, false>(x, dy, out, n);
+    return MESWISH_OK;
 }
 
 namespace meswish {

@@ -42,7 +42,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "meswish_copy", "meswish_strerror", "meswish_version", "swish_bwd",
+        "meswish_copy", "meswish_plan", "meswish_strerror", "meswish_version", "swish_bwd",
         "swish_bwd_grouped", "swish_fwd", "swish_fwd_grouped"])
 
 
@@ -65,6 +65,12 @@ def test_binding_constants_match_header(lib):
     m = re.search(r"#define MESWISH_MAX_GROUP (\d+)", _header_text())
     assert int(m.group(1)) == _lib.MAX_GROUP
     assert set(_lib.EXPORTED) == set(declared_functions())
+    m = re.findall(r"MESWISH_PATH_(\w+)\s*=\s*(-?\d+)", _header_text())
+    assert {k: int(v) for k, v in m} == {"NONE": _lib.PATH_NONE, "VECTOR": _lib.PATH_VECTOR,
+                                         "ELEMENT": _lib.PATH_ELEMENT}
+    fields = re.search(r"typedef struct \{([^{}]*)\}\s*meswish_plan_t;", _header_text()).group(1)
+    names = re.findall(r"(\w+);", fields)
+    assert names == [f[0] for f in _lib.Plan._fields_]
     # Descriptor layouts: pointer, pointer, size_t (+ one more pointer for bwd).
     assert ctypes.sizeof(_lib.FwdDesc) == 24 and ctypes.sizeof(_lib.BwdDesc) == 32
 
