@@ -14,8 +14,11 @@ What it computes (cited by page title and section):
   "How is Swish implemented?": y = x * Sigmoid(alpha x), Sigmoid(t) = 1/(1+e^-t).
 * [P1] "How is the memory efficient version Swish implemented?": backward from
   the input alone, dx = dy * s * (1 + t (1 - s)), t = alpha x, s = Sigmoid(t)
-  (alpha > 1 by the product rule; the page prints alpha = 1).
+  (alpha other than 1 by the product rule; the page prints alpha = 1).
 * Results are rounded once, to nearest even, to binary32 or bfloat16.
+* [P3] "What activations cost, in memory and in arithmetic", Given: the
+  activation family ReLU, LeakyReLU, sigmoid, tanh, GELU (erf) and GELU
+  (tanh approximation), each with its textbook derivative.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against facts
 that do not come from the oracle itself (closed forms, finite differences,
@@ -38,6 +41,10 @@ LIBRARY = os.path.join(HERE, "liboracle.so")
 
 F32 = 0
 BF16 = 1
+
+# Activation codes of the oracle's family (its own numbering).
+ACTS = {"swish": 0, "relu": 1, "leaky_relu": 2, "sigmoid": 3, "tanh": 4,
+        "gelu_erf": 5, "gelu_tanh": 6}
 
 GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
              "-fno-fast-math", "-Wall", "-Wextra"]
@@ -70,6 +77,17 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
                                          ctypes.c_double,
                                          ctypes.POINTER(ctypes.c_double)]
     lib.oracle_swish_bwd_f64.restype = ctypes.c_double
+    lib.oracle_act_f64.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_double]
+    lib.oracle_act_f64.restype = ctypes.c_double
+    lib.oracle_act_grad_f64.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_double,
+                                        ctypes.c_double, ctypes.POINTER(ctypes.c_double)]
+    lib.oracle_act_grad_f64.restype = ctypes.c_double
+    lib.oracle_act_fwd.argtypes = [ctypes.c_int, ctypes.c_int, c_void, c_void, c_size,
+                                   ctypes.c_float, ctypes.c_int]
+    lib.oracle_act_fwd.restype = ctypes.c_int
+    lib.oracle_act_bwd.argtypes = [ctypes.c_int, ctypes.c_int, c_void, c_void, c_void, c_void,
+                                   c_size, ctypes.c_float, ctypes.c_int]
+    lib.oracle_act_bwd.restype = ctypes.c_int
     return lib
 
 
@@ -151,6 +169,41 @@ class Oracle:
                                        x.size, float(np.float32(alpha)), int(threads))
         if rc != 0:
             raise RuntimeError(f"oracle_swish_bwd failed ({rc})")
+        return dx, scale
+
+    # --- the activation family ------------------------------------------
+    def act_f64(self, act: str, x: float, p: float = 0.0) -> float:
+        return self.lib.oracle_act_f64(ACTS[act], float(x), float(p))
+
+    def act_grad_f64(self, act: str, x: float, dy: float, p: float = 0.0) -> tuple[float, float]:
+        m = ctypes.c_double()
+        g = self.lib.oracle_act_grad_f64(ACTS[act], float(x), float(dy), float(p), ctypes.byref(m))
+        return g, m.value
+
+    def act_fwd(self, act: str, x: np.ndarray, p: float = 0.0, threads: int = 1) -> np.ndarray:
+        x = np.ascontiguousarray(x)
+        code = self._dtype_code(x)
+        y = np.empty_like(x)
+        rc = self.lib.oracle_act_fwd(ACTS[act], code, x.ctypes.data, y.ctypes.data, x.size,
+                                     float(np.float32(p)), int(threads))
+        if rc != 0:
+            raise RuntimeError(f"oracle_act_fwd failed ({rc})")
+        return y
+
+    def act_bwd(self, act: str, x: np.ndarray, dy: np.ndarray, p: float = 0.0, threads: int = 1,
+                want_scale: bool = True) -> tuple[np.ndarray, np.ndarray | None]:
+        x = np.ascontiguousarray(x)
+        dy = np.ascontiguousarray(dy)
+        if x.shape != dy.shape or x.dtype != dy.dtype:
+            raise ValueError("x and dy must have the same shape and dtype")
+        code = self._dtype_code(x)
+        dx = np.empty_like(x)
+        scale = np.empty(x.shape, dtype=np.float64) if want_scale else None
+        rc = self.lib.oracle_act_bwd(ACTS[act], code, x.ctypes.data, dy.ctypes.data,
+                                     dx.ctypes.data, scale.ctypes.data if want_scale else None,
+                                     x.size, float(np.float32(p)), int(threads))
+        if rc != 0:
+            raise RuntimeError(f"oracle_act_bwd failed ({rc})")
         return dx, scale
 
     def fwd_grouped(self, xs, alpha: float, threads: int = 1):

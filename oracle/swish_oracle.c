@@ -163,10 +163,131 @@ double oracle_swish_grad(double x, double dy, double alpha, double *scale)
 }
 
 /* ------------------------------------------------------------------ */
+/* The activation family of [P3] "What activations cost, in memory and */
+/* in arithmetic", Given: ReLU, LeakyReLU, sigmoid, tanh, GELU with    */
+/* erf and GELU with the tanh approximation.  The page names them and  */
+/* their flop counts; the definitions are the standard ones:           */
+/*   ReLU(x)      = x if x > 0 else 0,  derivative 1 if x > 0 else 0   */
+/*   LeakyReLU(x) = x if x > 0 else a x, derivative 1 if x > 0 else a  */
+/*   sigmoid(x)   = 1 / (1 + e^-x),     derivative s (1 - s)           */
+/*   tanh(x),                           derivative 1 / cosh(x)^2       */
+/*   GELU(x)      = x Phi(x), Phi the standard normal CDF,             */
+/*                  derivative Phi(x) + x phi(x), phi its density      */
+/*   GELU_tanh(x) = x (1 + tanh(u)) / 2, u = sqrt(2/pi)(x + 0.044715x^3)*/
+/* Where a textbook form would lose everything to cancellation in      */
+/* binary64 it is replaced by an exact identity:                        */
+/*   1 - sigmoid(x) = sigmoid(-x)  (the add-and-subtract-one step of   */
+/*                                 [P1] "What makes this               */
+/*                                 implementation save GPU memory?")   */
+/*   Phi(x) = erfc(-x / sqrt 2) / 2                                    */
+/*   (1 + tanh(u)) / 2 = sigmoid(2u)                                   */
+/*   1 - tanh(x)^2 = 1 / cosh(x)^2                                     */
+/* ------------------------------------------------------------------ */
+
+#define ORACLE_ACT_SWISH 0
+#define ORACLE_ACT_RELU 1
+#define ORACLE_ACT_LEAKY_RELU 2
+#define ORACLE_ACT_SIGMOID 3
+#define ORACLE_ACT_TANH 4
+#define ORACLE_ACT_GELU_ERF 5
+#define ORACLE_ACT_GELU_TANH 6
+
+static const double kInvSqrt2 = 0.70710678118654752440084436210484904;
+static const double kInvSqrt2Pi = 0.39894228040143267793994605993438187;
+static const double kSqrt2OverPi = 0.79788456080286535587989211986876374;
+static const double kGeluTanhCubic = 0.044715;
+
+static double std_normal_cdf(double x) { return 0.5 * erfc(-x * kInvSqrt2); }
+static double std_normal_pdf(double x) { return kInvSqrt2Pi * exp(-0.5 * x * x); }
+
+/* Value of activation `act` with parameter p (alpha of Swish, negative
+ * slope of LeakyReLU; ignored by the others).  NaN in, NaN out. */
+double oracle_act_f64(int act, double x, double p)
+{
+    if (isnan(x))
+        return x;
+    switch (act) {
+    case ORACLE_ACT_SWISH:
+        return oracle_swish(x, p);
+    case ORACLE_ACT_RELU:
+        return x > 0.0 ? x : 0.0;
+    case ORACLE_ACT_LEAKY_RELU:
+        return x > 0.0 ? x : p * x;
+    case ORACLE_ACT_SIGMOID:
+        return oracle_sigmoid(x);
+    case ORACLE_ACT_TANH:
+        return tanh(x);
+    case ORACLE_ACT_GELU_ERF:
+        return x * std_normal_cdf(x);
+    case ORACLE_ACT_GELU_TANH: {
+        double u = kSqrt2OverPi * (x + kGeluTanhCubic * x * x * x);
+        return x * oracle_sigmoid(2.0 * u);
+    }
+    default:
+        return NAN;
+    }
+}
+
+/* dy times the derivative of activation `act` at x, and (if scale is not
+ * NULL) the same expression with every term of its sum taken positive --
+ * the error scale for the sums that can cancel (Swish, GELU). */
+double oracle_act_grad_f64(int act, double x, double dy, double p, double *scale)
+{
+    double g, m;
+    if (isnan(x) || isnan(dy)) {
+        if (scale)
+            *scale = NAN;
+        return NAN;
+    }
+    switch (act) {
+    case ORACLE_ACT_SWISH:
+        return oracle_swish_grad(x, dy, p, scale);
+    case ORACLE_ACT_RELU:
+        g = dy * (x > 0.0 ? 1.0 : 0.0);
+        m = fabs(g);
+        break;
+    case ORACLE_ACT_LEAKY_RELU:
+        g = dy * (x > 0.0 ? 1.0 : p);
+        m = fabs(g);
+        break;
+    case ORACLE_ACT_SIGMOID:
+        g = dy * oracle_sigmoid(x) * oracle_sigmoid(-x);
+        m = fabs(g);
+        break;
+    case ORACLE_ACT_TANH: {
+        double c = cosh(x);
+        g = dy / (c * c);
+        m = fabs(g);
+        break;
+    }
+    case ORACLE_ACT_GELU_ERF: {
+        double cdf = std_normal_cdf(x), pdf = std_normal_pdf(x);
+        g = dy * (cdf + x * pdf);
+        m = fabs(dy) * (cdf + fabs(x) * pdf);
+        break;
+    }
+    case ORACLE_ACT_GELU_TANH: {
+        double u = kSqrt2OverPi * (x + kGeluTanhCubic * x * x * x);
+        double du = kSqrt2OverPi * (1.0 + 3.0 * kGeluTanhCubic * x * x);
+        double s = oracle_sigmoid(2.0 * u), c = oracle_sigmoid(-2.0 * u);
+        g = dy * (s + x * s * c * 2.0 * du);
+        m = fabs(dy) * (s + fabs(x) * s * c * 2.0 * du);
+        break;
+    }
+    default:
+        g = m = NAN;
+    }
+    if (scale)
+        *scale = m;
+    return g;
+}
+
+/* ------------------------------------------------------------------ */
 /* Array drivers.                                                      */
 /* ------------------------------------------------------------------ */
 
 typedef struct {
+    int act;
     int dtype;
     const void *x;
     const void *dy;
@@ -180,7 +301,7 @@ static void *fwd_range(void *arg)
 {
     const oracle_job *j = (const oracle_job *)arg;
     for (size_t i = j->begin; i < j->end; ++i)
-        store(j->dtype, j->out, i, oracle_swish(load(j->dtype, j->x, i), j->alpha));
+        store(j->dtype, j->out, i, oracle_act_f64(j->act, load(j->dtype, j->x, i), j->alpha));
     return NULL;
 }
 
@@ -189,8 +310,8 @@ static void *bwd_range(void *arg)
     const oracle_job *j = (const oracle_job *)arg;
     for (size_t i = j->begin; i < j->end; ++i) {
         double m;
-        double g = oracle_swish_grad(load(j->dtype, j->x, i),
-                                     load(j->dtype, j->dy, i), j->alpha, &m);
+        double g = oracle_act_grad_f64(j->act, load(j->dtype, j->x, i),
+                                       load(j->dtype, j->dy, i), j->alpha, &m);
         store(j->dtype, j->out, i, g);
         if (j->scale)
             j->scale[i] = m;
@@ -240,7 +361,7 @@ int oracle_swish_fwd(int dtype, const void *x, void *y, size_t n, float alpha,
 {
     if (dtype != ORACLE_F32 && dtype != ORACLE_BF16)
         return -1;
-    oracle_job j = {dtype, x, NULL, y, NULL, (double)alpha, 0, 0};
+    oracle_job j = {ORACLE_ACT_SWISH, dtype, x, NULL, y, NULL, (double)alpha, 0, 0};
     run_split(fwd_range, j, n, threads);
     return 0;
 }
@@ -253,7 +374,33 @@ int oracle_swish_bwd(int dtype, const void *x, const void *dy, void *dx,
 {
     if (dtype != ORACLE_F32 && dtype != ORACLE_BF16)
         return -1;
-    oracle_job j = {dtype, x, dy, dx, scale, (double)alpha, 0, 0};
+    oracle_job j = {ORACLE_ACT_SWISH, dtype, x, dy, dx, scale, (double)alpha, 0, 0};
+    run_split(bwd_range, j, n, threads);
+    return 0;
+}
+
+/* The same drivers for any activation of the family; p is the activation's
+ * parameter as a binary32 value.  Returns -1 for an unknown act or dtype. */
+int oracle_act_fwd(int act, int dtype, const void *x, void *y, size_t n, float p,
+                   int threads)
+{
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16)
+        return -1;
+    if (act < ORACLE_ACT_SWISH || act > ORACLE_ACT_GELU_TANH)
+        return -1;
+    oracle_job j = {act, dtype, x, NULL, y, NULL, (double)p, 0, 0};
+    run_split(fwd_range, j, n, threads);
+    return 0;
+}
+
+int oracle_act_bwd(int act, int dtype, const void *x, const void *dy, void *dx,
+                   double *scale, size_t n, float p, int threads)
+{
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16)
+        return -1;
+    if (act < ORACLE_ACT_SWISH || act > ORACLE_ACT_GELU_TANH)
+        return -1;
+    oracle_job j = {act, dtype, x, dy, dx, scale, (double)p, 0, 0};
     run_split(bwd_range, j, n, threads);
     return 0;
 }

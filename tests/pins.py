@@ -354,4 +354,172 @@ def pin_page3_sizing(_o=None):
     assert acc.fwd_bytes(n, "bf16") + acc.bwd_bytes(n, "bf16") == 671_088_640
 
 
+
+
+# --------------------------------------------------------------------------
+# The activation family of "What activations cost, in memory and in
+# arithmetic" (Given).
+# --------------------------------------------------------------------------
+
+FAMILY = ("relu", "leaky_relu", "sigmoid", "tanh", "gelu_erf", "gelu_tanh")
+LEAKY_SLOPE = 0.01
+
+
+def _param(act):
+    return LEAKY_SLOPE if act == "leaky_relu" else 0.0
+
+
+def pin_family_special_values(o):
+    for c in _golden("activation_family_special_values.json")["cases"]:
+        assert o.act_f64(c["act"], c["x"], c["p"]) == c["value"], c
+        assert o.act_grad_f64(c["act"], c["x"], 1.0, c["p"])[0] == c["grad"], c
+
+
+def _mp_family(act, p):
+    import mpmath
+    a = mpmath.mpf(p)
+    if act == "relu":
+        return lambda u: u if u > 0 else mpmath.mpf(0)
+    if act == "leaky_relu":
+        return lambda u: u if u > 0 else a * u
+    if act == "sigmoid":
+        return lambda u: 1 / (1 + mpmath.exp(-u))
+    if act == "tanh":
+        return mpmath.tanh
+    if act == "gelu_erf":
+        return lambda u: u * mpmath.ncdf(u)
+    k = mpmath.sqrt(2 / mpmath.pi)
+    return lambda u: u * (1 + mpmath.tanh(k * (u + mpmath.mpf("0.044715") * u ** 3))) / 2
+
+
+def pin_family_mpmath(o):
+    """Each activation and its derivative at 60 digits (mpmath's own
+    functions, the textbook formulas), including the far tails."""
+    import mpmath
+    mpmath.mp.dps = 60
+    for act in FAMILY:
+        p = _param(act)
+        f = _mp_family(act, p)
+        for x in np.concatenate([_grid(-30.0, 30.0, 40, 41), [-0.3, 0.7, 1e-3, -1e-3]]):
+            # (1 + tanh u) / 2 cancels to about e^(2u): carry enough digits.
+            mpmath.mp.dps = 60 + (int(0.04 * abs(x) ** 3) if act == "gelu_tanh" else 0)
+            X = mpmath.mpf(float(x))
+            ref = f(X)
+            y = o.act_f64(act, x, p)
+            # Where the function behaves like exp(-z), binary64 rounding of
+            # the argument z costs about |z| ulps: the condition number.
+            z = {"sigmoid": abs(x), "tanh": 2 * abs(x), "gelu_erf": x * x,
+                 "gelu_tanh": 0.08 * abs(x) ** 3 + 2 * abs(x)}.get(act, 0.0)
+            cond = 1.0 + z
+            assert abs(y - float(ref)) <= 1e-14 * cond * abs(float(ref)) + 1e-300, (act, x, y, ref)
+            if act in ("relu", "leaky_relu") and abs(x) < 1e-2:
+                continue  # kink at 0: no two-sided derivative
+            dref = mpmath.diff(f, X)
+            g, m = o.act_grad_f64(act, x, 1.0, p)
+            assert abs(g - float(dref)) <= 1e-13 * cond * max(m, 1e-300) + 1e-300, (act, x, g, dref)
+
+
+def pin_family_torch_autograd(o):
+    """Binary64 PyTorch CPU autograd of torch's own activations (an
+    independent implementation), where torch itself does not cancel."""
+    import torch
+    import torch.nn.functional as F
+    fns = {"relu": torch.relu, "leaky_relu": lambda t: F.leaky_relu(t, LEAKY_SLOPE),
+           "sigmoid": torch.sigmoid, "tanh": torch.tanh,
+           "gelu_erf": lambda t: F.gelu(t, approximate="none"),
+           "gelu_tanh": lambda t: F.gelu(t, approximate="tanh")}
+    rng = np.random.default_rng(43)
+    x_all = np.concatenate([rng.uniform(-4, 30, 500), rng.standard_normal(500) * 2, [0.0, 1e-6, -1e-6]])
+    dy_all = rng.standard_normal(x_all.size)
+    # torch's own backward works from the output (1 - y, 1 - y^2, 1 + erf),
+    # which cancels in the tails: compare where it keeps 13 digits.
+    limit = {"sigmoid": 6.0, "tanh": 3.0, "gelu_erf": 3.0, "gelu_tanh": 3.0}
+    for act, fn in fns.items():
+        p = _param(act)
+        lim = limit.get(act, np.inf)
+        x = x_all[np.abs(x_all) <= lim]
+        dy = dy_all[np.abs(x_all) <= lim]
+        xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+        y = fn(xt)
+        y.backward(torch.tensor(dy, dtype=torch.float64))
+        gt, yt = xt.grad.numpy(), y.detach().numpy()
+        for i in range(x.size):
+            g, m = o.act_grad_f64(act, x[i], dy[i], p)
+            assert abs(g - gt[i]) <= 1e-12 * max(m, 1e-300) + 1e-300, (act, x[i], g, gt[i])
+            yo = o.act_f64(act, x[i], p)
+            assert abs(yo - yt[i]) <= 1e-12 * abs(yo) + 1e-300, (act, x[i], yo, yt[i])
+
+
+def pin_family_library_routines(o):
+    from scipy.special import expit, ndtr
+    for x in _grid(-40.0, 40.0, 300, 47):
+        assert abs(o.act_f64("sigmoid", x) - expit(x)) <= 1e-15 * expit(x) + 1e-320
+        assert abs(o.act_f64("tanh", x) - np.tanh(x)) <= 2e-16 * abs(np.tanh(x)) + 1e-320
+        if x > -25.0:  # scipy's ndtr loses relative accuracy further out
+            ge = x * ndtr(x)
+            assert abs(o.act_f64("gelu_erf", x) - ge) <= 1e-13 * abs(ge) + 1e-320, x
+
+
+def pin_family_identities(o):
+    """sigma(x) + sigma(-x) = 1, tanh odd, GELU(x) - GELU(-x) = x for both
+    variants (u is odd in x), ReLU(x) - ReLU(-x) = x; derivatives of the
+    symmetric ones are even."""
+    for x in _grid(-20.0, 20.0, 200, 53):
+        assert abs(o.act_f64("sigmoid", x) + o.act_f64("sigmoid", -x) - 1) <= 4.5e-16
+        assert o.act_f64("tanh", -x) == -o.act_f64("tanh", x)
+        assert o.act_grad_f64("tanh", x, 1.0)[0] == o.act_grad_f64("tanh", -x, 1.0)[0]
+        gs, gsm = o.act_grad_f64("sigmoid", x, 1.0)[0], o.act_grad_f64("sigmoid", -x, 1.0)[0]
+        assert abs(gs - gsm) <= 1e-16 * gs
+        for act in ("gelu_erf", "gelu_tanh"):
+            d = o.act_f64(act, x) - o.act_f64(act, -x)
+            assert abs(d - x) <= 1e-15 * max(abs(x), 1.0), (act, x, d)
+            gsum = o.act_grad_f64(act, x, 1.0)[0] + o.act_grad_f64(act, -x, 1.0)[0]
+            assert abs(gsum - 1.0) <= 1e-13 * (1 + x * x), (act, x, gsum)
+        assert o.act_f64("relu", x) - o.act_f64("relu", -x) == x
+
+
+def pin_family_finite_differences(o):
+    for act in FAMILY:
+        p = _param(act)
+        for x in _grid(-12.0, 12.0, 300, 59):
+            if act in ("relu", "leaky_relu") and abs(x) < 1e-3:
+                continue
+            h = 1e-5 * max(1.0, abs(x))
+            fd = (o.act_f64(act, x + h, p) - o.act_f64(act, x - h, p)) / (2 * h)
+            g, m = o.act_grad_f64(act, x, 1.0, p)
+            assert abs(fd - g) <= 1e-8 * max(m, 1e-3), (act, x, fd, g)
+
+
+def pin_family_array_drivers(o):
+    rng = np.random.default_rng(61)
+    x64 = np.concatenate([rng.standard_normal(1500) * 5, rng.uniform(-100, 100, 500),
+                          [0.0, -0.0, 1e-40, -1e-40, 3e38, -3e38]])
+    dy64 = rng.standard_normal(x64.size)
+    x32, dy32 = x64.astype(np.float32), dy64.astype(np.float32)
+    u, ub = x32.view(np.uint32), dy32.view(np.uint32)
+    xb = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    dyb = ((ub + 0x7FFF + ((ub >> 16) & 1)) >> 16).astype(np.uint16)
+    xbf = (xb.astype(np.uint32) << 16).view(np.float32)
+    dybf = (dyb.astype(np.uint32) << 16).view(np.float32)
+    for act in FAMILY:
+        p = float(np.float32(_param(act)))
+        y1 = o.act_fwd(act, x32, p, threads=1)
+        y5 = o.act_fwd(act, x32, p, threads=5)
+        assert y1.tobytes() == y5.tobytes()
+        d1, m1 = o.act_bwd(act, x32, dy32, p, threads=3)
+        yb = o.act_fwd(act, xb, p, threads=2)
+        db, _ = o.act_bwd(act, xb, dyb, p, threads=2)
+        for i in range(x32.size):
+            assert y1[i].tobytes() == o.round_f32(o.act_f64(act, float(x32[i]), p)).tobytes()
+            g, m = o.act_grad_f64(act, float(x32[i]), float(dy32[i]), p)
+            assert d1[i].tobytes() == o.round_f32(g).tobytes() and m1[i] == m
+            assert int(yb[i]) == o.round_bf16(o.act_f64(act, float(xbf[i]), p))
+            assert int(db[i]) == o.round_bf16(o.act_grad_f64(act, float(xbf[i]), float(dybf[i]), p)[0])
+    # NaN in, NaN out.
+    for act in FAMILY:
+        assert math.isnan(o.act_f64(act, float("nan"), 0.01))
+        assert math.isnan(o.act_grad_f64(act, float("nan"), 1.0, 0.01)[0])
+        assert math.isnan(o.act_grad_f64(act, 1.0, float("nan"), 0.01)[0])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

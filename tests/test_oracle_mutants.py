@@ -39,8 +39,28 @@ MUTANTS = {
                         "*scale = fabs(dy) * s * (1.0 + t * one_minus_s);"),
     "split_drops_last": ("jobs[k].end = n * (size_t)(k + 1) / (size_t)threads;",
                          "jobs[k].end = n * (size_t)(k + 1) / (size_t)threads - (k + 1 == threads);"),
-    "alpha_rounded_to_int": ("oracle_job j = {dtype, x, NULL, y, NULL, (double)alpha, 0, 0};",
-                             "oracle_job j = {dtype, x, NULL, y, NULL, (double)(int)alpha, 0, 0};"),
+    "alpha_rounded_to_int": ("oracle_job j = {ORACLE_ACT_SWISH, dtype, x, NULL, y, NULL, (double)alpha, 0, 0};",
+                             "oracle_job j = {ORACLE_ACT_SWISH, dtype, x, NULL, y, NULL, (double)(int)alpha, 0, 0};"),
+    # The activation family.
+    "gelu_cdf_sign": ("return 0.5 * erfc(-x * kInvSqrt2);", "return 0.5 * erfc(x * kInvSqrt2);"),
+    "gelu_pdf_exponent": ("return kInvSqrt2Pi * exp(-0.5 * x * x);", "return kInvSqrt2Pi * exp(-x * x);"),
+    "gelu_pdf_constant": ("static const double kInvSqrt2Pi = 0.39894228040143267793994605993438187;",
+                          "static const double kInvSqrt2Pi = 0.5;"),
+    "gelu_grad_drops_cdf": ("g = dy * (cdf + x * pdf);", "g = dy * (x * pdf);"),
+    "gelu_tanh_cubic": ("static const double kGeluTanhCubic = 0.044715;",
+                        "static const double kGeluTanhCubic = 0.0447;"),
+    "gelu_tanh_du": ("double du = kSqrt2OverPi * (1.0 + 3.0 * kGeluTanhCubic * x * x);",
+                     "double du = kSqrt2OverPi * (1.0 + kGeluTanhCubic * x * x);"),
+    "gelu_tanh_half_u": ("return x * oracle_sigmoid(2.0 * u);", "return x * oracle_sigmoid(u);"),
+    "tanh_grad_not_squared": ("g = dy / (c * c);", "g = dy / c;"),
+    "sigmoid_grad_s_squared": ("g = dy * oracle_sigmoid(x) * oracle_sigmoid(-x);",
+                               "g = dy * oracle_sigmoid(x) * oracle_sigmoid(x);"),
+    "relu_grad_drops_dy": ("g = dy * (x > 0.0 ? 1.0 : 0.0);", "g = (x > 0.0 ? 1.0 : 0.0);"),
+    "leaky_fwd_drops_x": ("return x > 0.0 ? x : p * x;", "return x > 0.0 ? x : p;"),
+    "leaky_grad_at_zero": ("g = dy * (x > 0.0 ? 1.0 : p);", "g = dy * (x >= 0.0 ? 1.0 : p);"),
+    "gelu_scale_drops_abs": ("m = fabs(dy) * (cdf + fabs(x) * pdf);", "m = fabs(dy) * (cdf + x * pdf);"),
+    "family_nan_passthrough": ("    if (isnan(x))\n        return x;\n    switch (act) {",
+                               "    switch (act) {"),
 }
 
 
