@@ -96,6 +96,35 @@ int swish_fwd(const void *x, void *y, size_t n, float alpha, int dtype,
 int swish_bwd(const void *x, const void *dy, void *dx, size_t n, float alpha,
               int dtype, void *stream);
 
+/*
+ * The activation family of "What activations cost, in memory and in
+ * arithmetic" (Given), each with the save-the-input scheme of [P1] "How is
+ * the memory efficient version Swish implemented?": the forward writes y
+ * only; the backward recomputes what it needs from x and reads dy.
+ * Definitions (param: alpha of Swish, negative slope of LeakyReLU; ignored
+ * by the others but must be finite):
+ */
+typedef enum {
+    MESWISH_ACT_SWISH = 0,      /* x sigmoid(param x)                        */
+    MESWISH_ACT_RELU = 1,       /* x > 0 ? x : 0        (derivative 0 at 0)  */
+    MESWISH_ACT_LEAKY_RELU = 2, /* x > 0 ? x : param x  (derivative param at 0) */
+    MESWISH_ACT_SIGMOID = 3,    /* 1 / (1 + e^-x)                            */
+    MESWISH_ACT_TANH = 4,       /* tanh x                                    */
+    MESWISH_ACT_GELU_ERF = 5,   /* x Phi(x) = x (1 + erf(x / sqrt 2)) / 2    */
+    MESWISH_ACT_GELU_TANH = 6   /* x (1 + tanh(sqrt(2/pi)(x + 0.044715 x^3))) / 2 */
+} meswish_act;
+
+/*
+ * y[i] = f(x[i]) and dx[i] = dy[i] f'(x[i]) for the activation `act`, with
+ * the conventions of swish_fwd / swish_bwd (which equal these calls with
+ * MESWISH_ACT_SWISH).  Unknown act -> MESWISH_EINVAL.  NaN in x or dy gives
+ * NaN out.
+ */
+int meswish_act_fwd(int act, const void *x, void *y, size_t n, float param,
+                    int dtype, void *stream);
+int meswish_act_bwd(int act, const void *x, const void *dy, void *dx,
+                    size_t n, float param, int dtype, void *stream);
+
 /* One tensor of a grouped forward. */
 typedef struct {
     const void *x;
@@ -112,7 +141,7 @@ typedef struct {
 } meswish_bwd_desc;
 
 /*
- * Grouped variants: the same operation on `count` tensors that share alpha
+ * Grouped variants (Swish): the same operation on `count` tensors that share alpha
  * and dtype, in ONE kernel launch (for a network's many small activations,
  * e.g. the feature maps of an EfficientNet that the blog post measures in
  * "How much GPU memory is saved?").  `desc` is a HOST array of `count`

@@ -7,6 +7,8 @@ declared in include/meswish.h).  This package is a thin binding over it:
   -- tensor-level calls with the C ABI's names;
 * ``SwishFn`` / ``swish`` / ``MemoryEfficientSwish`` -- autograd function and
   module that keep only the input between forward and backward;
+* ``act_fwd`` / ``act_bwd`` / ``ActFn`` / ``MemoryEfficientActivation`` -- the
+  same scheme for ReLU, LeakyReLU, sigmoid, tanh and both GELUs;
 * ``naive.Swish`` -- the plain module, for comparisons;
 * ``inputs`` -- seeded synthetic workloads; ``accounting`` -- byte counts.
 
@@ -14,11 +16,13 @@ The shared library is loaded on first use; importing the package does not
 need a GPU.
 """
 
-from .functional import copy_bytes, swish_bwd, swish_bwd_grouped, swish_fwd, swish_fwd_grouped
-from .module import MemoryEfficientSwish, SwishFn, swish
+from .functional import (act_bwd, act_fwd, copy_bytes, swish_bwd, swish_bwd_grouped, swish_fwd,
+                         swish_fwd_grouped)
+from .module import ActFn, MemoryEfficientActivation, MemoryEfficientSwish, SwishFn, swish
 from ._lib import MeswishError
 
 __all__ = [
     "swish_fwd", "swish_bwd", "swish_fwd_grouped", "swish_bwd_grouped", "copy_bytes",
+    "act_fwd", "act_bwd", "ActFn", "MemoryEfficientActivation",
     "SwishFn", "swish", "MemoryEfficientSwish", "MeswishError",
 ]

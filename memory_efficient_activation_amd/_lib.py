@@ -20,7 +20,13 @@ F32, BF16 = 0, 1
 MAX_GROUP = 64
 
 EXPORTED = ("swish_fwd", "swish_bwd", "swish_fwd_grouped", "swish_bwd_grouped",
+            "meswish_act_fwd", "meswish_act_bwd",
             "meswish_strerror", "meswish_version", "meswish_copy", "meswish_plan")
+
+# Activation codes (mirror meswish_act) and their default parameters.
+ACTS = {"swish": 0, "relu": 1, "leaky_relu": 2, "sigmoid": 3, "tanh": 4, "gelu": 5,
+        "gelu_tanh": 6}
+DEFAULT_PARAM = {"swish": 1.0, "leaky_relu": 0.01}
 PATH_NONE, PATH_VECTOR, PATH_ELEMENT = -1, 0, 1
 
 
@@ -64,6 +70,10 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.meswish_version.restype = i
     lib.meswish_copy.argtypes = [vp, vp, sz, vp]
     lib.meswish_copy.restype = i
+    lib.meswish_act_fwd.argtypes = [i, vp, vp, sz, f, i, vp]
+    lib.meswish_act_fwd.restype = i
+    lib.meswish_act_bwd.argtypes = [i, vp, vp, vp, sz, f, i, vp]
+    lib.meswish_act_bwd.restype = i
     lib.meswish_plan.argtypes = [vp, vp, vp, sz, f, i, i, ctypes.POINTER(Plan)]
     lib.meswish_plan.restype = i
     return lib

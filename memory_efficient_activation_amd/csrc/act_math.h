@@ -1,0 +1,532 @@
+// act_math.h -- per-element binary32 math of the activations in libmeswish.
+//
+// Every activation is written as a struct with the same device interface:
+//
+//   fwd<P>(x, k, rare)       value at x                       (fast path)
+//   bwd<P>(x, dy, k, rare)   dy times the derivative at x     (fast path)
+//   is_rare<BWD, P>(x, k)    true exactly where the fast path sets `rare`
+//   fwd_rare(x, k), bwd_rare(x, dy, k)   the rare branch, taken per wave
+//
+// P (precise) is true for binary32 I/O, where results must agree with the
+// exact value to 1e-5 relative; bfloat16 I/O needs only 2^-9, so its fast
+// paths skip the extra-precision terms.  The fast paths set `rare` exactly
+// where is_rare is true; the caller then recomputes those elements.
+//
+// Sources, by page title and section:
+//   Swish: blog post "Memory efficient Swish" (adeeplearner.github.io),
+//     "How is Swish implemented?" (x Sigmoid(alpha x)) and "How is the
+//     memory efficient version Swish implemented?" (backward from x alone).
+//   The family: "What activations cost, in memory and in arithmetic",
+//     Given: ReLU, LeakyReLU, sigmoid, tanh, GELU with erf, GELU with the tanh
+//     approximation.  Standard definitions:
+//       ReLU(x) = x > 0 ? x : 0            LeakyReLU(x) = x > 0 ? x : a x
+//       sigmoid(x) = 1 / (1 + e^-x)        tanh(x)
+//       GELU(x) = x Phi(x) = x erfc(-x / sqrt 2) / 2
+//       GELU_tanh(x) = x (1 + tanh u) / 2 = x sigmoid(2u),
+//                      u = sqrt(2/pi) (x + 0.044715 x^3)
+//     Derivatives: 1 or 0; 1 or a; s (1 - s); 1 - tanh^2 = 4E / (1 + E)^2
+//     with E = e^-2|x|; Phi(x) + x phi(x); s (1 + x (1 - s) 2u').
+//
+// Building blocks: the hardware exp2 and reciprocal (v_exp_f32, v_rcp_f32,
+// which flush subnormals), exact hi+lo splits of products (fma), and
+// frexp/ldexp to apply factors below the binary32 normal range with a
+// single rounding at the end.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+namespace meswish {
+
+enum ActKind {
+    kSwish = 0,
+    kRelu = 1,
+    kLeakyRelu = 2,
+    kSigmoid = 3,
+    kTanh = 4,
+    kGeluErf = 5,
+    kGeluTanh = 6,
+    kActCount = 7
+};
+
+// Coefficients prepared on the host (make_coef in meswish.hip).
+struct Coef {
+    float p;       // alpha (Swish) or negative slope (LeakyReLU); unused otherwise
+    float c_hi;    // binary32 nearest to the exponent coefficient C (per activation)
+    float c_lo;    // C - c_hi
+    float aux_hi;  // GELU_tanh: binary32 nearest to 0.044715
+    float aux_lo;  // GELU_tanh: 0.044715 - aux_hi
+};
+
+constexpr float kLn2f = 0.693147180559945309f;
+// |base-2 exponent| beyond which 2^v leaves [2^-125, 2^125].
+constexpr float kMaxExp = 125.0f;
+// Base-2 exponent below which every rare-branch result rounds to zero:
+// its other factors are below 2^(128 + 10) and 2^(138 - 300) < 2^-150.
+constexpr float kZeroExp = -300.0f;
+constexpr float kInvSqrt2f = 0.707106781186547524f;
+constexpr float kInvSqrt2Pif = 0.398942280401432678f;
+constexpr float kGeluTanhK = 1.59576912160573071f;  // 2 sqrt(2/pi)
+
+__device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2f(v); }
+__device__ __forceinline__ float rcp_hw(float v) { return __builtin_amdgcn_rcpf(v); }
+
+// 2^(a C) for the activation's coefficient C.  v receives the binary32
+// exponent a c_hi.  With P the rounding error of v and of c_hi is carried
+// as w = (exact exponent - v) ln 2 and applied as 2^v (1 + w).
+template <bool P>
+__device__ __forceinline__ float exp2_lin(float a, const Coef& k, float& v)
+{
+    v = a * k.c_hi;
+    float e = exp2_hw(v);
+    if (P) {
+        float err = fmaf(a, k.c_hi, -v);  // exact
+        float w = fmaf(a, k.c_lo, err) * kLn2f;
+        e = fmaf(e, w, e);
+    }
+    return e;
+}
+
+// Exponent v = vh + vl (vh the binary32 part) -> 2^v = ef * 2^kf, ef in [1, 2].
+__device__ __forceinline__ void pow2_split(float vh, float vl, float& ef, int& kf)
+{
+    float f = floorf(vh);
+    ef = exp2_hw(vh - f);
+    ef = fmaf(ef, vl * kLn2f, ef);
+    kf = (int)f;
+}
+
+// The exponent a C as a hi+lo pair.
+__device__ __forceinline__ void lin_exponent(float a, const Coef& k, float& vh, float& vl)
+{
+    vh = a * k.c_hi;
+    vl = fmaf(a, k.c_lo, fmaf(a, k.c_hi, -vh));
+}
+
+// m * g * 2^kf * ef rounded once: |frexp mantissa of m * g * ef| stays in the
+// normal range for |g| in [2^-20, 2^10].
+__device__ __forceinline__ float scale_pow2(float m, float g, float ef, int kf)
+{
+    int em;
+    float mm = frexpf(m, &em);
+    return ldexpf(mm * ef * g, em + kf);
+}
+
+// ---------------------------------------------------------------------------
+// Swish: x Sigmoid(t), t = alpha x.  C = -alpha log2 e, so E = 2^(x C) = e^-t.
+// ---------------------------------------------------------------------------
+struct SwishOp {
+    static constexpr bool kHasRare = true;
+
+    template <bool P>
+    __device__ static float fwd(float x, const Coef& k, bool& rare)
+    {
+        float v;
+        float e = exp2_lin<P>(x, k, v);
+        float s = rcp_hw(1.0f + e);
+        rare |= fabsf(v) > kMaxExp;
+        return x * s;
+    }
+
+    template <bool P>
+    __device__ static float bwd(float x, float dy, const Coef& k, bool& rare)
+    {
+        float v;
+        float e = exp2_lin<P>(x, k, v);
+        float s = rcp_hw(1.0f + e);
+        float c = e * s;  // 1 - s without cancellation
+        float g = fmaf(k.p * x, c, 1.0f);
+        rare |= fabsf(v) > kMaxExp;
+        return dy * (s * g);
+    }
+
+    template <bool BWD, bool P>
+    __device__ static bool is_rare(float x, const Coef& k)
+    {
+        return fabsf(x * k.c_hi) > kMaxExp;
+    }
+
+    // |t| > 86.6.  t > 0: Sigmoid(t) rounds to 1, y = x.  t < 0: y = x e^t.
+    __device__ static float fwd_rare(float x, const Coef& k)
+    {
+        if (k.p * x >= 0.0f)
+            return x;
+        float vh, vl, ef;
+        int kf;
+        lin_exponent(x, k, vh, vl);  // = |t| log2 e
+        if (-vh < kZeroExp)
+            return x * 0.0f;
+        pow2_split(-vh, -vl, ef, kf);
+        return scale_pow2(x, 1.0f, ef, kf);
+    }
+
+    // t > 0: dx = dy.  t < 0: 1 - s rounds to 1, dx = dy e^t (1 + t).
+    __device__ static float bwd_rare(float x, float dy, const Coef& k)
+    {
+        float t = k.p * x;
+        if (t >= 0.0f)
+            return dy;
+        float vh, vl, ef;
+        int kf;
+        lin_exponent(x, k, vh, vl);
+        if (-vh < kZeroExp)
+            return dy * -0.0f;
+        pow2_split(-vh, -vl, ef, kf);
+        return scale_pow2(dy, 1.0f + t, ef, kf);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Sigmoid: C = -log2 e, E = e^-x, s = 1 / (1 + E), s' = s (E s).
+// ---------------------------------------------------------------------------
+struct SigmoidOp {
+    static constexpr bool kHasRare = true;
+
+    template <bool P>
+    __device__ static float fwd(float x, const Coef& k, bool& rare)
+    {
+        float v;
+        float e = exp2_lin<P>(x, k, v);
+        // x < -86.6: s is e^x, possibly subnormal.  x > 86.6: s rounds to 1
+        // (and the exponent may have overflowed, which the P terms dislike).
+        rare |= fabsf(v) > kMaxExp;
+        return rcp_hw(1.0f + e);
+    }
+
+    template <bool P>
+    __device__ static float bwd(float x, float dy, const Coef& k, bool& rare)
+    {
+        float v;
+        float e = exp2_lin<P>(x, k, v);
+        float s = rcp_hw(1.0f + e);
+        rare |= fabsf(v) > kMaxExp;
+        return dy * (s * (e * s));
+    }
+
+    template <bool BWD, bool P>
+    __device__ static bool is_rare(float x, const Coef& k)
+    {
+        return fabsf(x * k.c_hi) > kMaxExp;
+    }
+
+    __device__ static float fwd_rare(float x, const Coef& k)
+    {
+        if (x > 0.0f)
+            return 1.0f;
+        float vh, vl, ef;
+        int kf;
+        lin_exponent(x, k, vh, vl);  // = -x log2 e > 125
+        if (-vh < kZeroExp)
+            return 0.0f;
+        pow2_split(-vh, -vl, ef, kf);
+        return ldexpf(ef, kf);
+    }
+
+    // |x| > 86.6: s (1 - s) = e^-|x| (1 + O(e^-|x|)).
+    __device__ static float bwd_rare(float x, float dy, const Coef& k)
+    {
+        float vh, vl, ef;
+        int kf;
+        lin_exponent(fabsf(x), k, vh, vl);  // = -|x| log2 e
+        if (vh < kZeroExp)
+            return dy * 0.0f;
+        pow2_split(vh, vl, ef, kf);
+        return scale_pow2(dy, 1.0f, ef, kf);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// tanh: C = -2 log2 e, E = e^-2|x|.  tanh x = sign(x) (1 - E) / (1 + E) for
+// |x| >= 1/8 (1 - E >= 0.22, no cancellation), the Maclaurin series
+// x - x^3/3 + 2x^5/15 - 17x^7/315 below (truncation < 2e-9 relative).
+// Derivative 1 - tanh^2 = 4 E / (1 + E)^2.
+// ---------------------------------------------------------------------------
+struct TanhOp {
+    static constexpr bool kHasRare = true;
+
+    template <bool P>
+    __device__ static float fwd(float x, const Coef& k, bool& rare)
+    {
+        float a = fabsf(x);
+        float v;
+        float e = exp2_lin<false>(a, k, v);
+        float big = (1.0f - e) * rcp_hw(1.0f + e);
+        float x2 = x * x;
+        float poly = fmaf(x2, -17.0f / 315.0f, 2.0f / 15.0f);
+        poly = fmaf(x2, poly, -1.0f / 3.0f);
+        float small = fmaf(x * x2, poly, x);
+        return a < 0.125f ? small : copysignf(big, x);
+    }
+
+    template <bool P>
+    __device__ static float bwd(float x, float dy, const Coef& k, bool& rare)
+    {
+        float v;
+        float e = exp2_lin<P>(fabsf(x), k, v);
+        float r = rcp_hw(1.0f + e);
+        rare |= v < -kMaxExp;  // |x| > 43.3: 4E below the normal range
+        return dy * (4.0f * e * r * r);
+    }
+
+    template <bool BWD, bool P>
+    __device__ static bool is_rare(float x, const Coef& k)
+    {
+        return BWD && fabsf(x) * k.c_hi < -kMaxExp;
+    }
+
+    __device__ static float fwd_rare(float x, const Coef&) { return x; }  // never taken
+
+    __device__ static float bwd_rare(float x, float dy, const Coef& k)
+    {
+        float vh, vl, ef;
+        int kf;
+        lin_exponent(fabsf(x), k, vh, vl);  // = -2|x| log2 e
+        if (vh < kZeroExp)
+            return dy * 0.0f;
+        pow2_split(vh, vl, ef, kf);
+        return scale_pow2(dy, 4.0f, ef, kf);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// ReLU and LeakyReLU (slope a = k.p): compare and select; NaN propagates.
+// ---------------------------------------------------------------------------
+struct ReluOp {
+    static constexpr bool kHasRare = false;
+
+    template <bool P>
+    __device__ static float fwd(float x, const Coef&, bool&)
+    {
+        return x > 0.0f ? x : x * 0.0f;
+    }
+
+    template <bool P>
+    __device__ static float bwd(float x, float dy, const Coef&, bool&)
+    {
+        return dy * (x > 0.0f ? 1.0f : x * 0.0f);
+    }
+
+    template <bool BWD, bool P>
+    __device__ static bool is_rare(float, const Coef&) { return false; }
+    __device__ static float fwd_rare(float x, const Coef&) { return x; }
+    __device__ static float bwd_rare(float, float dy, const Coef&) { return dy; }
+};
+
+struct LeakyReluOp {
+    static constexpr bool kHasRare = false;
+
+    template <bool P>
+    __device__ static float fwd(float x, const Coef& k, bool&)
+    {
+        return x > 0.0f ? x : k.p * x;
+    }
+
+    template <bool P>
+    __device__ static float bwd(float x, float dy, const Coef& k, bool&)
+    {
+        return dy * (x > 0.0f ? 1.0f : fmaf(0.0f, x, k.p));
+    }
+
+    template <bool BWD, bool P>
+    __device__ static bool is_rare(float, const Coef&) { return false; }
+    __device__ static float fwd_rare(float x, const Coef&) { return x; }
+    __device__ static float bwd_rare(float, float dy, const Coef&) { return dy; }
+};
+
+// ---------------------------------------------------------------------------
+// GELU with erf: Phi(x) = erfc(-x / sqrt 2) / 2 (device erfcf), phi(x) =
+// e^(-x^2/2) / sqrt(2 pi) with C = -log2(e) / 2 on the exact x^2.  For
+// x < -6 the rare branch uses the scaled erfc (erfcx) so that Phi's factor
+// e^(-x^2/2) is applied exactly, by powers of two.
+// ---------------------------------------------------------------------------
+struct GeluErfOp {
+    static constexpr bool kHasRare = true;
+    static constexpr float kRareBelow = -6.0f;
+
+    template <bool P>
+    __device__ static float fwd(float x, const Coef&, bool& rare)
+    {
+        rare |= x < kRareBelow;
+        return x * (0.5f * erfcf(-x * kInvSqrt2f));
+    }
+
+    template <bool P>
+    __device__ static float bwd(float x, float dy, const Coef& k, bool& rare)
+    {
+        float cdf = 0.5f * erfcf(-x * kInvSqrt2f);
+        // phi is even and below 2^-2900 beyond |x| = 64: clamping keeps x^2
+        // finite (NaN still reaches the result through cdf).
+        float xa = fminf(fabsf(x), 64.0f);
+        float x2 = xa * xa;
+        float v = x2 * k.c_hi;
+        float e = exp2_hw(v);
+        if (P) {
+            float x2e = fmaf(xa, xa, -x2);
+            float w = (fmaf(x2, k.c_lo, fmaf(x2, k.c_hi, -v)) + x2e * k.c_hi) * kLn2f;
+            e = fmaf(e, w, e);
+        }
+        rare |= x < kRareBelow;
+        return dy * fmaf(x, e * kInvSqrt2Pif, cdf);
+    }
+
+    template <bool BWD, bool P>
+    __device__ static bool is_rare(float x, const Coef&)
+    {
+        return x < kRareBelow;
+    }
+
+    // e^(-x^2/2) = 2^(x^2 C) with x^2 exact as a hi+lo pair.
+    __device__ static void half_square_exp(float x, const Coef& k, float& vh, float& vl)
+    {
+        float x2 = x * x, x2e = fmaf(x, x, -x2);
+        vh = x2 * k.c_hi;
+        vl = fmaf(x2, k.c_lo, fmaf(x2, k.c_hi, -vh)) + x2e * k.c_hi;
+    }
+
+    // y = x Phi(x) = x erfcx(z) e^(-z^2) / 2, z = -x / sqrt 2 > 4.2.
+    __device__ static float fwd_rare(float x, const Coef& k)
+    {
+        float vh, vl, ef;
+        int kf;
+        half_square_exp(x, k, vh, vl);
+        if (vh < kZeroExp)
+            return x * 0.0f;
+        pow2_split(vh, vl, ef, kf);
+        return scale_pow2(x, 0.5f * erfcxf(-x * kInvSqrt2f), ef, kf);
+    }
+
+    // dx = dy (Phi + x phi) = dy e^(-x^2/2) (erfcx(z) / 2 + x / sqrt(2 pi)).
+    __device__ static float bwd_rare(float x, float dy, const Coef& k)
+    {
+        float vh, vl, ef;
+        int kf;
+        half_square_exp(x, k, vh, vl);
+        if (vh < kZeroExp)
+            return dy * -0.0f;
+        pow2_split(vh, vl, ef, kf);
+        float g = fmaf(0.5f, erfcxf(-x * kInvSqrt2f), x * kInvSqrt2Pif);
+        return scale_pow2(dy, g, ef, kf);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// GELU with the tanh approximation, as x sigmoid(2u): C = -2 sqrt(2/pi) log2 e
+// on a = x (1 + 0.044715 x^2), E = e^-2u.  The binary32 exponent carries
+// about 2 ulps of rounding; with binary32 I/O the fast path is used only
+// where that stays far inside the tolerance (|v| <= 20), and the rare branch
+// carries the exponent as an exact-to-2^-44 hi+lo pair.
+// ---------------------------------------------------------------------------
+struct GeluTanhOp {
+    static constexpr bool kHasRare = true;
+    static constexpr float kPreciseMaxExp = 20.0f;
+
+    // Binary32 I/O: rare outside |v| <= 20 (exponent precision).  bfloat16
+    // I/O: rare outside |v| <= 125 (range; also keeps x (1 - s) 2u' from
+    // forming 0 * inf for huge x).
+    template <bool P>
+    __device__ static bool flag(float v)
+    {
+        return fabsf(v) > (P ? kPreciseMaxExp : kMaxExp);
+    }
+
+    template <bool P>
+    __device__ static float fwd(float x, const Coef& k, bool& rare)
+    {
+        float a = x * fmaf(k.aux_hi * x, x, 1.0f);
+        float v;
+        float e = exp2_lin<false>(a, k, v);
+        rare |= flag<P>(v);
+        return x * rcp_hw(1.0f + e);
+    }
+
+    template <bool P>
+    __device__ static float bwd(float x, float dy, const Coef& k, bool& rare)
+    {
+        float a = x * fmaf(k.aux_hi * x, x, 1.0f);
+        float v;
+        float e = exp2_lin<false>(a, k, v);
+        float s = rcp_hw(1.0f + e);
+        float c = e * s;                                               // 1 - s
+        float du2 = kGeluTanhK * fmaf(3.0f * k.aux_hi * x, x, 1.0f);  // 2 u'
+        float g = fmaf(x * c, du2, 1.0f);
+        rare |= flag<P>(v);
+        return dy * (s * g);
+    }
+
+    template <bool BWD, bool P>
+    __device__ static bool is_rare(float x, const Coef& k)
+    {
+        float a = x * fmaf(k.aux_hi * x, x, 1.0f);
+        return flag<P>(a * k.c_hi);
+    }
+
+    // v = C (x + 0.044715 x^3) as vh + vl.
+    __device__ static void exponent(float x, const Coef& k, float& vh, float& vl)
+    {
+        float x2 = x * x, x2e = fmaf(x, x, -x2);
+        float p = k.aux_hi * x2;
+        float pe = fmaf(k.aux_hi, x2, -p) + fmaf(k.aux_hi, x2e, k.aux_lo * x2);
+        float q = 1.0f + p;  // two-sum of 1 and p
+        float bb = q - 1.0f;
+        float qe = ((1.0f - (q - bb)) + (p - bb)) + pe;
+        float a = x * q;
+        float ae = fmaf(x, q, -a) + x * qe;
+        vh = k.c_hi * a;
+        vl = fmaf(k.c_hi, a, -vh) + fmaf(k.c_hi, ae, k.c_lo * a);
+    }
+
+    __device__ static float fwd_rare(float x, const Coef& k)
+    {
+        float vh, vl;
+        exponent(x, k, vh, vl);
+        if (vh < -kMaxExp)
+            return x;  // sigmoid(2u) rounds to 1
+        if (vh > kMaxExp) {
+            if (-vh < kZeroExp)
+                return x * 0.0f;
+            float ef;
+            int kf;
+            pow2_split(-vh, -vl, ef, kf);  // sigmoid(2u) = e^2u
+            return scale_pow2(x, 1.0f, ef, kf);
+        }
+        float e = exp2_hw(vh);
+        e = fmaf(e, vl * kLn2f, e);
+        return x * rcp_hw(1.0f + e);
+    }
+
+    __device__ static float bwd_rare(float x, float dy, const Coef& k)
+    {
+        float vh, vl;
+        exponent(x, k, vh, vl);
+        float du2 = kGeluTanhK * fmaf(3.0f * k.aux_hi * x, x, 1.0f);
+        if (vh < -kMaxExp)
+            return dy;
+        if (vh > kMaxExp) {
+            if (-vh < kZeroExp)
+                return dy * -0.0f;
+            float ef;
+            int kf;
+            pow2_split(-vh, -vl, ef, kf);
+            // s = e^2u, 1 - s rounds to 1: dx = dy e^2u (1 + x 2u').
+            return scale_pow2(dy, fmaf(x, du2, 1.0f), ef, kf);
+        }
+        float e = exp2_hw(vh);
+        e = fmaf(e, vl * kLn2f, e);
+        float s = rcp_hw(1.0f + e);
+        float g = fmaf(x * (e * s), du2, 1.0f);
+        return dy * (s * g);
+    }
+};
+
+template <int ACT> struct ActOp;
+template <> struct ActOp<kSwish> : SwishOp {};
+template <> struct ActOp<kRelu> : ReluOp {};
+template <> struct ActOp<kLeakyRelu> : LeakyReluOp {};
+template <> struct ActOp<kSigmoid> : SigmoidOp {};
+template <> struct ActOp<kTanh> : TanhOp {};
+template <> struct ActOp<kGeluErf> : GeluErfOp {};
+template <> struct ActOp<kGeluTanh> : GeluTanhOp {};
+
+}  // namespace meswish

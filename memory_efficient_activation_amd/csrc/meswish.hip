@@ -7,7 +7,9 @@
 //                                                          dx = dy * s * (1 + t (1 - s))
 // with t = alpha x and s = Sigmoid(t) = 1 / (1 + e^-t) ("What is a Swish
 // activation function?").  The backward reads only x and dy: the input is
-// the one tensor kept between the passes.
+// the one tensor kept between the passes.  The same save-the-input skeleton
+// serves the activation family of "What activations cost, in memory and in
+// arithmetic" (Given); the per-element math of each is in act_math.h.
 //
 // Design for MI355X (CDNA4):
 //   * The work is element-wise with an arithmetic intensity of about one to
@@ -16,24 +18,23 @@
 //     chip's vector ALUs, so HBM bandwidth is the bound: no LDS, no MFMA, no
 //     atomics, no barriers.  Each lane moves 16-byte vectors (4 binary32 or
 //     8 bfloat16), a wave touches 1 KiB contiguous per access, and a thread
-//     issues all its loads of an iteration before any arithmetic.
+//     issues all its loads of a tile before any arithmetic.
 //   * One tile of kBlock x kUnroll vectors per block, one block
 //     per tile (the dispatcher keeps all 256 CUs of the 8 XCDs busy and
 //     balances the tail); the loop over tiles only matters when the grid
 //     is capped.  Tile shape and cache policy (non-temporal loads/stores
 //     per stream) were chosen by measurement on MI355X.
 //   * Arithmetic is binary32 with the hardware exp2 and reciprocal
-//     (v_exp_f32, v_rcp_f32): E = e^-t = 2^(-t log2 e), s = 1 / (1 + E),
-//     1 - s = E s.  Both s and 1 - s come out with small relative error for
-//     every t (no cancellation), the forward costs one exp, one reciprocal
-//     and three multiply/adds per element, and the backward four more.
-//   * binary32 I/O: the exponent -alpha x log2 e is carried as a hi+lo pair
-//     so that E keeps binary32 accuracy up to |alpha x| ~ 87.
-//   * |alpha x| > 86.6 (E outside [2^-125, 2^125]) takes a rare branch:
-//     there s or 1 - s rounds to exactly 1, and the small factor
-//     e^-|alpha x| is applied by powers of two (frexp/ldexp) so that
-//     subnormal results round once and keep gradual underflow (the hardware
-//     transcendentals flush subnormals).
+//     (v_exp_f32, v_rcp_f32).  For Swish: E = e^-t = 2^(-t log2 e),
+//     s = 1 / (1 + E), 1 - s = E s.  Both s and 1 - s come out with small
+//     relative error for every t (no cancellation); the forward costs one
+//     exp, one reciprocal and three multiply/adds per element.
+//   * binary32 I/O: exponents are carried as hi+lo pairs where the result's
+//     accuracy depends on them.
+//   * Results whose exponential leaves [2^-125, 2^125] take a rare branch,
+//     per wave, that applies small factors by powers of two (frexp/ldexp)
+//     so that subnormal results round once and keep gradual underflow (the
+//     hardware transcendentals flush subnormals).
 //   * bfloat16 I/O: widening is a 16-bit shift; narrowing is the gfx950
 //     v_cvt_pk_bf16_f32 (round to nearest even), two elements per op.
 
@@ -46,6 +47,7 @@
 #include <atomic>
 
 #include "meswish.h"
+#include "act_math.h"
 
 // Threads per block, per element type.
 #ifndef MESWISH_BLOCK_BF16
@@ -109,135 +111,6 @@ namespace meswish {
 constexpr int kCopyBlock = MESWISH_COPY_BLOCK;
 constexpr int kCopyUnroll = MESWISH_COPY_UNROLL;
 constexpr int kCopyTileVecs = kCopyBlock * kCopyUnroll;
-
-// ---------------------------------------------------------------------------
-// Coefficients prepared on the host.
-// ---------------------------------------------------------------------------
-
-struct Coef {
-    float alpha;      // alpha
-    float c_hi;       // binary32 nearest to -alpha log2(e)
-    float c_lo_ln2;   // (-alpha log2(e) - c_hi) * ln 2
-};
-
-static Coef make_coef(float alpha)
-{
-    const double log2e = 1.44269504088896340735992468100189214;
-    const double ln2 = 0.693147180559945309417232121458176568;
-    double c = -(double)alpha * log2e;
-    float hi = (float)c;
-    Coef k;
-    k.alpha = alpha;
-    k.c_hi = hi;
-    k.c_lo_ln2 = (float)((c - (double)hi) * ln2);
-    return k;
-}
-
-// ---------------------------------------------------------------------------
-// Element math.
-// ---------------------------------------------------------------------------
-
-constexpr float kLn2f = 0.693147180559945309f;
-// |exponent| above which E = 2^v leaves [2^-125, 2^125]: then the rare
-// branch takes over (|alpha x| > 86.6).
-constexpr float kMaxExp = 125.0f;
-// Below this base-2 exponent every result of the rare branch rounds to zero:
-// |x|, |dy| < 2^128, |1 + t| < 2^9 and 2^(128 + 9 + 1 - 300) < 2^-150.
-constexpr float kZeroExp = -300.0f;
-
-__device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2f(v); }
-__device__ __forceinline__ float rcp_hw(float v) { return __builtin_amdgcn_rcpf(v); }
-
-// E = e^(-alpha x) = 2^v, v = x * (-alpha log2 e).  With kPrecise the
-// rounding error of v (and of the binary32 coefficient) is carried as
-// w = (exact v - v) ln 2 and applied as E (1 + w).  The caller flags
-// |v| > kMaxExp for the rare branch.
-template <bool kPrecise>
-__device__ __forceinline__ float exp_neg_t(float x, const Coef& k, float& v)
-{
-    v = x * k.c_hi;
-    float e = exp2_hw(v);
-    if (kPrecise) {
-        float err = fmaf(x, k.c_hi, -v);               // exact error of v
-        float w = fmaf(x, k.c_lo_ln2, err * kLn2f);     // rest of the exponent, times ln 2
-        e = fmaf(e, w, e);
-    }
-    return e;
-}
-
-template <bool kPrecise>
-__device__ __forceinline__ float fwd_fast(float x, const Coef& k, bool& rare)
-{
-    float v;
-    float e = exp_neg_t<kPrecise>(x, k, v);
-    float s = rcp_hw(1.0f + e);  // Sigmoid(alpha x)
-    rare |= fabsf(v) > kMaxExp;
-    return x * s;
-}
-
-template <bool kPrecise>
-__device__ __forceinline__ float bwd_fast(float x, float dy, const Coef& k, bool& rare)
-{
-    float v;
-    float e = exp_neg_t<kPrecise>(x, k, v);
-    float s = rcp_hw(1.0f + e);  // Sigmoid(t)
-    float c = e * s;             // 1 - Sigmoid(t), without cancellation
-    float g = fmaf(k.alpha * x, c, 1.0f);
-    rare |= fabsf(v) > kMaxExp;
-    return dy * (s * g);
-}
-
-__device__ __forceinline__ bool is_rare(float x, const Coef& k)
-{
-    return fabsf(x * k.c_hi) > kMaxExp;
-}
-
-// The rare branch, |t| > 86.6 with t = alpha x.  For t > 0, Sigmoid(t)
-// rounds to 1 and t (1 - Sigmoid(t)) to 0: y = x and dx = dy.  For t < 0,
-// 1 - Sigmoid(t) rounds to 1 and Sigmoid(t) = e^t = ef * 2^kf with ef in
-// [1, 2]: the result is assembled as (mantissa product) * 2^(exponents) so
-// that it is rounded once, at the end, even when it is subnormal.
-__device__ __forceinline__ void small_sigmoid(float x, const Coef& k, float& ef, int& kf)
-{
-    float v = x * k.c_hi;                          // = |t| log2 e here
-    float err = fmaf(x, k.c_hi, -v);
-    float w = fmaf(x, k.c_lo_ln2, err * kLn2f);    // e^t = 2^(-v) (1 - w)
-    float vh = -v;
-    float f = floorf(vh);
-    ef = exp2_hw(vh - f);
-    ef = fmaf(ef, -w, ef);
-    kf = (int)f;
-}
-
-__device__ __forceinline__ float fwd_rare(float x, const Coef& k)
-{
-    if (k.alpha * x >= 0.0f)
-        return x;
-    if (-(x * k.c_hi) < kZeroExp)
-        return x * 0.0f;
-    float ef;
-    int kf;
-    small_sigmoid(x, k, ef, kf);
-    int ex;
-    float mx = frexpf(x, &ex);
-    return ldexpf(mx * ef, ex + kf);
-}
-
-__device__ __forceinline__ float bwd_rare(float x, float dy, const Coef& k)
-{
-    float t = k.alpha * x;
-    if (t >= 0.0f)
-        return dy;
-    if (-(x * k.c_hi) < kZeroExp)
-        return dy * -0.0f;
-    float ef;
-    int kf;
-    small_sigmoid(x, k, ef, kf);
-    float g = 1.0f + t;  // 1 + t (1 - s) with 1 - s rounding to 1
-    int ed;
-    float md = frexpf(dy, &ed);
-    return ldexpf(md * ef * g, ed + kf);
-}
 
 // ---------------------------------------------------------------------------
 // Element types.
@@ -349,63 +222,69 @@ __device__ __forceinline__ void st16(uint4* p, const uint4& v)
 
 constexpr int kNtCopy = MESWISH_NT_COPY;
 
-// One 16-byte vector of the forward / backward.
-template <typename IO>
+// One 16-byte vector of the forward / backward of activation ACT.
+template <typename IO, int ACT>
 __device__ __forceinline__ uint4 fwd_vec(const uint4& xv, const Coef& k)
 {
+    using Op = ActOp<ACT>;
     constexpr int E = Io<IO>::kPerVec;
+    constexpr bool P = Io<IO>::kPrecise;
     float xf[E], yf[E];
     Io<IO>::unpack(xv, xf);
     bool rare = false;
 #pragma unroll
     for (int j = 0; j < E; ++j)
-        yf[j] = fwd_fast<Io<IO>::kPrecise>(xf[j], k, rare);
-    if (__builtin_expect(rare, 0)) {
+        yf[j] = Op::template fwd<P>(xf[j], k, rare);
+    if (Op::kHasRare && __builtin_expect(rare, 0)) {
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            if (is_rare(xf[j], k))
-                yf[j] = fwd_rare(xf[j], k);
+            if (Op::template is_rare<false, P>(xf[j], k))
+                yf[j] = Op::fwd_rare(xf[j], k);
     }
     return Io<IO>::pack(yf);
 }
 
-template <typename IO>
+template <typename IO, int ACT>
 __device__ __forceinline__ uint4 bwd_vec(const uint4& xv, const uint4& dv, const Coef& k)
 {
+    using Op = ActOp<ACT>;
     constexpr int E = Io<IO>::kPerVec;
+    constexpr bool P = Io<IO>::kPrecise;
     float xf[E], df[E], gf[E];
     Io<IO>::unpack(xv, xf);
     Io<IO>::unpack(dv, df);
     bool rare = false;
 #pragma unroll
     for (int j = 0; j < E; ++j)
-        gf[j] = bwd_fast<Io<IO>::kPrecise>(xf[j], df[j], k, rare);
-    if (__builtin_expect(rare, 0)) {
+        gf[j] = Op::template bwd<P>(xf[j], df[j], k, rare);
+    if (Op::kHasRare && __builtin_expect(rare, 0)) {
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            if (is_rare(xf[j], k))
-                gf[j] = bwd_rare(xf[j], df[j], k);
+            if (Op::template is_rare<true, P>(xf[j], k))
+                gf[j] = Op::bwd_rare(xf[j], df[j], k);
     }
     return Io<IO>::pack(gf);
 }
 
 // One element (head, tail and unaligned paths).
-template <typename IO, bool kBwd>
+template <typename IO, bool kBwd, int ACT>
 __device__ __forceinline__ void one_element(const IO* x, const IO* dy, IO* out, int64_t i,
                                             const Coef& k)
 {
+    using Op = ActOp<ACT>;
+    constexpr bool P = Io<IO>::kPrecise;
     float xv = Io<IO>::load1(x, i);
     bool rare = false;
     float r;
     if (kBwd) {
         float dv = Io<IO>::load1(dy, i);
-        r = bwd_fast<Io<IO>::kPrecise>(xv, dv, k, rare);
-        if (rare)
-            r = bwd_rare(xv, dv, k);
+        r = Op::template bwd<P>(xv, dv, k, rare);
+        if (Op::kHasRare && rare)
+            r = Op::bwd_rare(xv, dv, k);
     } else {
-        r = fwd_fast<Io<IO>::kPrecise>(xv, k, rare);
-        if (rare)
-            r = fwd_rare(xv, k);
+        r = Op::template fwd<P>(xv, k, rare);
+        if (Op::kHasRare && rare)
+            r = Op::fwd_rare(xv, k);
     }
     Io<IO>::store1(out, i, r);
 }
@@ -413,7 +292,7 @@ __device__ __forceinline__ void one_element(const IO* x, const IO* dy, IO* out, 
 // Vectors [v_begin, v_end) of the 16-byte-aligned body starting at x, dy, out
 // (already offset past the head), processed by this block as tiles of
 // tile_vecs<IO>() vectors.
-template <typename IO, bool kBwd, int kNt = NtPolicy<IO, kBwd>::kMask>
+template <typename IO, bool kBwd, int ACT, int kNt = NtPolicy<IO, kBwd>::kMask>
 __device__ __forceinline__ void body_tile(const uint4* xv, const uint4* dv, uint4* ov,
                                           int64_t tile_first, int64_t nvec, const Coef& k)
 {
@@ -436,7 +315,7 @@ __device__ __forceinline__ void body_tile(const uint4* xv, const uint4* dv, uint
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
             st16<(kNt & 4) != 0>(ov + i + u * kBlock,
-                                  kBwd ? bwd_vec<IO>(a[u], b[u], k) : fwd_vec<IO>(a[u], k));
+                                  kBwd ? bwd_vec<IO, ACT>(a[u], b[u], k) : fwd_vec<IO, ACT>(a[u], k));
     } else {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -445,9 +324,9 @@ __device__ __forceinline__ void body_tile(const uint4* xv, const uint4* dv, uint
                 uint4 a = ld16<(kNt & 1) != 0>(xv + j);
                 uint4 r;
                 if (kBwd)
-                    r = bwd_vec<IO>(a, ld16<(kNt & 2) != 0>(dv + j), k);
+                    r = bwd_vec<IO, ACT>(a, ld16<(kNt & 2) != 0>(dv + j), k);
                 else
-                    r = fwd_vec<IO>(a, k);
+                    r = fwd_vec<IO, ACT>(a, k);
                 st16<(kNt & 4) != 0>(ov + j, r);
             }
         }
@@ -460,8 +339,8 @@ __device__ __forceinline__ void body_tile(const uint4* xv, const uint4* dv, uint
 
 // Single tensor, all pointers congruent modulo 16 bytes: `head` scalar
 // elements, then nvec 16-byte vectors, then `tail` scalar elements.
-template <typename IO, bool kBwd>
-__global__ MESWISH_BOUNDS void swish_vec_kernel(const IO* x, const IO* dy, IO* out,
+template <typename IO, bool kBwd, int ACT>
+__global__ MESWISH_BOUNDS void act_vec_kernel(const IO* x, const IO* dy, IO* out,
                                                            int64_t head, int64_t nvec,
                                                            int64_t tail, Coef k)
 {
@@ -477,23 +356,23 @@ __global__ MESWISH_BOUNDS void swish_vec_kernel(const IO* x, const IO* dy, IO* o
         b = (b & 7) * (gridDim.x >> 3) + (b >> 3);
 #endif
     for (int64_t t0 = b * kTileVecs; t0 < nvec; t0 += stride)
-        body_tile<IO, kBwd>(xv, dv, ov, t0, nvec, k);
+        body_tile<IO, kBwd, ACT>(xv, dv, ov, t0, nvec, k);
     if (blockIdx.x == 0 && threadIdx.x < head + tail) {
         int64_t i = threadIdx.x < head ? (int64_t)threadIdx.x
                                        : head + nvec * E + (threadIdx.x - head);
-        one_element<IO, kBwd>(x, dy, out, i, k);
+        one_element<IO, kBwd, ACT>(x, dy, out, i, k);
     }
 }
 
 // Single tensor, element by element (pointers not congruent modulo 16).
-template <typename IO, bool kBwd>
-__global__ MESWISH_BOUNDS void swish_elem_kernel(const IO* x, const IO* dy, IO* out,
+template <typename IO, bool kBwd, int ACT>
+__global__ MESWISH_BOUNDS void act_elem_kernel(const IO* x, const IO* dy, IO* out,
                                                             int64_t n, Coef k)
 {
     constexpr int kBlock = Io<IO>::kBlock;
     const int64_t stride = (int64_t)gridDim.x * kBlock;
     for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride)
-        one_element<IO, kBwd>(x, dy, out, i, k);
+        one_element<IO, kBwd, ACT>(x, dy, out, i, k);
 }
 
 // Grouped: up to MESWISH_MAX_GROUP tensors in one launch.  Tensor j covers
@@ -513,8 +392,8 @@ struct GroupArgs {
     int32_t count;
 };
 
-template <typename IO, bool kBwd>
-__global__ MESWISH_BOUNDS void swish_group_kernel(GroupArgs g, Coef k)
+template <typename IO, bool kBwd, int ACT>
+__global__ MESWISH_BOUNDS void act_group_kernel(GroupArgs g, Coef k)
 {
     constexpr int E = Io<IO>::kPerVec;
     constexpr int kUnroll = Io<IO>::kUnroll;
@@ -536,19 +415,19 @@ __global__ MESWISH_BOUNDS void swish_group_kernel(GroupArgs g, Coef k)
             for (int u = 0; u < kUnroll; ++u) {
                 int64_t i = e0 + u * Io<IO>::kBlock + threadIdx.x;
                 if (i < n)
-                    one_element<IO, kBwd>(x, dy, out, i, k);
+                    one_element<IO, kBwd, ACT>(x, dy, out, i, k);
             }
             continue;
         }
         const int64_t nvec = (n - head) / E;
         const int64_t tail = n - head - nvec * E;
-        body_tile<IO, kBwd>(reinterpret_cast<const uint4*>(x + head),
+        body_tile<IO, kBwd, ACT>(reinterpret_cast<const uint4*>(x + head),
                             kBwd ? reinterpret_cast<const uint4*>(dy + head) : nullptr,
                             reinterpret_cast<uint4*>(out + head), local * kTileVecs, nvec, k);
         if (local == 0 && threadIdx.x < head + tail) {
             int64_t i = threadIdx.x < head ? (int64_t)threadIdx.x
                                            : head + nvec * E + (threadIdx.x - head);
-            one_element<IO, kBwd>(x, dy, out, i, k);
+            one_element<IO, kBwd, ACT>(x, dy, out, i, k);
         }
     }
 }
@@ -644,6 +523,41 @@ static int64_t head_elems(const void* p, size_t esize)
     return mis ? (int64_t)((16u - mis) / esize) : 0;
 }
 
+// Per-activation coefficients (see Coef in act_math.h).
+static Coef make_coef(int act, float p)
+{
+    const double log2e = 1.44269504088896340735992468100189214;
+    const double sqrt_2_over_pi = 0.797884560802865355879892119868763737;
+    double c = 0.0;
+    switch (act) {
+    case kSwish:
+        c = -(double)p * log2e;  // e^-(p x)
+        break;
+    case kSigmoid:
+        c = -log2e;  // e^-x
+        break;
+    case kTanh:
+        c = -2.0 * log2e;  // e^-2|x|
+        break;
+    case kGeluErf:
+        c = -0.5 * log2e;  // e^-(x^2 / 2)
+        break;
+    case kGeluTanh:
+        c = -2.0 * sqrt_2_over_pi * log2e;  // e^-2u over x (1 + 0.044715 x^2)
+        break;
+    default:
+        break;
+    }
+    const double cubic = 0.044715;
+    Coef k;
+    k.p = p;
+    k.c_hi = (float)c;
+    k.c_lo = (float)(c - (double)k.c_hi);
+    k.aux_hi = (float)cubic;
+    k.aux_lo = (float)(cubic - (double)k.aux_hi);
+    return k;
+}
+
 // How one tensor is split between the kernels' paths (see meswish_plan_t).
 template <typename IO, bool kBwd>
 static meswish_plan_t make_plan(const void* x, const void* dy, const void* out, size_t n)
@@ -676,7 +590,7 @@ static meswish_plan_t make_plan(const void* x, const void* dy, const void* out, 
     return p;
 }
 
-template <typename IO, bool kBwd>
+template <typename IO, bool kBwd, int ACT>
 static int run_single(const void* x, const void* dy, void* out, size_t n, Coef k,
                       hipStream_t stream)
 {
@@ -687,13 +601,47 @@ static int run_single(const void* x, const void* dy, void* out, size_t n, Coef k
     int64_t head = p.head, nvec = p.nvec, tail = p.tail;
     if (p.path == MESWISH_PATH_VECTOR) {
         void* args[] = {&xp, &dp, &op, &head, &nvec, &tail, &k};
-        return launch(reinterpret_cast<const void*>(&swish_vec_kernel<IO, kBwd>), p.grid, args,
+        return launch(reinterpret_cast<const void*>(&act_vec_kernel<IO, kBwd, ACT>), p.grid, args,
                       stream, (int)p.block);
     }
     int64_t nn = (int64_t)n;
     void* args[] = {&xp, &dp, &op, &nn, &k};
-    return launch(reinterpret_cast<const void*>(&swish_elem_kernel<IO, kBwd>), p.grid, args,
+    return launch(reinterpret_cast<const void*>(&act_elem_kernel<IO, kBwd, ACT>), p.grid, args,
                   stream, (int)p.block);
+}
+
+template <bool kBwd, int ACT>
+static int run_dtype(int dtype, const void* x, const void* dy, void* out, size_t n, Coef k,
+                     hipStream_t s)
+{
+    if (dtype == MESWISH_F32)
+        return run_single<float, kBwd, ACT>(x, dy, out, n, k, s);
+    return run_single<bf16_t, kBwd, ACT>(x, dy, out, n, k, s);
+}
+
+template <bool kBwd>
+static int run_act(int act, int dtype, const void* x, const void* dy, void* out, size_t n,
+                   float p, hipStream_t s)
+{
+    const Coef k = make_coef(act, p);
+    switch (act) {
+    case kSwish:
+        return run_dtype<kBwd, kSwish>(dtype, x, dy, out, n, k, s);
+    case kRelu:
+        return run_dtype<kBwd, kRelu>(dtype, x, dy, out, n, k, s);
+    case kLeakyRelu:
+        return run_dtype<kBwd, kLeakyRelu>(dtype, x, dy, out, n, k, s);
+    case kSigmoid:
+        return run_dtype<kBwd, kSigmoid>(dtype, x, dy, out, n, k, s);
+    case kTanh:
+        return run_dtype<kBwd, kTanh>(dtype, x, dy, out, n, k, s);
+    case kGeluErf:
+        return run_dtype<kBwd, kGeluErf>(dtype, x, dy, out, n, k, s);
+    case kGeluTanh:
+        return run_dtype<kBwd, kGeluTanh>(dtype, x, dy, out, n, k, s);
+    default:
+        return MESWISH_EINVAL;
+    }
 }
 
 template <typename IO, bool kBwd>
@@ -722,7 +670,7 @@ static int run_group(GroupArgs& g, Coef k, hipStream_t stream)
         return MESWISH_OK;
     int64_t grid = grid_for_tiles(tiles);
     void* args[] = {&g, &k};
-    return launch(reinterpret_cast<const void*>(&swish_group_kernel<IO, kBwd>), grid, args,
+    return launch(reinterpret_cast<const void*>(&act_group_kernel<IO, kBwd, kSwish>), grid, args,
                   stream, Io<IO>::kBlock);
 }
 
@@ -772,29 +720,37 @@ static int check_single(const void* x, const void* dy, const void* out, size_t n
 
 }  // namespace meswish
 
-extern "C" int swish_fwd(const void* x, void* y, size_t n, float alpha, int dtype, void* stream)
+extern "C" int meswish_act_fwd(int act, const void* x, void* y, size_t n, float param, int dtype,
+                               void* stream)
 {
-    int rc = check_single(x, nullptr, y, n, alpha, dtype, false);
+    if (act < 0 || act >= kActCount)
+        return MESWISH_EINVAL;
+    int rc = check_single(x, nullptr, y, n, param, dtype, false);
     if (rc != MESWISH_OK || n == 0)
         return rc;
-    Coef k = make_coef(alpha);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (dtype == MESWISH_F32)
-        return run_single<float, false>(x, nullptr, y, n, k, s);
-    return run_single<bf16_t, false>(x, nullptr, y, n, k, s);
+    return run_act<false>(act, dtype, x, nullptr, y, n, param, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int meswish_act_bwd(int act, const void* x, const void* dy, void* dx, size_t n,
+                               float param, int dtype, void* stream)
+{
+    if (act < 0 || act >= kActCount)
+        return MESWISH_EINVAL;
+    int rc = check_single(x, dy, dx, n, param, dtype, true);
+    if (rc != MESWISH_OK || n == 0)
+        return rc;
+    return run_act<true>(act, dtype, x, dy, dx, n, param, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int swish_fwd(const void* x, void* y, size_t n, float alpha, int dtype, void* stream)
+{
+    return meswish_act_fwd(kSwish, x, y, n, alpha, dtype, stream);
 }
 
 extern "C" int swish_bwd(const void* x, const void* dy, void* dx, size_t n, float alpha, int dtype,
                          void* stream)
 {
-    int rc = check_single(x, dy, dx, n, alpha, dtype, true);
-    if (rc != MESWISH_OK || n == 0)
-        return rc;
-    Coef k = make_coef(alpha);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (dtype == MESWISH_F32)
-        return run_single<float, true>(x, dy, dx, n, k, s);
-    return run_single<bf16_t, true>(x, dy, dx, n, k, s);
+    return meswish_act_bwd(kSwish, x, dy, dx, n, alpha, dtype, stream);
 }
 
 extern "C" int meswish_plan(const void* x, const void* dy, const void* out, size_t n, float alpha,
@@ -887,7 +843,7 @@ extern "C" int swish_fwd_grouped(const meswish_fwd_desc* desc, int count, float 
     memset(&g, 0, sizeof g);
     if ((rc = fill_group(g, count, in1, nullptr, out, n, dtype)) != MESWISH_OK)
         return rc;
-    Coef k = make_coef(alpha);
+    Coef k = make_coef(kSwish, alpha);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == MESWISH_F32)
         return run_group<float, false>(g, k, s);
@@ -920,7 +876,7 @@ extern "C" int swish_bwd_grouped(const meswish_bwd_desc* desc, int count, float 
     memset(&g, 0, sizeof g);
     if ((rc = fill_group(g, count, in1, in2, out, n, dtype)) != MESWISH_OK)
         return rc;
-    Coef k = make_coef(alpha);
+    Coef k = make_coef(kSwish, alpha);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == MESWISH_F32)
         return run_group<float, true>(g, k, s);

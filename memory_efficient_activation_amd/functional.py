@@ -148,6 +148,51 @@ def swish_bwd_grouped(xs: Sequence[torch.Tensor], dys: Sequence[torch.Tensor], a
     return dxs
 
 
+def _act_code(kind: str) -> int:
+    try:
+        return _lib.ACTS[kind]
+    except KeyError:
+        raise ValueError(f"unknown activation {kind!r}; one of {sorted(_lib.ACTS)}") from None
+
+
+def act_fwd(kind: str, x: torch.Tensor, param: float | None = None,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = f(x) for an activation of the family ("What activations cost, in
+    memory and in arithmetic", Given): swish, relu, leaky_relu, sigmoid,
+    tanh, gelu (erf), gelu_tanh.  ``param`` is Swish's alpha (default 1) or
+    LeakyReLU's negative slope (default 0.01)."""
+    code = _act_code(kind)
+    p = _lib.DEFAULT_PARAM.get(kind, 0.0) if param is None else float(param)
+    _require_device(x, "x")
+    dt = _dtype_code(x)
+    x = x.contiguous()
+    y = _out(x, out, "out")
+    with torch.cuda.device(x.device):
+        st = _lib.library().meswish_act_fwd(code, x.data_ptr(), y.data_ptr(), x.numel(), p, dt,
+                                            _stream(x.device))
+    _lib.check(st, f"meswish_act_fwd({kind})")
+    return y
+
+
+def act_bwd(kind: str, x: torch.Tensor, dy: torch.Tensor, param: float | None = None,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    """dx = dy f'(x), recomputed from the saved input x alone."""
+    code = _act_code(kind)
+    p = _lib.DEFAULT_PARAM.get(kind, 0.0) if param is None else float(param)
+    _require_device(x, "x")
+    _require_device(dy, "dy")
+    _same(x, dy, "x", "dy")
+    dt = _dtype_code(x)
+    x = x.contiguous()
+    dy = dy.contiguous()
+    dx = _out(x, out, "out")
+    with torch.cuda.device(x.device):
+        st = _lib.library().meswish_act_bwd(code, x.data_ptr(), dy.data_ptr(), dx.data_ptr(),
+                                            x.numel(), p, dt, _stream(x.device))
+    _lib.check(st, f"meswish_act_bwd({kind})")
+    return dx
+
+
 def copy_bytes(src: torch.Tensor, dst: torch.Tensor) -> None:
     """Plain 16-byte-vector device copy (bandwidth ceiling and counter calibration)."""
     _require_device(src, "src")

@@ -17,7 +17,7 @@ from __future__ import annotations
 import torch
 from torch import nn
 
-from .functional import swish_bwd, swish_fwd
+from .functional import act_bwd, act_fwd, swish_bwd, swish_fwd
 
 
 class SwishFn(torch.autograd.Function):
@@ -52,3 +52,39 @@ class MemoryEfficientSwish(nn.Module):
 
     def extra_repr(self) -> str:
         return f"alpha={self.alpha}"
+
+
+class ActFn(torch.autograd.Function):
+    """Any activation of the family, keeping only the input for backward."""
+
+    @staticmethod
+    def forward(ctx, x: torch.Tensor, kind: str, param: float | None = None) -> torch.Tensor:
+        y = act_fwd(kind, x, param)
+        ctx.save_for_backward(x)
+        ctx.kind = kind
+        ctx.param = param
+        return y
+
+    @staticmethod
+    def backward(ctx, dy: torch.Tensor):
+        (x,) = ctx.saved_tensors
+        return act_bwd(ctx.kind, x, dy, ctx.param), None, None
+
+
+class MemoryEfficientActivation(nn.Module):
+    """Activation module (swish, relu, leaky_relu, sigmoid, tanh, gelu,
+    gelu_tanh) that keeps one tensor -- its input -- for the backward."""
+
+    def __init__(self, kind: str, param: float | None = None):
+        super().__init__()
+        from ._lib import ACTS
+        if kind not in ACTS:
+            raise ValueError(f"unknown activation {kind!r}; one of {sorted(ACTS)}")
+        self.kind = kind
+        self.param = param
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        return ActFn.apply(x, self.kind, self.param)
+
+    def extra_repr(self) -> str:
+        return f"kind={self.kind}, param={self.param}"

@@ -42,6 +42,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
+        "meswish_act_bwd", "meswish_act_fwd",
         "meswish_copy", "meswish_plan", "meswish_strerror", "meswish_version", "swish_bwd",
         "swish_bwd_grouped", "swish_fwd", "swish_fwd_grouped"])
 
@@ -62,6 +63,9 @@ def test_binding_constants_match_header(lib):
                   "MESWISH_EALIAS": _lib.EALIAS, "MESWISH_EHIP": _lib.EHIP,
                   "MESWISH_ETOOMANY": _lib.ETOOMANY}
     assert declared_enum("meswish_dtype") == {"MESWISH_F32": _lib.F32, "MESWISH_BF16": _lib.BF16}
+    acts = declared_enum("meswish_act")
+    assert {k[len("MESWISH_ACT_"):].lower(): v for k, v in acts.items()} == {
+        ("gelu_erf" if k == "gelu" else k): v for k, v in _lib.ACTS.items()}
     m = re.search(r"#define MESWISH_MAX_GROUP (\d+)", _header_text())
     assert int(m.group(1)) == _lib.MAX_GROUP
     assert set(_lib.EXPORTED) == set(declared_functions())
@@ -104,6 +108,11 @@ def test_rejections_before_launch(lib):
     assert lib.swish_fwd_grouped(d, 65, 1.0, _lib.F32, None) == _lib.ETOOMANY
     b = (_lib.BwdDesc * 65)()
     assert lib.swish_bwd_grouped(b, 65, 1.0, _lib.BF16, None) == _lib.ETOOMANY
+    # Unknown activation; non-finite parameter.
+    assert lib.meswish_act_fwd(7, None, None, 16, 1.0, _lib.F32, None) == _lib.EINVAL
+    assert lib.meswish_act_bwd(-1, None, None, None, 16, 1.0, _lib.F32, None) == _lib.EINVAL
+    assert lib.meswish_act_fwd(2, None, None, 16, nan, _lib.F32, None) == _lib.EINVAL
+    assert lib.meswish_act_fwd(4, None, None, 0, 1.0, _lib.BF16, None) == _lib.OK
     # Copy helper: misaligned or odd sizes.
     assert lib.meswish_copy(None, None, 0, None) == _lib.OK
     assert lib.meswish_copy(None, None, 16, None) == _lib.EINVAL
