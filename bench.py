@@ -25,6 +25,10 @@ Also reported (one JSON line on stdout):
                 workload, same algorithmic bytes.
   copy_ceiling  a plain 16-byte copy kernel (read one tensor, write one).
   bytes_retained  bytes kept for the backward: x only, vs 3 maps (naive).
+
+``--act KIND`` measures another activation of the family of the same page
+(relu, leaky_relu, sigmoid, tanh, gelu, gelu_tanh) on the same workload;
+``--act all`` prints one line per activation, Swish first.
 """
 
 from __future__ import annotations
@@ -44,9 +48,16 @@ if ROOT not in sys.path:
 
 METRIC = "HBM GB/s + fraction of peak, Swish fwd+bwd, 67M-elem bf16, 1 MI355X"
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD public specification
-KERNEL_SOURCE = os.path.join(ROOT, "memory_efficient_activation_amd", "csrc", "meswish.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "memory_efficient_activation_amd", "csrc", f)
+                  for f in ("meswish.hip", "act_math.h")]
 SETS = 4
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "swish_bwd_bf16_8x2048x4096_traffic.md")
+FAMILY = ["swish", "relu", "leaky_relu", "sigmoid", "tanh", "gelu", "gelu_tanh"]
+ORACLE_NAME = {"gelu": "gelu_erf"}
+# Flops per element of each activation as "What activations cost, in memory
+# and in arithmetic" (Given) counts them, forward; Swish is sigmoid + 2.
+PAGE_FLOPS = {"swish": 6, "relu": 1, "leaky_relu": 2, "sigmoid": 4, "tanh": 6, "gelu": 12,
+              "gelu_tanh": 8}
 
 
 def log(*a):
@@ -58,6 +69,8 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--act", default="swish", choices=FAMILY + ["all"],
+                   help="activation to measure (default swish, the headline)")
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the CPU oracle timing (profiling runs)")
     p.add_argument("--no-extras", action="store_true",
@@ -67,13 +80,16 @@ def parse_args():
 
 
 def source_sha256() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def traffic_from_profile():
     """HBM bytes per backward launch measured by rocprofv3 counters, if the
-    committed summary was taken on the current kernel source."""
+    committed summary was taken on the current kernel sources."""
     if not os.path.exists(TRAFFIC_PROFILE):
         return None, "no counter summary"
     text = open(TRAFFIC_PROFILE).read()
@@ -86,6 +102,155 @@ def traffic_from_profile():
     return float(m_b.group(1)), "rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated"
 
 
+class Rig:
+    """The workload on the device: SETS copies of (x, dy, y, dx)."""
+
+    def __init__(self, torch, w, dev):
+        self.torch = torch
+        self.n = w.numel
+
+        def to_dev(a):
+            return torch.from_numpy(a).view(torch.int16).view(torch.bfloat16).to(dev)
+
+        # Kernel number k (forward and backward alternate) uses set k % SETS,
+        # so no kernel reads memory that any of the previous SETS - 1 kernels
+        # touched (>= 800 MB of traffic, three times the 256 MB Infinity
+        # Cache): every input byte comes from HBM.
+        x0, dy0 = to_dev(w.xs[0]), to_dev(w.dys[0])
+        self.bufs = []
+        for _ in range(SETS):
+            xs, dys = x0.clone(), dy0.clone()
+            self.bufs.append((xs, dys, torch.empty_like(xs), torch.empty_like(xs)))
+        del x0, dy0
+        self.ptrs = [tuple(t.data_ptr() for t in b) for b in self.bufs]
+        self.stream = torch.cuda.current_stream(dev)
+        self.sh = self.stream.cuda_stream
+
+    def region(self, fn, count):
+        """count calls of fn(i) between two events on the launch stream."""
+        torch = self.torch
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        a.record(self.stream)
+        for i in range(count):
+            fn(i)
+        b.record(self.stream)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, a.elapsed_time(b)
+
+
+def measure(args, act, rig, w, lib, torch):
+    from memory_efficient_activation_amd import _lib, accounting
+
+    n, dtype = w.numel, w.dtype
+    param = w.alpha if act == "swish" else _lib.DEFAULT_PARAM.get(act, 0.0)
+    code, dt = _lib.ACTS[act], _lib.BF16
+    ptrs, sh = rig.ptrs, rig.sh
+
+    def fwd(j):
+        xp, _, yp, _ = ptrs[j % SETS]
+        _lib.check(lib.meswish_act_fwd(code, xp, yp, n, param, dt, sh), "meswish_act_fwd")
+
+    def bwd(j):
+        xp, dyp, _, dxp = ptrs[j % SETS]
+        _lib.check(lib.meswish_act_bwd(code, xp, dyp, dxp, n, param, dt, sh), "meswish_act_bwd")
+
+    def step(i):
+        fwd(2 * i)
+        bwd(2 * i + 1)
+
+    fwd_b = accounting.fwd_bytes(n, dtype)
+    bwd_b = accounting.bwd_bytes(n, dtype)
+    step_b = fwd_b + bwd_b
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    wall, gpu_ms = rig.region(step, K)
+    log(f"[bench] {act}: timed {K} steps: wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms")
+    # Per-kernel launch durations: each kernel alone, back to back on the
+    # rotating sets, between two events on the launch stream.
+    _, bwd_total = rig.region(bwd, K)
+    _, fwd_total = rig.region(fwd, K)
+    bwd_us, fwd_us = bwd_total * 1e3 / K, fwd_total * 1e3 / K
+    bwd_gbps = bwd_b / (bwd_us * 1e-6) / 1e9
+    fwd_gbps = fwd_b / (fwd_us * 1e-6) / 1e9
+    value = step_b * K / wall / 1e9
+    headline = act == "swish"
+    traffic, traffic_note = traffic_from_profile() if headline else (None, "counters taken for Swish")
+
+    result = {
+        "metric": METRIC if headline else
+        f"HBM GB/s + fraction of peak, {act} fwd+bwd, 67M-elem bf16, 1 MI355X",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "io_dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{act} fwd+bwd, bf16 [8,2048,4096] (67,108,864 elements)"
+                               + (", alpha=1.0" if headline else ""),
+                   "n": n, "param": param, "bytes_per_step": step_b,
+                   "x": "N(0,1) seed 0", "dy": "0.01*N(0,1) seed 1", "buffer_sets": SETS},
+        "frac_peak": round(value / PEAK_HBM_GBPS, 4),
+        "elements_per_s": round(n * K / wall, 1),
+        "gpu_ms_per_step_events": round(gpu_ms / K, 5),
+        "fwd": {"bytes": fwd_b, "mean_us": round(fwd_us, 2), "GBps": round(fwd_gbps, 1)},
+        "bwd": {"bytes": bwd_b, "mean_us": round(bwd_us, 2), "GBps": round(bwd_gbps, 1)},
+        "roofline": {"kernel": f"act_vec_kernel<bf16, bwd, {act}>", "bound": "hbm",
+                     "achieved": round(bwd_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(bwd_gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic, "traffic_note": traffic_note,
+                     "bytes_per_launch": bwd_b, "mean_launch_us": round(bwd_us, 2),
+                     "page_flops_per_element_fwd": PAGE_FLOPS[act]},
+        "bytes_retained": {"memory_efficient": accounting.retained_bytes(n, dtype),
+                           "naive_3_maps": accounting.retained_bytes(n, dtype, naive=True)},
+    }
+
+    if not args.no_extras:
+        def copy(j):
+            xp, _, yp, _ = ptrs[j % SETS]
+            _lib.check(lib.meswish_copy(xp, yp, 2 * n, sh), "meswish_copy")
+        for i in range(5):
+            copy(i)
+        _, cms = rig.region(copy, K)
+        copy_us = cms * 1e3 / K
+        copy_gbps = 2 * (2 * n) / (copy_us * 1e-6) / 1e9
+        result["copy_ceiling"] = {"bytes": 4 * n, "mean_us": round(copy_us, 2),
+                                  "GBps": round(copy_gbps, 1),
+                                  "bwd_frac_of_copy": round(bwd_gbps / copy_gbps, 4),
+                                  "value_frac_of_copy": round(value / copy_gbps, 4)}
+
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.Oracle()
+        threads = len(os.sched_getaffinity(0))
+        oname = ORACLE_NAME.get(act, act)
+        times = []
+        for _ in range(max(1, args.cpu_reps)):
+            c0 = time.perf_counter()
+            orc.act_fwd(oname, w.xs[0], param, threads=threads)
+            orc.act_bwd(oname, w.xs[0], w.dys[0], param, threads=threads, want_scale=False)
+            times.append(time.perf_counter() - c0)
+        ct = statistics.median(times)
+        result["cpu_baseline"] = {"value": round(step_b / ct / 1e9, 3), "unit": "GB/s",
+                                  "cores": threads, "kind": "oracle",
+                                  "sample": f"the full workload ({n} elements) fwd+bwd, binary64 C "
+                                            f"oracle, median of {len(times)} runs ({ct:.2f} s each)",
+                                  "elements_per_s": round(n / ct, 1)}
+        log(f"[bench] {act}: cpu baseline {ct:.2f} s with {threads} threads")
+    return result
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -95,10 +260,9 @@ def main():
               "part of this build. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    from memory_efficient_activation_amd import _lib, accounting, inputs
+    from memory_efficient_activation_amd import _lib, inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a HIP GPU", file=sys.stderr)
@@ -109,145 +273,11 @@ def main():
 
     t_gen = time.perf_counter()
     w = inputs.make(3)
-    n, dtype, alpha = w.numel, w.dtype, w.alpha
-    log(f"[bench] inputs generated in {time.perf_counter() - t_gen:.1f} s: {w.name}, n={n}")
-
-    def to_dev(a):
-        return torch.from_numpy(a).view(torch.int16).view(torch.bfloat16).to(dev)
-
-    # SETS copies of (x, dy, y, dx).  Kernel number k (forward and backward
-    # alternate) uses set k % SETS, so no kernel reads memory that any of
-    # the previous SETS - 1 kernels touched (>= 800 MB of traffic, three
-    # times the 256 MB Infinity Cache): every input byte comes from HBM.
-    x0, dy0 = to_dev(w.xs[0]), to_dev(w.dys[0])
-    bufs = []
-    for _ in range(SETS):
-        xs, dys = x0.clone(), dy0.clone()
-        bufs.append((xs, dys, torch.empty_like(xs), torch.empty_like(xs)))
-    del x0, dy0
-    ptrs = [tuple(t.data_ptr() for t in b) for b in bufs]
-    stream = torch.cuda.current_stream(dev)
-    sh = stream.cuda_stream
-    code = _lib.BF16
-
-    fwd_b = accounting.fwd_bytes(n, dtype)
-    bwd_b = accounting.bwd_bytes(n, dtype)
-    step_b = fwd_b + bwd_b
-
-    def fwd(j):
-        xp, _, yp, _ = ptrs[j % SETS]
-        _lib.check(lib.swish_fwd(xp, yp, n, alpha, code, sh), "swish_fwd")
-
-    def bwd(j):
-        xp, dyp, _, dxp = ptrs[j % SETS]
-        _lib.check(lib.swish_bwd(xp, dyp, dxp, n, alpha, code, sh), "swish_bwd")
-
-    def step(i):
-        fwd(2 * i)
-        bwd(2 * i + 1)
-
-    def region(fn, count):
-        """count calls of fn(i) between two events on the launch stream."""
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        a.record(stream)
-        for i in range(count):
-            fn(i)
-        b.record(stream)
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0, a.elapsed_time(b)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    log(f"[bench] warmup {args.warmup} steps done")
-
-    K = args.steps
-    wall, gpu_ms = region(step, K)
-    log(f"[bench] timed {K} steps: wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms")
-
-    # Per-kernel launch durations: each kernel alone, back to back on the
-    # rotating sets, between two events on the launch stream.
-    _, bwd_total = region(bwd, K)
-    _, fwd_total = region(fwd, K)
-    bwd_us = bwd_total * 1e3 / K
-    fwd_us = fwd_total * 1e3 / K
-    bwd_gbps = bwd_b / (bwd_us * 1e-6) / 1e9
-    fwd_gbps = fwd_b / (fwd_us * 1e-6) / 1e9
-
-    ms_per_step = wall * 1e3 / K
-    value = step_b * K / wall / 1e9
-    traffic, traffic_note = traffic_from_profile()
-
-    result = {
-        "metric": METRIC,
-        "value": round(value, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "io_dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "swish fwd+bwd, bf16 [8,2048,4096] (67,108,864 elements), alpha=1.0",
-                   "n": n, "alpha": alpha, "bytes_per_step": step_b,
-                   "x": "N(0,1) seed 0", "dy": "0.01*N(0,1) seed 1",
-                   "buffer_sets": SETS},
-        "frac_peak": round(value / PEAK_HBM_GBPS, 4),
-        "elements_per_s": round(n * K / wall, 1),
-        "gpu_ms_per_step_events": round(gpu_ms / K, 5),
-        "fwd": {"bytes": fwd_b, "mean_us": round(fwd_us, 2), "GBps": round(fwd_gbps, 1)},
-        "bwd": {"bytes": bwd_b, "mean_us": round(bwd_us, 2), "GBps": round(bwd_gbps, 1)},
-        "roofline": {"kernel": "swish_vec_kernel<bf16, bwd>", "bound": "hbm",
-                     "achieved": round(bwd_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(bwd_gbps / PEAK_HBM_GBPS, 4),
-                     "traffic": traffic, "traffic_note": traffic_note,
-                     "bytes_per_launch": bwd_b, "mean_launch_us": round(bwd_us, 2)},
-        "bytes_retained": {"memory_efficient": accounting.retained_bytes(n, dtype),
-                           "naive_3_maps": accounting.retained_bytes(n, dtype, naive=True)},
-    }
-
-    if not args.no_extras:
-        # Plain 16-byte copy of one tensor (read b n, write b n), same rotation.
-        def copy(j):
-            xp, _, yp, _ = ptrs[j % SETS]
-            _lib.check(lib.meswish_copy(xp, yp, 2 * n, sh), "meswish_copy")
-        for i in range(5):
-            copy(i)
-        _, cms = region(copy, K)
-        copy_us = cms * 1e3 / K
-        copy_gbps = 2 * (2 * n) / (copy_us * 1e-6) / 1e9
-        result["copy_ceiling"] = {"bytes": 4 * n, "mean_us": round(copy_us, 2),
-                                  "GBps": round(copy_gbps, 1),
-                                  "bwd_frac_of_copy": round(bwd_gbps / copy_gbps, 4),
-                                  "value_frac_of_copy": round(value / copy_gbps, 4)}
-        log(f"[bench] copy ceiling {copy_gbps:.0f} GB/s")
-
-    if not args.no_cpu_baseline:
-        import oracle
-        orc = oracle.Oracle()
-        threads = len(os.sched_getaffinity(0))
-        times = []
-        for _ in range(max(1, args.cpu_reps)):
-            c0 = time.perf_counter()
-            orc.fwd(w.xs[0], alpha, threads=threads)
-            orc.bwd(w.xs[0], w.dys[0], alpha, threads=threads, want_scale=False)
-            times.append(time.perf_counter() - c0)
-        ct = statistics.median(times)
-        result["cpu_baseline"] = {"value": round(step_b / ct / 1e9, 3), "unit": "GB/s",
-                                  "cores": threads, "kind": "oracle",
-                                  "sample": f"the full workload ({n} elements) fwd+bwd, binary64 C oracle, "
-                                            f"median of {len(times)} runs ({ct:.2f} s each)",
-                                  "elements_per_s": round(n / ct, 1)}
-        log(f"[bench] cpu baseline {ct:.2f} s with {threads} threads")
-
-    print(json.dumps(result), flush=True)
+    log(f"[bench] inputs generated in {time.perf_counter() - t_gen:.1f} s: {w.name}, n={w.numel}")
+    rig = Rig(torch, w, dev)
+    acts = FAMILY if args.act == "all" else [args.act]
+    for act in acts:
+        print(json.dumps(measure(args, act, rig, w, lib, torch)), flush=True)
 
 
 if __name__ == "__main__":

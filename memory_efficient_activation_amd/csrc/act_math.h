@@ -240,7 +240,8 @@ struct SigmoidOp {
 // ---------------------------------------------------------------------------
 // tanh: C = -2 log2 e, E = e^-2|x|.  tanh x = sign(x) (1 - E) / (1 + E) for
 // |x| >= 1/8 (1 - E >= 0.22, no cancellation), the Maclaurin series
-// x - x^3/3 + 2x^5/15 - 17x^7/315 below (truncation < 2e-9 relative).
+// x - x^3/3 + 2x^5/15 - 17x^7/315 below (truncation < 2e-9 relative); with
+// bfloat16 I/O the switch is at 2^-8 and the series is just x.
 // Derivative 1 - tanh^2 = 4 E / (1 + E)^2.
 // ---------------------------------------------------------------------------
 struct TanhOp {
@@ -253,6 +254,9 @@ struct TanhOp {
         float v;
         float e = exp2_lin<false>(a, k, v);
         float big = (1.0f - e) * rcp_hw(1.0f + e);
+        if (!P)  // bfloat16: tanh x = x to 2^-17 below 2^-8, and the
+                 // cancellation of 1 - E costs under 2^-16 above it
+            return a < 0.00390625f ? x : copysignf(big, x);
         float x2 = x * x;
         float poly = fmaf(x2, -17.0f / 315.0f, 2.0f / 15.0f);
         poly = fmaf(x2, poly, -1.0f / 3.0f);
@@ -336,39 +340,89 @@ struct LeakyReluOp {
 };
 
 // ---------------------------------------------------------------------------
-// GELU with erf: Phi(x) = erfc(-x / sqrt 2) / 2 (device erfcf), phi(x) =
-// e^(-x^2/2) / sqrt(2 pi) with C = -log2(e) / 2 on the exact x^2.  For
-// x < -6 the rare branch uses the scaled erfc (erfcx) so that Phi's factor
-// e^(-x^2/2) is applied exactly, by powers of two.
+// GELU with erf.  Phi(x) = erfc(z) / 2 with z = -x / sqrt 2, evaluated by the
+// Chebyshev-fitted form of Numerical Recipes in C (Press, Teukolsky,
+// Vetterling, Flannery, 2nd ed., section 6.2, function erfcc):
+//   erfc(|z|) = t exp(-z^2 + Q(t)),  t = 1 / (1 + |z| / 2),
+// Q a degree-9 polynomial; fractional error below 1.2e-7 for every z >= 0,
+// and erfc(-|z|) = 2 - erfc(|z|).  z^2 = x^2 / 2 is taken from the exact
+// x^2 (hi+lo).  phi(x) = e^(-x^2/2) / sqrt(2 pi) with C = -log2(e) / 2.
+// For x < -6 the rare branch applies e^(-x^2/2) by powers of two.
 // ---------------------------------------------------------------------------
 struct GeluErfOp {
     static constexpr bool kHasRare = true;
     static constexpr float kRareBelow = -6.0f;
+    static constexpr float kLog2ef = 1.44269504088896341f;
+
+    // Q(t) of the erfc form above (t in (0, 1]).  FULL false: a degree-4
+    // polynomial with relative erfc error below 7.1e-5 on the fast path's
+    // range x >= -6 replaces the degree-9 fit -- Chebyshev interpolation of
+    // the exact Q, computed by gen_gelu_bf16_poly.py.  Only the bfloat16
+    // forward uses it: the backward's Phi + x phi cancels near its zero
+    // (x = -0.75), where only the full fit keeps bfloat16 within 1 ulp.
+    template <bool FULL>
+    __device__ static float q_poly(float t)
+    {
+        if (!FULL) {
+            float r = 0.05114523f;
+            r = fmaf(t, r, -0.5033026f);
+            r = fmaf(t, r, 0.86044306f);
+            r = fmaf(t, r, 0.83762014f);
+            return fmaf(t, r, -1.2459551f);
+        }
+        float p = 0.17087277f;
+        p = fmaf(t, p, -0.82215223f);
+        p = fmaf(t, p, 1.48851587f);
+        p = fmaf(t, p, -1.13520398f);
+        p = fmaf(t, p, 0.27886807f);
+        p = fmaf(t, p, -0.18628806f);
+        p = fmaf(t, p, 0.09678418f);
+        p = fmaf(t, p, 0.37409196f);
+        p = fmaf(t, p, 1.00002368f);
+        return fmaf(t, p, -1.26551223f);
+    }
+
+    // erfc(|x| / sqrt 2) / 2 and, through e2 (if not NULL), e^(-x^2/2).
+    // Both are below 2^-2900 beyond |x| = 64: clamping keeps x^2 finite (a
+    // NaN x still reaches the caller's result through its own factor x).
+    template <bool P, bool FULL>
+    __device__ static float half_erfc_abs(float x, const Coef& k, float* e2)
+    {
+        float a = fminf(fabsf(x), 64.0f);
+        float t = rcp_hw(fmaf(0.5f * kInvSqrt2f, a, 1.0f));
+        float q = q_poly<FULL>(t);
+        float x2 = a * a;
+        float vh = x2 * k.c_hi;  // -x^2 log2(e) / 2
+        float vl = 0.0f;
+        if (P)
+            vl = fmaf(x2, k.c_lo, fmaf(x2, k.c_hi, -vh)) + fmaf(a, a, -x2) * k.c_hi;
+        float eq = exp2_hw(fmaf(q, kLog2ef, vh + vl));  // e^(-z^2 + Q(t))
+        if (e2) {
+            float e = exp2_hw(vh);
+            if (P)
+                e = fmaf(e, vl * kLn2f, e);
+            *e2 = e;
+        }
+        return 0.5f * t * eq;
+    }
 
     template <bool P>
-    __device__ static float fwd(float x, const Coef&, bool& rare)
+    __device__ static float fwd(float x, const Coef& k, bool& rare)
     {
+        float h = half_erfc_abs<P, P>(x, k, nullptr);
+        float cdf = x < 0.0f ? h : 1.0f - h;
         rare |= x < kRareBelow;
-        return x * (0.5f * erfcf(-x * kInvSqrt2f));
+        return x * cdf;
     }
 
     template <bool P>
     __device__ static float bwd(float x, float dy, const Coef& k, bool& rare)
     {
-        float cdf = 0.5f * erfcf(-x * kInvSqrt2f);
-        // phi is even and below 2^-2900 beyond |x| = 64: clamping keeps x^2
-        // finite (NaN still reaches the result through cdf).
-        float xa = fminf(fabsf(x), 64.0f);
-        float x2 = xa * xa;
-        float v = x2 * k.c_hi;
-        float e = exp2_hw(v);
-        if (P) {
-            float x2e = fmaf(xa, xa, -x2);
-            float w = (fmaf(x2, k.c_lo, fmaf(x2, k.c_hi, -v)) + x2e * k.c_hi) * kLn2f;
-            e = fmaf(e, w, e);
-        }
+        float e2;
+        float h = half_erfc_abs<P, true>(x, k, &e2);
+        float cdf = x < 0.0f ? h : 1.0f - h;
         rare |= x < kRareBelow;
-        return dy * fmaf(x, e * kInvSqrt2Pif, cdf);
+        return dy * fmaf(x, e2 * kInvSqrt2Pif, cdf);
     }
 
     template <bool BWD, bool P>
@@ -377,37 +431,39 @@ struct GeluErfOp {
         return x < kRareBelow;
     }
 
-    // e^(-x^2/2) = 2^(x^2 C) with x^2 exact as a hi+lo pair.
-    __device__ static void half_square_exp(float x, const Coef& k, float& vh, float& vl)
+    // x < -6.  Phi(x) = g e^(-x^2/2) with g = t e^Q(t) / 2 (the erfc form
+    // without its Gaussian factor), which is applied by powers of two from
+    // the exact x^2.
+    __device__ static void split(float x, const Coef& k, float& g, float& ef, int& kf, bool& zero)
     {
-        float x2 = x * x, x2e = fmaf(x, x, -x2);
-        vh = x2 * k.c_hi;
-        vl = fmaf(x2, k.c_lo, fmaf(x2, k.c_hi, -vh)) + x2e * k.c_hi;
+        float a = fabsf(x);
+        float t = rcp_hw(fmaf(0.5f * kInvSqrt2f, a, 1.0f));
+        g = 0.5f * t * exp2_hw(q_poly<true>(t) * kLog2ef);
+        float x2 = a * a;
+        float vh = x2 * k.c_hi;
+        float vl = fmaf(x2, k.c_lo, fmaf(x2, k.c_hi, -vh)) + fmaf(a, a, -x2) * k.c_hi;
+        zero = vh < kZeroExp;
+        if (!zero)
+            pow2_split(vh, vl, ef, kf);
     }
 
-    // y = x Phi(x) = x erfcx(z) e^(-z^2) / 2, z = -x / sqrt 2 > 4.2.
     __device__ static float fwd_rare(float x, const Coef& k)
     {
-        float vh, vl, ef;
+        float g, ef;
         int kf;
-        half_square_exp(x, k, vh, vl);
-        if (vh < kZeroExp)
-            return x * 0.0f;
-        pow2_split(vh, vl, ef, kf);
-        return scale_pow2(x, 0.5f * erfcxf(-x * kInvSqrt2f), ef, kf);
+        bool zero;
+        split(x, k, g, ef, kf, zero);
+        return zero ? x * 0.0f : scale_pow2(x, g, ef, kf);
     }
 
-    // dx = dy (Phi + x phi) = dy e^(-x^2/2) (erfcx(z) / 2 + x / sqrt(2 pi)).
+    // dx = dy (Phi + x phi) = dy e^(-x^2/2) (g + x / sqrt(2 pi)).
     __device__ static float bwd_rare(float x, float dy, const Coef& k)
     {
-        float vh, vl, ef;
+        float g, ef;
         int kf;
-        half_square_exp(x, k, vh, vl);
-        if (vh < kZeroExp)
-            return dy * -0.0f;
-        pow2_split(vh, vl, ef, kf);
-        float g = fmaf(0.5f, erfcxf(-x * kInvSqrt2f), x * kInvSqrt2Pif);
-        return scale_pow2(dy, g, ef, kf);
+        bool zero;
+        split(x, k, g, ef, kf, zero);
+        return zero ? dy * -0.0f : scale_pow2(dy, fmaf(x, kInvSqrt2Pif, g), ef, kf);
     }
 };
 

@@ -24,11 +24,12 @@ import csv
 import glob
 import hashlib
 import os
+import re
 import statistics
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCE = os.path.join(HERE, "csrc", "meswish.hip")
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("meswish.hip", "act_math.h")]
 
 N = 8 * 2048 * 4096          # elements of the benchmark tensor
 BF16 = 2                     # bytes per element
@@ -36,12 +37,25 @@ COPY_BYTES = BF16 * N        # bytes the copy kernel reads (and writes) per laun
 ALGO = {"fwd": 2 * BF16 * N, "bwd": 3 * BF16 * N, "copy": 2 * BF16 * N}
 
 
-def kind(name: str) -> str:
-    if "swish_vec_kernel" in name:
-        return "bwd" if ", true>" in name else "fwd"
+ACT_NAMES = ["swish", "relu", "leaky_relu", "sigmoid", "tanh", "gelu", "gelu_tanh"]
+
+
+def kind(name: str, act: str = "swish") -> str:
+    """'fwd' / 'bwd' for the bf16 vector kernel of activation `act`, 'copy'
+    for the copy kernel, 'other' otherwise."""
+    m = re.search(r"act_vec_kernel<meswish::bf16_t, (true|false), (\d+)>", name)
+    if m:
+        if ACT_NAMES[int(m.group(2))] != act:
+            return "other"
+        return "bwd" if m.group(1) == "true" else "fwd"
     if "copy16_kernel" in name:
         return "copy"
     return "other"
+
+
+def act_of(name: str) -> str:
+    m = re.search(r"act_vec_kernel<meswish::bf16_t, (?:true|false), (\d+)>", name)
+    return ACT_NAMES[int(m.group(1))] if m else ""
 
 
 def _one(pattern: str) -> str:
@@ -58,8 +72,10 @@ def trace(d: str) -> str:
     for r in stats:
         out.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
-    seq = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), kind(r["Kernel_Name"]))
-                 for r in rows)
+    seq = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+                  kind(r["Kernel_Name"], act_of(r["Kernel_Name"]) or "swish"),
+                  act_of(r["Kernel_Name"])) for r in rows)
+    seq = [(s_, e_, (f"{a}:{k}" if a and k in ("fwd", "bwd") else k)) for s_, e_, k, a in seq]
     runs, cur = [], None
     for i, (_, _, k) in enumerate(seq):
         if cur and cur[0] == k:
@@ -72,7 +88,7 @@ def trace(d: str) -> str:
         runs.append(cur)
     out += ["", "| region (consecutive launches) | launches | mean kernel time (us) | "
                 "algorithmic GB/s |", "|---|---|---|---|"]
-    alt = [r for r in seq if r[2] in ("fwd", "bwd")]
+    alt = [r for r in seq if r[2] in ("swish:fwd", "swish:bwd")]
     # The alternating region is the longest run of fwd/bwd pairs.
     best, start = (0, 0), None
     for i in range(len(alt)):
@@ -84,16 +100,18 @@ def trace(d: str) -> str:
             start = None
     if best[0] > 4:
         seg = alt[best[1]:best[1] + best[0]]
-        for k in ("fwd", "bwd"):
+        for k in ("swish:fwd", "swish:bwd"):
             d_ = [e - s for s, e, kk in seg if kk == k]
             t = statistics.fmean(d_)
-            out.append(f"| alternating fwd/bwd steps: {k} | {len(d_)} | {t / 1e3:.2f} | "
-                       f"{ALGO[k] / t:.0f} |")
+            out.append(f"| alternating swish fwd/bwd steps: {k.split(':')[1]} | {len(d_)} | "
+                       f"{t / 1e3:.2f} | {ALGO[k.split(':')[1]] / t:.0f} |")
     for k, a, b in runs:
-        if b - a >= 4 and k in ALGO:
+        base = k.split(":")[-1]
+        if b - a >= 4 and base in ALGO:
             d_ = [seq[i][1] - seq[i][0] for i in range(a, b + 1)]
             t = statistics.fmean(d_)
-            out.append(f"| {k} only, back to back | {len(d_)} | {t / 1e3:.2f} | {ALGO[k] / t:.0f} |")
+            out.append(f"| {k} only, back to back | {len(d_)} | {t / 1e3:.2f} | "
+                       f"{ALGO[base] / t:.0f} |")
     return "\n".join(out)
 
 
@@ -111,7 +129,10 @@ def traffic(fetch_dir: str, write_dir: str) -> str:
     w = _counter(write_dir, "WRITE_SIZE")
     kib = COPY_BYTES / 1024
     cf, cw = kib / f["copy"], kib / w["copy"]
-    sha = hashlib.sha256(open(SOURCE, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for path in SOURCES:
+        h.update(open(path, "rb").read())
+    sha = h.hexdigest()
     out = [f"calibration (copy kernel, {COPY_BYTES} B read and written per launch): "
            f"FETCH_SIZE reads {f['copy']:.1f} KiB -> factor {cf:.5f}; "
            f"WRITE_SIZE reads {w['copy']:.1f} KiB -> factor {cw:.5f}", "",
