@@ -63,6 +63,8 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_round_f32.restype = ctypes.c_float
     lib.oracle_round_bf16.argtypes = [ctypes.c_double]
     lib.oracle_round_bf16.restype = ctypes.c_uint16
+    lib.oracle_round_n.argtypes = [ctypes.c_int, c_void, c_void, c_size]
+    lib.oracle_round_n.restype = None
     lib.oracle_sigmoid.argtypes = [ctypes.c_double]
     lib.oracle_sigmoid.restype = ctypes.c_double
     lib.oracle_swish_fwd.argtypes = [ctypes.c_int, c_void, c_void, c_size,
@@ -131,6 +133,15 @@ class Oracle:
 
     def round_bf16(self, v: float) -> int:
         return int(self.lib.oracle_round_bf16(float(v)))
+
+    def round_array(self, v: np.ndarray, dtype: str) -> np.ndarray:
+        """Round binary64 values once to "f32" (float32 array) or "bf16"
+        (uint16 bit patterns), to nearest even."""
+        v = np.ascontiguousarray(v, dtype=np.float64)
+        out = np.empty(v.shape, dtype=np.float32 if dtype == "f32" else np.uint16)
+        self.lib.oracle_round_n(F32 if dtype == "f32" else BF16, v.ctypes.data, out.ctypes.data,
+                                v.size)
+        return out
 
     # --- arrays ----------------------------------------------------------
     @staticmethod

@@ -9,6 +9,13 @@
   to -(bits & 0x7FFF), so both zeros map to 0), differ by at most 1.
 * NaN must meet NaN and nothing else; the two zeros compare equal.
 
+* bfloat16 with a term scale (results that sum terms of either sign, such as
+  batch normalization's): ordered distance at most 1 from the oracle's
+  rounded value, or |g - v| <= rtol * m with v the oracle's binary64 value --
+  an evaluation in binary32 arithmetic may move a cancelled result by more
+  than one bfloat16 step of its own size, but not by more than rtol times
+  the size of its terms.
+
 The floor 2^-126 (the smallest binary32 normal) reads "relative error" for
 references that are zero or subnormal, where a relative measure is
 undefined.  o is the oracle's value rounded to the output type.
@@ -63,3 +70,26 @@ def f32_report(got: np.ndarray, want: np.ndarray, scale: np.ndarray | None = Non
             "n_bad": bad, "ok": bad == 0,
             "first_bad": int(idx[np.nonzero(bad_mask)[0][0]]) if np.any(bad_mask) else
             (int(np.nonzero(gn != wn)[0][0]) if nan_mismatch else -1)}
+
+
+def bf16_scaled_report(got: np.ndarray, want_bits: np.ndarray, want64: np.ndarray,
+                       scale: np.ndarray, rtol: float = 1e-5) -> dict:
+    """bfloat16 rule with a term scale m (see the module docstring)."""
+    got = np.asarray(got, dtype=np.uint16).ravel()
+    want_bits = np.asarray(want_bits, dtype=np.uint16).ravel()
+    want64 = np.asarray(want64, np.float64).ravel()
+    scale = np.asarray(scale, np.float64).ravel()
+    isn = lambda b: ((b & 0x7F80) == 0x7F80) & ((b & 0x007F) != 0)
+    gn, wn, nan_mismatch = _nan_mask(got, want_bits, isn)
+    ok = ~(gn | wn)
+    d = np.abs(ord_bf16(got[ok]) - ord_bf16(want_bits[ok]))
+    gv = (got[ok].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    near = np.abs(gv - want64[ok]) <= rtol * np.maximum(scale[ok], FLOOR)
+    bad_mask = (d > 1) & ~near
+    bad = int(np.count_nonzero(bad_mask)) + nan_mismatch
+    idx = np.nonzero(ok)[0]
+    return {"n": int(got.size), "max_ulp": int(d.max()) if d.size else 0,
+            "n_off_by_one": int(np.count_nonzero(d == 1)),
+            "n_beyond_one_within_scale": int(np.count_nonzero((d > 1) & near)),
+            "n_bad": bad, "ok": bad == 0,
+            "first_bad": int(idx[np.nonzero(bad_mask)[0][0]]) if np.any(bad_mask) else -1}

@@ -124,6 +124,15 @@ static void store(int dtype, void *p, size_t i, double v)
         ((uint16_t *)p)[i] = oracle_round_bf16(v);
 }
 
+/* Round n binary64 values once to the output type (binary32 or bfloat16
+ * bit patterns).  Used by the oracles whose arithmetic is written in numpy,
+ * so that every oracle rounds through the same pinned routines. */
+void oracle_round_n(int dtype, const double *v, void *out, size_t n)
+{
+    for (size_t i = 0; i < n; ++i)
+        store(dtype, out, i, v[i]);
+}
+
 /* ------------------------------------------------------------------ */
 /* The function and its derivative, in binary64.                      */
 /* ------------------------------------------------------------------ */

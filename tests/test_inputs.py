@@ -53,3 +53,20 @@ def test_exhaustive_bf16_count():
     b = inputs.exhaustive_bf16_finite()
     assert b.size == 65280
     assert np.isfinite(inputs.bf16_bits_to_f32(b)).all()
+
+
+def test_densenet_bc100_channel_bookkeeping():
+    """DenseNet-BC-100 at growth 12: 16 layers per block, block inputs 24,
+    108 (= (24 + 16 * 12) / 2) and 150 (= (108 + 16 * 12) / 2) channels."""
+    from memory_efficient_activation_amd import dense_inputs as di
+    assert (100 - 4) // 6 == di.BLOCK_LAYERS
+    assert di.BLOCKS[1][0] == (di.BLOCKS[0][0] + di.BLOCK_LAYERS * di.GROWTH) // 2
+    assert di.BLOCKS[2][0] == (di.BLOCKS[1][0] + di.BLOCK_LAYERS * di.GROWTH) // 2
+    assert sum(di.block_layer_channels(0, 15)) == 204
+    assert di.block_layer_channels(2, 0) == [150]
+    w = di.dense_layer([3, 2], 2, 5, "bf16", seed=1)
+    assert [s.shape for s in w.sources] == [(2, 3, 5), (2, 2, 5)]
+    assert w.dz.shape == (2, 5, 5) and w.dz.dtype == np.uint16
+    assert w.gamma.dtype == np.float32 and w.gamma.shape == (5,)
+    w2 = di.dense_layer([3, 2], 2, 5, "bf16", seed=1)
+    assert all(np.array_equal(a, b) for a, b in zip(w.sources, w2.sources))
