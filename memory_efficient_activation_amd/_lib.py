@@ -1,4 +1,5 @@
-"""ctypes loader for libmeswish.so (the C ABI declared in include/meswish.h).
+"""ctypes loader for libmeswish.so (the C ABI declared in include/meswish.h
+and include/dense_bn.h).
 
 Argument marshalling only: every element of every pass is computed by the
 HIP kernels inside the library.  There is no CPU fallback -- if the library
@@ -21,7 +22,9 @@ MAX_GROUP = 64
 
 EXPORTED = ("swish_fwd", "swish_bwd", "swish_fwd_grouped", "swish_bwd_grouped",
             "meswish_act_fwd", "meswish_act_bwd",
-            "meswish_strerror", "meswish_version", "meswish_copy", "meswish_plan")
+            "meswish_strerror", "meswish_version", "meswish_copy", "meswish_plan",
+            "dense_bn_workspace_bytes", "dense_bn_stats", "dense_bn_relu_fwd", "dense_bn_relu_bwd")
+DENSE_MAX_SOURCES = 64
 
 # Activation codes (mirror meswish_act) and their default parameters.
 ACTS = {"swish": 0, "relu": 1, "leaky_relu": 2, "sigmoid": 3, "tanh": 4, "gelu": 5,
@@ -44,6 +47,12 @@ class Plan(ctypes.Structure):
                 ("tail", ctypes.c_longlong), ("tiles", ctypes.c_longlong),
                 ("grid", ctypes.c_longlong), ("block", ctypes.c_longlong),
                 ("elems_per_vector", ctypes.c_longlong), ("vectors_per_tile", ctypes.c_longlong)]
+
+
+class DenseSource(ctypes.Structure):
+    """dense_bn_source of include/dense_bn.h."""
+    _fields_ = [("x", ctypes.c_void_p), ("dx", ctypes.c_void_p), ("stats", ctypes.c_void_p),
+                ("channels", ctypes.c_int), ("offset", ctypes.c_int)]
 
 
 class MeswishError(RuntimeError):
@@ -76,6 +85,16 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.meswish_act_bwd.restype = i
     lib.meswish_plan.argtypes = [vp, vp, vp, sz, f, i, i, ctypes.POINTER(Plan)]
     lib.meswish_plan.restype = i
+    lib.dense_bn_workspace_bytes.argtypes = [sz, sz, sz]
+    lib.dense_bn_workspace_bytes.restype = sz
+    lib.dense_bn_stats.argtypes = [vp, sz, i, sz, i, vp, vp, sz, vp]
+    lib.dense_bn_stats.restype = i
+    lib.dense_bn_relu_fwd.argtypes = [ctypes.POINTER(DenseSource), i, sz, sz, i, vp, vp, f, vp, i,
+                                      vp]
+    lib.dense_bn_relu_fwd.restype = i
+    lib.dense_bn_relu_bwd.argtypes = [ctypes.POINTER(DenseSource), i, sz, sz, i, vp, vp, f, vp, vp,
+                                      vp, vp, sz, i, vp]
+    lib.dense_bn_relu_bwd.restype = i
     return lib
 
 

@@ -7,7 +7,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCE = os.path.join(HERE, "csrc", "meswish.hip")
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("meswish.hip", "dense_bn.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libmeswish.so")
 
@@ -31,7 +31,7 @@ def hipcc() -> str:
 def build(output: str = LIBRARY, extra_flags: list[str] | None = None) -> str:
     """Compile libmeswish.so (always recompiles) and return its path."""
     tmp = output + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", SOURCE, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", *SOURCES, "-o", tmp]
     subprocess.run(cmd, check=True)
     os.replace(tmp, output)
     return output

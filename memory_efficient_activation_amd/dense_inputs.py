@@ -34,7 +34,8 @@ BATCH = 64
 BLOCK_LAYERS = 16
 # (block input channels, height = width) of the three dense blocks.
 BLOCKS = [(24, 32), (108, 16), (150, 8)]
-EPS = 1e-5
+# batch normalization's eps, as the binary32 value the kernels receive.
+EPS = float(np.float32(1e-5))
 
 
 def block_layer_channels(block: int, layer: int) -> list[int]:

@@ -62,7 +62,8 @@ def forward(sources, gamma, beta, eps):
     """z = ReLU(gamma xhat + beta) of the concatenated sources, in binary64.
 
     Returns (z, aux) where aux holds mean, var, xhat, h and the error scale
-    of z: |gamma xhat| + |beta| (the terms of h)."""
+    of z where h > 0: |gamma| r (|u| + |mean|) + |beta|, the size of the
+    terms gamma r u, gamma r mean and beta that h sums (r = 1/sqrt(var + eps))."""
     u = concat(sources)
     gamma = np.asarray(gamma, np.float64)[None, :, None]
     beta = np.asarray(beta, np.float64)[None, :, None]
@@ -70,7 +71,9 @@ def forward(sources, gamma, beta, eps):
     xhat = (u - mean[None, :, None]) / np.sqrt(var + eps)[None, :, None]
     h = gamma * xhat + beta
     z = np.maximum(h, 0.0)
-    scale = np.where(h > 0, np.abs(gamma * xhat) + np.abs(beta), 0.0)
+    r = (1.0 / np.sqrt(var + eps))[None, :, None]
+    terms = np.abs(gamma) * r * (np.abs(u) + np.abs(mean)[None, :, None]) + np.abs(beta)
+    scale = np.where(h > 0, terms, 0.0)
     return z, {"mean": mean, "var": var, "xhat": xhat, "h": h, "scale": scale}
 
 
@@ -88,8 +91,10 @@ def backward(sources, dz, gamma, beta, eps):
     dz of z, recomputing everything from the sources.
 
     Returns (dsources, dgamma, dbeta, aux); aux holds the error scales:
-    for du, |gamma| r (|g| + |dbeta| / M + |xhat| |dgamma| / M); for dgamma,
-    sum |g xhat|; for dbeta, sum |g|."""
+    for du, |gamma| r (|g| + |dbeta| / M + (|u| + |mean|) r |dgamma| / M);
+    for dgamma, sum |g| (|u| + |mean|) r; for dbeta, sum |g| -- the sizes of
+    the terms each result sums, xhat counted as its two terms u r and
+    mean r."""
     _, f = forward(sources, gamma, beta, eps)
     dz = np.asarray(dz, np.float64)
     n, c, p = dz.shape
@@ -102,11 +107,12 @@ def backward(sources, dz, gamma, beta, eps):
     r = 1.0 / np.sqrt(f["var"] + eps)
     k = (gam * r)[None, :, None]
     du = k * (g - dbeta[None, :, None] / m - xhat * dgamma[None, :, None] / m)
+    xsize = (np.abs(concat(sources)) + np.abs(f["mean"])[None, :, None]) * r[None, :, None]
     du_scale = np.abs(k) * (np.abs(g) + np.abs(dbeta)[None, :, None] / m
-                            + np.abs(xhat) * np.abs(dgamma)[None, :, None] / m)
+                            + xsize * np.abs(dgamma)[None, :, None] / m)
     channels = [np.shape(s)[1] for s in sources]
     aux = {"du_scale": split(du_scale, channels),
-           "dgamma_scale": np.abs(g * xhat).sum(axis=(0, 2)),
+           "dgamma_scale": (np.abs(g) * xsize).sum(axis=(0, 2)),
            "dbeta_scale": np.abs(g).sum(axis=(0, 2)),
            "mean": f["mean"], "var": f["var"], "h": f["h"]}
     return split(du, channels), dgamma, dbeta, aux

@@ -1,5 +1,6 @@
-"""The C-ABI library: it loads, it exports every symbol include/meswish.h
-declares, and its host-side argument checks answer without a GPU.
+"""The C-ABI library: it loads, it exports every symbol include/meswish.h and
+include/dense_bn.h declare, and its host-side argument checks answer without
+a GPU.
 
 No compute call is made here: every call below is rejected (or is a no-op)
 before anything is launched.
@@ -13,13 +14,15 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "meswish.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("meswish.h", "dense_bn.h")]
 LIB = os.path.join(ROOT, "memory_efficient_activation_amd", "libmeswish.so")
 
 
 def _header_text():
-    with open(HEADER) as f:
-        text = f.read()
+    text = ""
+    for h in HEADERS:
+        with open(h) as f:
+            text += f.read() + "\n"
     return re.sub(r"/\*.*?\*/", "", text, flags=re.S)
 
 
@@ -44,7 +47,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "meswish_act_bwd", "meswish_act_fwd",
         "meswish_copy", "meswish_plan", "meswish_strerror", "meswish_version", "swish_bwd",
-        "swish_bwd_grouped", "swish_fwd", "swish_fwd_grouped"])
+        "swish_bwd_grouped", "swish_fwd", "swish_fwd_grouped",
+        "dense_bn_workspace_bytes", "dense_bn_stats", "dense_bn_relu_fwd", "dense_bn_relu_bwd"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -77,6 +81,11 @@ def test_binding_constants_match_header(lib):
     assert names == [f[0] for f in _lib.Plan._fields_]
     # Descriptor layouts: pointer, pointer, size_t (+ one more pointer for bwd).
     assert ctypes.sizeof(_lib.FwdDesc) == 24 and ctypes.sizeof(_lib.BwdDesc) == 32
+    m = re.search(r"#define DENSE_BN_MAX_SOURCES (\d+)", _header_text())
+    assert int(m.group(1)) == _lib.DENSE_MAX_SOURCES
+    fields = re.search(r"typedef struct \{([^{}]*)\}\s*dense_bn_source;", _header_text()).group(1)
+    assert re.findall(r"(\w+);", fields) == [f[0] for f in _lib.DenseSource._fields_]
+    assert ctypes.sizeof(_lib.DenseSource) == 32
 
 
 def test_strerror_and_version(lib):
@@ -137,3 +146,76 @@ def test_alias_and_alignment_rejections_without_gpu(lib):
     # Grouped: output of tensor 0 coinciding with the input of tensor 1.
     d = (_lib.FwdDesc * 2)(_lib.FwdDesc(base, base + 4096, 256), _lib.FwdDesc(base + 4096, base + 8192, 256))
     assert lib.swish_fwd_grouped(d, 2, 1.0, _lib.F32, None) == _lib.EALIAS
+
+
+def test_dense_workspace_size_and_rejections(lib):
+    """dense_bn_*: workspace sizing (16 bytes per channel per 4096-element
+    chunk of n * hw) and the argument checks that run before any launch."""
+    from memory_efficient_activation_amd import _lib
+    ws = lib.dense_bn_workspace_bytes
+    assert ws(64, 204, 1024) == 204 * 16 * 16          # 65536 elements: 16 chunks
+    assert ws(1, 3, 4096) == 3 * 1 * 16 and ws(1, 3, 4097) == 3 * 2 * 16
+    assert ws(0, 3, 10) == 0 and ws(3, 0, 10) == 0 and ws(3, 2, 0) == 0
+    assert ws(1 << 16, 1, 1 << 15) == 0                # n * hw = 2^31: beyond the limit
+    assert ws(1, 1, (1 << 31) - 1) > 0
+    src = (_lib.DenseSource * 65)()
+    g = ctypes.c_void_p(0x10000000)
+    # Too many sources; count < 0; NULL table.
+    assert lib.dense_bn_relu_fwd(src, 65, 2, 16, 8, g, g, 1e-5, g, _lib.F32, None) == _lib.ETOOMANY
+    assert lib.dense_bn_relu_fwd(src, -1, 2, 16, 8, g, g, 1e-5, g, _lib.F32, None) == _lib.EINVAL
+    assert lib.dense_bn_relu_fwd(None, 1, 2, 16, 8, g, g, 1e-5, g, _lib.F32, None) == _lib.EINVAL
+    # eps must be finite and positive; dtype known; sizes in range.
+    for eps in (0.0, -1.0, float("nan"), float("inf")):
+        assert lib.dense_bn_relu_fwd(src, 0, 2, 16, 8, g, g, eps, g, _lib.F32, None) == _lib.EINVAL
+    assert lib.dense_bn_relu_fwd(src, 0, 2, 16, 8, g, g, 1e-5, g, 5, None) == _lib.EINVAL
+    assert lib.dense_bn_relu_fwd(src, 0, 0, 16, 8, g, g, 1e-5, g, _lib.F32, None) == _lib.EINVAL
+    # count == 0 with valid arguments is a no-op.
+    assert lib.dense_bn_relu_fwd(src, 0, 2, 16, 8, g, g, 1e-5, g, _lib.F32, None) == _lib.OK
+    # A source with NULL x, or channels beyond z_channels, or no stats.
+    one = (_lib.DenseSource * 1)(_lib.DenseSource(None, None, 0x20000000, 4, 0))
+    assert lib.dense_bn_relu_fwd(one, 1, 2, 16, 8, g, g, 1e-5, g, _lib.F32, None) == _lib.EINVAL
+    one[0] = _lib.DenseSource(0x30000000, None, 0x20000000, 4, 6)
+    assert lib.dense_bn_relu_fwd(one, 1, 2, 16, 8, g, g, 1e-5, g, _lib.F32, None) == _lib.EINVAL
+    one[0] = _lib.DenseSource(0x30000000, None, None, 4, 0)
+    assert lib.dense_bn_relu_fwd(one, 1, 2, 16, 8, g, g, 1e-5, g, _lib.F32, None) == _lib.EINVAL
+    # Backward: a source without dx; too small a workspace.
+    one[0] = _lib.DenseSource(0x30000000, None, 0x20000000, 4, 0)
+    assert lib.dense_bn_relu_bwd(one, 1, 2, 16, 8, g, g, 1e-5, g, g, g, g, 1 << 20, _lib.F32,
+                                 None) == _lib.EINVAL
+    one[0] = _lib.DenseSource(0x30000000, 0x40000000, 0x20000000, 4, 0)
+    assert lib.dense_bn_relu_bwd(one, 1, 2, 16, 8, g, g, 1e-5, g, g, g, g, 8, _lib.F32,
+                                 None) == _lib.EINVAL
+    # Statistics: NULL workspace, too small a workspace, empty channel.
+    assert lib.dense_bn_stats(g, 2, 3, 16, _lib.F32, g, None, 1 << 20, None) == _lib.EINVAL
+    assert lib.dense_bn_stats(g, 2, 3, 16, _lib.F32, g, g, 8, None) == _lib.EINVAL
+    assert lib.dense_bn_stats(g, 0, 3, 16, _lib.F32, g, g, 1 << 20, None) == _lib.EINVAL
+
+
+def test_dense_alias_rejections_without_gpu(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("covered with real device buffers by the GPU tests")
+    from memory_efficient_activation_amd import _lib
+    base = 0x10000000
+    n, c, hw = 2, 4, 16
+    xb = n * c * hw * 4
+    stats, gam, bet = base + 0x100000, base + 0x200000, base + 0x201000
+    # z overlapping the source.
+    s = (_lib.DenseSource * 1)(_lib.DenseSource(base, None, stats, c, 0))
+    assert lib.dense_bn_relu_fwd(s, 1, n, hw, c, gam, bet, 1e-5, base + xb - 64, _lib.F32,
+                                 None) == _lib.EALIAS
+    # Two sources claiming the same z channels.
+    s2 = (_lib.DenseSource * 2)(_lib.DenseSource(base, None, stats, c, 0),
+                                _lib.DenseSource(base + xb, None, stats + 64, c, 2))
+    assert lib.dense_bn_relu_fwd(s2, 2, n, hw, 8, gam, bet, 1e-5, base + 0x400000, _lib.F32,
+                                 None) == _lib.EINVAL
+    # dx of one source on top of the other source.
+    s2 = (_lib.DenseSource * 2)(_lib.DenseSource(base, base + xb, stats, c, 0),
+                                _lib.DenseSource(base + xb, base + 0x300000, stats + 64, c, c))
+    wsb = lib.dense_bn_workspace_bytes(n, 2 * c, hw)
+    assert lib.dense_bn_relu_bwd(s2, 2, n, hw, 2 * c, gam, bet, 1e-5, base + 0x500000,
+                                 base + 0x600000, base + 0x601000, base + 0x700000, wsb, _lib.F32,
+                                 None) == _lib.EALIAS
+    # Statistics on top of the source.
+    assert lib.dense_bn_stats(base, n, c, hw, _lib.F32, base + 64, base + 0x700000, 1 << 16,
+                              None) == _lib.EALIAS
