@@ -29,6 +29,15 @@ Also reported (one JSON line on stdout):
 ``--act KIND`` measures another activation of the family of the same page
 (relu, leaky_relu, sigmoid, tanh, gelu, gelu_tanh) on the same workload;
 ``--act all`` prints one line per activation, Swish first.
+
+``--dense`` measures instead the shared-buffer DenseNet layer stage (README
+of efficient_densenet_pytorch, "A memory-efficient implementation of
+DenseNets", Motivation) on the widest layer of DenseNet-BC-100's first
+block at batch 64 (204 channels of 64 x 32 x 32, the README's Performance
+configuration): per training step of that layer, the statistics of its
+newest source, the forward, the backward's re-population of the shared
+buffer, and the backward (reduction + apply).  ``--dense-dtype`` picks
+binary32 (default) or bfloat16 feature maps.
 """
 
 from __future__ import annotations
@@ -76,6 +85,9 @@ def parse_args():
     p.add_argument("--no-extras", action="store_true",
                    help="skip the copy-ceiling measurement")
     p.add_argument("--cpu-reps", type=int, default=3)
+    p.add_argument("--dense", action="store_true",
+                   help="measure the shared-buffer DenseNet layer stage instead")
+    p.add_argument("--dense-dtype", default="f32", choices=["f32", "bf16"])
     return p.parse_args()
 
 
@@ -251,6 +263,179 @@ def measure(args, act, rig, w, lib, torch):
     return result
 
 
+DENSE_SETS = 8
+
+
+def measure_dense(args, lib, torch, dev):
+    """The DenseNet layer stage: see the module docstring (``--dense``)."""
+    from memory_efficient_activation_amd import _lib, dense, dense_inputs as di
+
+    w = di.densenet_bc100_layer(0, di.BLOCK_LAYERS - 1, args.dense_dtype)
+    n, hw, C = w.n, w.hw, w.total_channels
+    esz = 4 if w.dtype == "f32" else 2
+    code = _lib.F32 if w.dtype == "f32" else _lib.BF16
+    cmb = C * n * hw * esz                       # one concatenated map, bytes
+    new_c = w.channels[-1]                       # the layer's newest source
+
+    def to_dev(a):
+        t = torch.from_numpy(a)
+        if a.dtype.name == "uint16":
+            t = t.view(torch.int16).view(torch.bfloat16)
+        return t.to(dev)
+
+    gamma, beta = to_dev(w.gamma), to_dev(w.beta)
+    sets = []
+    xs0 = [to_dev(s_) for s_ in w.sources]
+    dz0 = to_dev(w.dz)
+    for _ in range(DENSE_SETS):
+        xs = [x.clone() for x in xs0]
+        st = [dense.bn_stats(x) for x in xs]
+        dxs = [torch.empty_like(x) for x in xs]
+        z = torch.empty_like(dz0)
+        dz = dz0.clone()
+        descs = (_lib.DenseSource * len(xs))(*[
+            _lib.DenseSource(x.data_ptr(), d.data_ptr(), t.data_ptr(), int(x.shape[1]), off)
+            for x, d, t, off in zip(xs, dxs, st, [sum(w.channels[:j]) for j in range(len(xs))])])
+        nbytes = lib.dense_bn_workspace_bytes(n, C, hw)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        ws_new = torch.empty(lib.dense_bn_workspace_bytes(n, new_c, hw), dtype=torch.uint8,
+                             device=dev)
+        stat_new = torch.empty((new_c, 2), dtype=torch.float64, device=dev)
+        dg = torch.empty(C, dtype=torch.float32, device=dev)
+        db = torch.empty(C, dtype=torch.float32, device=dev)
+        sets.append(dict(xs=xs, st=st, dxs=dxs, z=z, dz=dz, descs=descs, ws=ws, ws_new=ws_new,
+                         stat_new=stat_new, dg=dg, db=db))
+    del xs0, dz0
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    eps = float(w.eps)
+    nsrc = len(w.sources)
+
+    def k_stats(j):
+        s_ = sets[j % DENSE_SETS]
+        _lib.check(lib.dense_bn_stats(s_["xs"][-1].data_ptr(), n, new_c, hw, code,
+                                      s_["stat_new"].data_ptr(), s_["ws_new"].data_ptr(),
+                                      s_["ws_new"].numel(), sh), "dense_bn_stats")
+
+    def k_fwd(j):
+        s_ = sets[j % DENSE_SETS]
+        _lib.check(lib.dense_bn_relu_fwd(s_["descs"], nsrc, n, hw, C, gamma.data_ptr(),
+                                         beta.data_ptr(), eps, s_["z"].data_ptr(), code, sh),
+                   "dense_bn_relu_fwd")
+
+    def k_bwd(j):
+        s_ = sets[j % DENSE_SETS]
+        _lib.check(lib.dense_bn_relu_bwd(s_["descs"], nsrc, n, hw, C, gamma.data_ptr(),
+                                         beta.data_ptr(), eps, s_["dz"].data_ptr(),
+                                         s_["dg"].data_ptr(), s_["db"].data_ptr(),
+                                         s_["ws"].data_ptr(), s_["ws"].numel(), code, sh),
+                   "dense_bn_relu_bwd")
+
+    def step(i):
+        k_stats(4 * i)
+        k_fwd(4 * i + 1)
+        k_fwd(4 * i + 2)      # the backward's re-population of the shared buffer
+        k_bwd(4 * i + 3)
+
+    stats_b, fwd_b, bwd_b = new_c * n * hw * esz, 2 * cmb, 5 * cmb
+    step_b = stats_b + 2 * fwd_b + bwd_b
+
+    def region(fn, count):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        a.record(stream)
+        for i in range(count):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, a.elapsed_time(b)
+
+    for i in range(args.warmup):
+        step(i)
+    K = args.steps
+    wall, gpu_ms = region(step, K)
+    log(f"[bench] dense: timed {K} steps: wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms")
+    per = {}
+    for name, fn, nb in (("stats", k_stats, stats_b), ("fwd", k_fwd, fwd_b),
+                         ("bwd", k_bwd, bwd_b)):
+        _, ms = region(fn, K)
+        us = ms * 1e3 / K
+        per[name] = {"bytes": nb, "mean_us": round(us, 2), "GBps": round(nb / (us * 1e-6) / 1e9, 1)}
+    value = step_b * K / wall / 1e9
+
+    # PyTorch's own path on the same layer, for context: torch.cat +
+    # batch_norm (training) + relu, forward and autograd backward.
+    tx = [x.clone().requires_grad_(True) for x in sets[0]["xs"]]
+    tg = gamma.clone().requires_grad_(True)
+    tb = beta.clone().requires_grad_(True)
+    tdz = sets[0]["dz"]
+
+    def torch_step(_):
+        u = torch.cat(tx, dim=1)
+        h = torch.relu(torch.nn.functional.batch_norm(u, None, None, tg.to(u.dtype), tb.to(u.dtype),
+                                                      training=True, eps=eps))
+        h.backward(tdz)
+
+    for i in range(3):
+        torch_step(i)
+    reps = max(10, K // 10)
+    t_wall, _ = region(torch_step, reps)
+
+    result = {
+        "metric": f"HBM GB/s + fraction of peak, DenseNet layer stage (concat+BN+ReLU, shared "
+                  f"buffer) fwd+recompute+bwd, DenseNet-BC-100 block-1 layer-16 {w.dtype}, "
+                  f"1 MI355X",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "io_dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"DenseNet-BC-100 (growth 12) block 1 layer 16 at batch 64: "
+                               f"{nsrc} sources, {C} channels of 64x32x32, {w.dtype}",
+                   "channels": w.channels, "n": n, "hw": hw, "eps": eps,
+                   "bytes_per_step": step_b, "buffer_sets": DENSE_SETS,
+                   "step": "stats(newest source) + fwd + fwd (recompute) + bwd (reduce+apply)"},
+        "frac_peak": round(value / PEAK_HBM_GBPS, 4),
+        "kernels": per,
+        "roofline": {"kernel": "dense_bn_relu_bwd (bwd_reduce_kernel + bwd_apply_kernel)",
+                     "bound": "hbm", "achieved": per["bwd"]["GBps"], "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(per["bwd"]["GBps"] / PEAK_HBM_GBPS, 4),
+                     "traffic": None, "traffic_note": "no counter summary for this kernel",
+                     "bytes_per_launch": bwd_b, "mean_launch_us": per["bwd"]["mean_us"]},
+        "torch_eager_same_layer": {"ms_per_step": round(t_wall * 1e3 / reps, 4),
+                                   "note": "torch.cat + batch_norm + relu, fwd + autograd bwd; "
+                                           "keeps the concatenation and the output"},
+    }
+    if not args.no_cpu_baseline:
+        import numpy as np
+        from oracle import dense_oracle
+        from memory_efficient_activation_amd import inputs
+        srcs = [inputs.decode(s_).astype(np.float64) for s_ in w.sources]
+        dz64 = inputs.decode(w.dz).astype(np.float64)
+        c0 = time.perf_counter()
+        dense_oracle.forward(srcs, w.gamma, w.beta, eps)
+        dense_oracle.backward(srcs, dz64, w.gamma, w.beta, eps)
+        ct = time.perf_counter() - c0
+        # The oracle's backward recomputes the forward, as the method does:
+        # count the same bytes as one GPU step without the statistics pass.
+        cb = 2 * fwd_b + bwd_b
+        result["cpu_baseline"] = {"value": round(cb / ct / 1e9, 3), "unit": "GB/s", "cores": 1,
+                                  "kind": "oracle",
+                                  "sample": f"the full layer ({C} x {n * hw} elements), numpy "
+                                            f"binary64 forward + backward, one run ({ct:.2f} s)"}
+        log(f"[bench] dense: cpu baseline {ct:.2f} s")
+    return result
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -270,6 +455,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lib = _lib.library()
+    if args.dense:
+        print(json.dumps(measure_dense(args, lib, torch, dev)), flush=True)
+        return
 
     t_gen = time.perf_counter()
     w = inputs.make(3)
