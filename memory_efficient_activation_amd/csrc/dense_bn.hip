@@ -42,10 +42,26 @@
 
 namespace dense_bn {
 
+// Bytes of one channel per block (16 KiB: 4096 binary32 or 8192 bfloat16
+// elements), and the non-temporal (streaming) cache policy as a bit mask:
+// 1 = loads of the sources, 2 = loads of dz, 4 = stores of z and dx.  Both
+// chosen by measurement on MI355X (streaming stores: +10 % on every pass).
+#ifndef DENSE_BN_CHUNK_BYTES
+#define DENSE_BN_CHUNK_BYTES 16384
+#endif
+#ifndef DENSE_BN_NT
+#define DENSE_BN_NT 4
+#endif
+
 constexpr int kBlock = 256;             // threads per block
 constexpr int kWaves = kBlock / 64;
-constexpr int kChunk = 4096;            // elements of one channel per block
 constexpr int kMaxSources = DENSE_BN_MAX_SOURCES;
+// The workspace is sized for the smallest chunk (binary32).
+constexpr int kMinChunk = DENSE_BN_CHUNK_BYTES / 4;
+static_assert(kMinChunk % (kBlock * 8) == 0, "a chunk must give every lane whole vectors");
+constexpr bool kNtX = (DENSE_BN_NT & 1) != 0;
+constexpr bool kNtDz = (DENSE_BN_NT & 2) != 0;
+constexpr bool kNtOut = (DENSE_BN_NT & 4) != 0;
 
 // ---------------------------------------------------------------------------
 // Element types and vector access.
@@ -71,30 +87,59 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 
 template <typename IO> struct Elem;
 
+typedef uint32_t u32x4_v __attribute__((ext_vector_type(4)));
+
+// 16-byte global load / store; kNT selects the non-temporal policy.
+template <bool kNT>
+__device__ __forceinline__ uint4 ld16(const void* p)
+{
+    if (kNT) {
+        u32x4_v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_v*>(p));
+        return make_uint4(v.x, v.y, v.z, v.w);
+    }
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+template <bool kNT>
+__device__ __forceinline__ void st16(void* p, const uint4& v)
+{
+    if (kNT) {
+        u32x4_v w = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4_v*>(p));
+    } else {
+        *reinterpret_cast<uint4*>(p) = v;
+    }
+}
+
 template <> struct Elem<float> {
     static constexpr int kVec = 4;  // elements per 16-byte vector
+    template <bool kNT>
     __device__ static void load(const float* p, int64_t i, float (&f)[4])
     {
-        uint4 v = *reinterpret_cast<const uint4*>(p + i);
+        uint4 v = ld16<kNT>(p + i);
         f[0] = __uint_as_float(v.x);
         f[1] = __uint_as_float(v.y);
         f[2] = __uint_as_float(v.z);
         f[3] = __uint_as_float(v.w);
     }
+    template <bool kNT>
     __device__ static void store(float* p, int64_t i, const float (&f)[4])
     {
-        *reinterpret_cast<uint4*>(p + i) = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
-                                                      __float_as_uint(f[2]), __float_as_uint(f[3]));
+        st16<kNT>(p + i, make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
+                                    __float_as_uint(f[2]), __float_as_uint(f[3])));
     }
+    template <bool kNT>
     __device__ static void load(const float* p, int64_t i, float (&f)[1]) { f[0] = p[i]; }
+    template <bool kNT>
     __device__ static void store(float* p, int64_t i, const float (&f)[1]) { p[i] = f[0]; }
 };
 
 template <> struct Elem<bf16_t> {
     static constexpr int kVec = 8;
+    template <bool kNT>
     __device__ static void load(const bf16_t* p, int64_t i, float (&f)[8])
     {
-        uint4 v = *reinterpret_cast<const uint4*>(p + i);
+        uint4 v = ld16<kNT>(p + i);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -102,16 +147,18 @@ template <> struct Elem<bf16_t> {
             f[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
         }
     }
+    template <bool kNT>
     __device__ static void store(bf16_t* p, int64_t i, const float (&f)[8])
     {
-        *reinterpret_cast<uint4*>(p + i) =
-            make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                       pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+        st16<kNT>(p + i, make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                                    pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])));
     }
+    template <bool kNT>
     __device__ static void load(const bf16_t* p, int64_t i, float (&f)[1])
     {
         f[0] = __uint_as_float((uint32_t)p[i].bits << 16);
     }
+    template <bool kNT>
     __device__ static void store(bf16_t* p, int64_t i, const float (&f)[1])
     {
         p[i].bits = (uint16_t)(pack_bf16x2(f[0], 0.0f) & 0xFFFFu);
@@ -126,6 +173,10 @@ template <> struct Elem<bf16_t> {
 // multiplication", 1994): q = (umulhi(v, m) + v) >> s with s = ceil(log2 d)
 // and m = floor(2^32 (2^s - d) / d) + 1, exact for v < 2^31.
 // ---------------------------------------------------------------------------
+
+// Elements of one channel per block for element type IO.
+template <typename IO>
+constexpr int chunk_elems() { return DENSE_BN_CHUNK_BYTES / (int)sizeof(IO); }
 
 struct FastDiv {
     uint32_t d, m, s;
@@ -147,18 +198,16 @@ struct Geom {
 // Source table of a call (kernel argument; at most 64 sources).
 // ---------------------------------------------------------------------------
 
-struct SrcDesc {
-    const void* x;
-    void* dx;
-    const double* stats;
-    int channels;   // C_j
-    int offset;     // first channel in z / gamma / beta / dz / dgamma / dbeta
-    int first;      // first channel of this source in the call's channel order
-};
-
+// Structure of arrays, so that `first` is one contiguous block of the
+// kernel arguments that a block reads with a few wide scalar loads.
 struct Table {
-    SrcDesc s[kMaxSources];
-    int count;
+    const void* x[kMaxSources];
+    void* dx[kMaxSources];
+    const double* stats[kMaxSources];
+    int channels[kMaxSources];   // C_j
+    int offset[kMaxSources];     // first channel in z / gamma / beta / dz / dgamma / dbeta
+    int first[kMaxSources];      // first channel of source j in the call's channel order;
+                                 // INT_MAX past the last source
 };
 
 // Source and channel of this block: blocks are (channel, chunk) pairs in the
@@ -172,12 +221,15 @@ __device__ __forceinline__ Where locate(const Table& t, int chunks)
     Where w;
     w.g = (int)blockIdx.x / chunks;
     w.chunk = (int)blockIdx.x - w.g * chunks;
+    // j = number of sources after the first whose first channel is <= g:
+    // independent compares, no chain of dependent loads.
     int j = 0;
-    while (j + 1 < t.count && w.g >= t.s[j + 1].first)
-        ++j;
+#pragma unroll
+    for (int k = 1; k < kMaxSources; ++k)
+        j += (w.g >= t.first[k]) ? 1 : 0;
     w.j = j;
-    w.cl = w.g - t.s[j].first;
-    w.zc = t.s[j].offset + w.cl;
+    w.cl = w.g - t.first[j];
+    w.zc = t.offset[j] + w.cl;
     return w;
 }
 
@@ -302,6 +354,7 @@ __global__ __launch_bounds__(kBlock) void stats_partial_kernel(const IO* __restr
                                                                int channels, Geom geo,
                                                                double* __restrict__ ws)
 {
+    constexpr int kChunk = chunk_elems<IO>();
     constexpr int kPer = kChunk / (kBlock * V);
     const int c = (int)blockIdx.x / geo.chunks;
     const int chunk = (int)blockIdx.x - c * geo.chunks;
@@ -313,10 +366,10 @@ __global__ __launch_bounds__(kBlock) void stats_partial_kernel(const IO* __restr
                            threadIdx.x;
         ok[i] = v < geo.mv;
         if (ok[i])
-            Elem<IO>::load(x, elem_offset(v, geo.pv, channels, c, V), f[i]);
+            Elem<IO>::template load<kNtX>(x, elem_offset(v, geo.pv, channels, c, V), f[i]);
     }
     float pivot[1];
-    Elem<IO>::load(x, (int64_t)c * geo.pv.d * V, pivot);
+    Elem<IO>::template load<false>(x, (int64_t)c * geo.pv.d * V, pivot);
     const double k = (double)pivot[0];
     double s1 = 0.0, s2 = 0.0;
 #pragma unroll
@@ -353,7 +406,7 @@ __global__ __launch_bounds__(kBlock) void stats_final_kernel(const IO* __restric
     block_sum2(s1, s2);
     if (threadIdx.x == 0) {
         float pivot[1];
-        Elem<IO>::load(x, (int64_t)c * geo.pv.d * vec, pivot);
+        Elem<IO>::template load<false>(x, (int64_t)c * geo.pv.d * vec, pivot);
         const double m1 = s1 / geo.m;
         double var = s2 / geo.m - m1 * m1;
         if (!(var > 0.0))
@@ -369,10 +422,11 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(Table t, Geom geo, int z_ch
                                                      const float* __restrict__ beta, float eps,
                                                      IO* __restrict__ z)
 {
+    constexpr int kChunk = chunk_elems<IO>();
     constexpr int kPer = kChunk / (kBlock * V);
     const Where w = locate(t, geo.chunks);
-    const IO* x = static_cast<const IO*>(t.s[w.j].x);
-    const int cj = t.s[w.j].channels;
+    const IO* x = static_cast<const IO*>(t.x[w.j]);
+    const int cj = t.channels[w.j];
     float f[kPer][V];
     uint32_t vv[kPer];
     bool ok[kPer];
@@ -381,9 +435,9 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(Table t, Geom geo, int z_ch
         vv[i] = (uint32_t)w.chunk * (uint32_t)(kChunk / V) + (uint32_t)(i * kBlock) + threadIdx.x;
         ok[i] = vv[i] < geo.mv;
         if (ok[i])
-            Elem<IO>::load(x, elem_offset(vv[i], geo.pv, cj, w.cl, V), f[i]);
+            Elem<IO>::template load<kNtX>(x, elem_offset(vv[i], geo.pv, cj, w.cl, V), f[i]);
     }
-    const Chan ch = chan_params(t.s[w.j].stats, w.cl, gamma[w.zc], beta[w.zc], eps);
+    const Chan ch = chan_params(t.stats[w.j], w.cl, gamma[w.zc], beta[w.zc], eps);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         if (!ok[i])
@@ -394,7 +448,7 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(Table t, Geom geo, int z_ch
             const float h = fmaf(f[i][e] - ch.mu, ch.a, ch.beta);
             y[e] = passes(f[i][e], ch) ? fmaxf(h, 0.0f) : 0.0f;
         }
-        Elem<IO>::store(z, elem_offset(vv[i], geo.pv, z_channels, w.zc, V), y);
+        Elem<IO>::template store<kNtOut>(z, elem_offset(vv[i], geo.pv, z_channels, w.zc, V), y);
     }
 }
 
@@ -405,10 +459,11 @@ __global__ __launch_bounds__(kBlock) void bwd_reduce_kernel(Table t, Geom geo, i
                                                             float eps, const IO* __restrict__ dz,
                                                             double* __restrict__ ws)
 {
+    constexpr int kChunk = chunk_elems<IO>();
     constexpr int kPer = kChunk / (kBlock * V);
     const Where w = locate(t, geo.chunks);
-    const IO* x = static_cast<const IO*>(t.s[w.j].x);
-    const int cj = t.s[w.j].channels;
+    const IO* x = static_cast<const IO*>(t.x[w.j]);
+    const int cj = t.channels[w.j];
     float f[kPer][V], d[kPer][V];
     bool ok[kPer];
 #pragma unroll
@@ -417,11 +472,11 @@ __global__ __launch_bounds__(kBlock) void bwd_reduce_kernel(Table t, Geom geo, i
             (uint32_t)w.chunk * (uint32_t)(kChunk / V) + (uint32_t)(i * kBlock) + threadIdx.x;
         ok[i] = v < geo.mv;
         if (ok[i]) {
-            Elem<IO>::load(x, elem_offset(v, geo.pv, cj, w.cl, V), f[i]);
-            Elem<IO>::load(dz, elem_offset(v, geo.pv, z_channels, w.zc, V), d[i]);
+            Elem<IO>::template load<kNtX>(x, elem_offset(v, geo.pv, cj, w.cl, V), f[i]);
+            Elem<IO>::template load<kNtDz>(dz, elem_offset(v, geo.pv, z_channels, w.zc, V), d[i]);
         }
     }
-    const Chan ch = chan_params(t.s[w.j].stats, w.cl, gamma[w.zc], beta[w.zc], eps);
+    const Chan ch = chan_params(t.stats[w.j], w.cl, gamma[w.zc], beta[w.zc], eps);
     double sg = 0.0, sgx = 0.0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -451,11 +506,12 @@ __global__ __launch_bounds__(kBlock) void bwd_apply_kernel(Table t, Geom geo, in
                                                            float* __restrict__ dgamma,
                                                            float* __restrict__ dbeta)
 {
+    constexpr int kChunk = chunk_elems<IO>();
     constexpr int kPer = kChunk / (kBlock * V);
     const Where w = locate(t, geo.chunks);
-    const IO* x = static_cast<const IO*>(t.s[w.j].x);
-    IO* dx = static_cast<IO*>(t.s[w.j].dx);
-    const int cj = t.s[w.j].channels;
+    const IO* x = static_cast<const IO*>(t.x[w.j]);
+    IO* dx = static_cast<IO*>(t.dx[w.j]);
+    const int cj = t.channels[w.j];
     float f[kPer][V], d[kPer][V];
     int64_t off[kPer];
     bool ok[kPer];
@@ -466,8 +522,8 @@ __global__ __launch_bounds__(kBlock) void bwd_apply_kernel(Table t, Geom geo, in
         ok[i] = v < geo.mv;
         if (ok[i]) {
             off[i] = elem_offset(v, geo.pv, cj, w.cl, V);
-            Elem<IO>::load(x, off[i], f[i]);
-            Elem<IO>::load(dz, elem_offset(v, geo.pv, z_channels, w.zc, V), d[i]);
+            Elem<IO>::template load<kNtX>(x, off[i], f[i]);
+            Elem<IO>::template load<kNtDz>(dz, elem_offset(v, geo.pv, z_channels, w.zc, V), d[i]);
         }
     }
     // This channel's sums over all its blocks' partials.
@@ -482,7 +538,7 @@ __global__ __launch_bounds__(kBlock) void bwd_apply_kernel(Table t, Geom geo, in
         dbeta[w.zc] = (float)sg;
         dgamma[w.zc] = (float)sgx;
     }
-    const Chan ch = chan_params(t.s[w.j].stats, w.cl, gamma[w.zc], beta[w.zc], eps);
+    const Chan ch = chan_params(t.stats[w.j], w.cl, gamma[w.zc], beta[w.zc], eps);
     const float k1 = (float)(sg / geo.m);
     const float k2 = (float)(sgx / geo.m);
 #pragma unroll
@@ -496,7 +552,7 @@ __global__ __launch_bounds__(kBlock) void bwd_apply_kernel(Table t, Geom geo, in
             const float xh = (f[i][e] - ch.mu) * ch.r;
             out[e] = ch.a * (g - fmaf(xh, k2, k1));
         }
-        Elem<IO>::store(dx, off[i], out);
+        Elem<IO>::template store<kNtOut>(dx, off[i], out);
     }
 }
 
@@ -532,15 +588,16 @@ static uint64_t channel_elems(size_t n, size_t hw)
     return m < (1ull << 31) ? m : 0;
 }
 
-static int chunks_of(uint64_t m) { return (int)((m + kChunk - 1) / kChunk); }
+static int chunks_of(uint64_t m, int chunk) { return (int)((m + chunk - 1) / chunk); }
 
+template <typename IO>
 static Geom make_geom(size_t n, size_t hw, int V)
 {
     Geom g;
     g.pv = make_fastdiv((uint32_t)(hw / V));
     g.mv = (uint32_t)(n * (hw / V));
     g.m = (double)((uint64_t)n * hw);
-    g.chunks = chunks_of((uint64_t)n * hw);
+    g.chunks = chunks_of((uint64_t)n * hw, chunk_elems<IO>());
     return g;
 }
 
@@ -590,7 +647,14 @@ static int build_table(const dense_bn_source* src, int count, size_t n, size_t h
     const size_t vec_bytes = 16;
     vec = (hw * es) % vec_bytes == 0;
     total = 0;
-    t.count = count;
+    for (int j = 0; j < kMaxSources; ++j) {
+        t.x[j] = nullptr;
+        t.dx[j] = nullptr;
+        t.stats[j] = nullptr;
+        t.channels[j] = 0;
+        t.offset[j] = 0;
+        t.first[j] = 0x7FFFFFFF;
+    }
     for (int j = 0; j < count; ++j) {
         const dense_bn_source& s = src[j];
         if (!s.x || !s.stats || s.channels < 1 || s.offset < 0 ||
@@ -606,7 +670,12 @@ static int build_table(const dense_bn_source* src, int count, size_t n, size_t h
                 return MESWISH_EINVAL;  // two sources claim the same channel
         if ((int64_t)total + s.channels > 0x7FFFFFFF)
             return MESWISH_EINVAL;
-        t.s[j] = SrcDesc{s.x, s.dx, s.stats, s.channels, s.offset, total};
+        t.x[j] = s.x;
+        t.dx[j] = s.dx;
+        t.stats[j] = s.stats;
+        t.channels[j] = s.channels;
+        t.offset[j] = s.offset;
+        t.first[j] = total;
         total += s.channels;
         const size_t bytes = n * (size_t)s.channels * hw * es;
         reg.add(s.x, bytes, false);
@@ -621,7 +690,7 @@ template <typename IO, int V>
 static int run_stats(const void* x, size_t n, int channels, size_t hw, double* stats, double* ws,
                      hipStream_t stream)
 {
-    Geom geo = make_geom(n, hw, V);
+    Geom geo = make_geom<IO>(n, hw, V);
     const IO* xp = static_cast<const IO*>(x);
     void* a1[] = {&xp, &channels, &geo, &ws};
     int st = launch(reinterpret_cast<const void*>(&stats_partial_kernel<IO, V>),
@@ -637,7 +706,7 @@ template <typename IO, int V>
 static int run_fwd(Table& t, int total, size_t n, size_t hw, int z_channels, const float* gamma,
                    const float* beta, float eps, void* z, hipStream_t stream)
 {
-    Geom geo = make_geom(n, hw, V);
+    Geom geo = make_geom<IO>(n, hw, V);
     IO* zp = static_cast<IO*>(z);
     void* a[] = {&t, &geo, &z_channels, &gamma, &beta, &eps, &zp};
     return launch(reinterpret_cast<const void*>(&fwd_kernel<IO, V>),
@@ -649,7 +718,7 @@ static int run_bwd(Table& t, int total, size_t n, size_t hw, int z_channels, con
                    const float* beta, float eps, const void* dz, float* dgamma, float* dbeta,
                    double* ws, hipStream_t stream)
 {
-    Geom geo = make_geom(n, hw, V);
+    Geom geo = make_geom<IO>(n, hw, V);
     const IO* dzp = static_cast<const IO*>(dz);
     const int64_t grid = (int64_t)total * geo.chunks;
     void* a1[] = {&t, &geo, &z_channels, &gamma, &beta, &eps, &dzp, &ws};
@@ -670,7 +739,7 @@ extern "C" size_t dense_bn_workspace_bytes(size_t n, size_t channels, size_t hw)
     const uint64_t m = channel_elems(n, hw);
     if (m == 0 || channels == 0 || channels >= (1ull << 31))
         return 0;
-    return channels * (size_t)chunks_of(m) * 2 * sizeof(double);
+    return channels * (size_t)chunks_of(m, kMinChunk) * 2 * sizeof(double);
 }
 
 extern "C" int dense_bn_stats(const void* x, size_t n, int channels, size_t hw, int dtype,

@@ -55,19 +55,19 @@ class DenseLayer(nn.Module):
 class DenseBlock(nn.Module):
     def __init__(self, layers: int, in_channels: int, growth: int, efficient: bool, shared):
         super().__init__()
-        self.efficient = efficient
+        self.efficient, self.shared = efficient, shared
         self.layers = nn.ModuleList(
             DenseLayer(in_channels + i * growth, growth, efficient, shared) for i in range(layers))
 
     def forward(self, x):
         feats = [x]
         # Each feature map's batch statistics, computed once when it is made.
-        stats = [dense.bn_stats(x)] if self.efficient else None
+        stats = [dense.bn_stats(x, self.shared)] if self.efficient else None
         for layer in self.layers:
             y = layer(feats, stats)
             feats.append(y)
             if self.efficient:
-                stats.append(dense.bn_stats(y))
+                stats.append(dense.bn_stats(y, self.shared))
         return torch.cat(feats, dim=1)
 
 
