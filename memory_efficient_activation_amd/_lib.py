@@ -1,5 +1,5 @@
-"""ctypes loader for libmeswish.so (the C ABI declared in include/meswish.h
-and include/dense_bn.h).
+"""ctypes loader for libmeswish.so (the C ABI declared in include/meswish.h,
+include/dense_bn.h and include/fft_conv.h).
 
 Argument marshalling only: every element of every pass is computed by the
 HIP kernels inside the library.  There is no CPU fallback -- if the library
@@ -23,7 +23,9 @@ MAX_GROUP = 64
 EXPORTED = ("swish_fwd", "swish_bwd", "swish_fwd_grouped", "swish_bwd_grouped",
             "meswish_act_fwd", "meswish_act_bwd",
             "meswish_strerror", "meswish_version", "meswish_copy", "meswish_plan",
-            "dense_bn_workspace_bytes", "dense_bn_stats", "dense_bn_relu_fwd", "dense_bn_relu_bwd")
+            "dense_bn_workspace_bytes", "dense_bn_stats", "dense_bn_relu_fwd", "dense_bn_relu_bwd",
+            "fftconv_buffer_bytes", "fftconv_fprop", "fftconv_bprop", "fftconv_accgrad",
+            "fftconv_r2c", "fftconv_c2r", "fftconv_cmul")
 DENSE_MAX_SOURCES = 64
 
 # Activation codes (mirror meswish_act) and their default parameters.
@@ -95,6 +97,17 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.dense_bn_relu_bwd.argtypes = [ctypes.POINTER(DenseSource), i, sz, sz, i, vp, vp, f, vp, vp,
                                       vp, vp, sz, i, vp]
     lib.dense_bn_relu_bwd.restype = i
+    lib.fftconv_buffer_bytes.argtypes = [i, i, i, i]
+    lib.fftconv_buffer_bytes.restype = sz
+    for name in ("fftconv_fprop", "fftconv_bprop", "fftconv_accgrad"):
+        getattr(lib, name).argtypes = [vp, vp, vp, i, i, i, i, i, vp, sz, vp]
+        getattr(lib, name).restype = i
+    lib.fftconv_r2c.argtypes = [vp, i, i, i, vp, vp]
+    lib.fftconv_r2c.restype = i
+    lib.fftconv_c2r.argtypes = [vp, i, i, i, f, vp, vp]
+    lib.fftconv_c2r.restype = i
+    lib.fftconv_cmul.argtypes = [i, vp, vp, vp, i, i, i, i, vp]
+    lib.fftconv_cmul.restype = i
     return lib
 
 

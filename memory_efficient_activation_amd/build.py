@@ -7,7 +7,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("meswish.hip", "dense_bn.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("meswish.hip", "dense_bn.hip", "fft_conv.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libmeswish.so")
 

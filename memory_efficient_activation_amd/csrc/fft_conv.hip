@@ -1,0 +1,551 @@
+// fft_conv.hip -- FFT convolution layers of libmeswish for gfx950: batched
+// small 2-D real FFTs, per-bin complex contractions, inverse FFTs with
+// cropping, over one reused frequency buffer.
+//
+// The method ("Fast Training of Convolutional Networks through FFTs"):
+// transform every input map, kernel and output gradient of a layer once,
+// turn every pairwise convolution into a pointwise product in the
+// frequency domain, transform back.  Formulas, layouts and contracts:
+// include/fft_conv.h.
+//
+// Design for MI355X (CDNA4):
+//   * Transforms.  The page's point is that a GPU FFT library parallelises
+//     within one large transform, while this workload is many small ones.
+//     Here one block of 256 threads transforms T maps of n x n at once
+//     (T n = 512 rows): every thread runs whole length-n transforms in
+//     registers (radix-2 Cooley-Tukey, fully unrolled: no data-dependent
+//     indexing, no scratch), first over rows, then -- through LDS -- over
+//     the n/2 + 1 columns of the half spectrum.  Twiddles e^{-2 pi i j/n}
+//     come from sincospi once per block into LDS.  Zero rows of padded maps
+//     (kernels, output gradients) skip their row transform.
+//   * Spectra are stored bin-major (bin p, then map b), so the per-bin
+//     matrices of the contraction are contiguous and the column pass writes
+//     T consecutive maps of one bin together.
+//   * Contraction.  For every bin, a complex matrix product (M x K) (K x N)
+//     -- S x f by f x f' for the forward.  Tiles of 64 x 64 complex outputs,
+//     K in steps of 16 through LDS, 4 x 4 complex outputs per thread.
+//   * Inverse.  Column transforms first, keeping only the rows that survive
+//     the crop, then row transforms of the Hermitian half rows; only the
+//     kept m x m corner is written, scaled by 1/n^2.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fft_conv.h"
+
+namespace fftconv {
+
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------------------
+// Complex helpers and the in-register transform.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
+__device__ __forceinline__ float2 csub(float2 a, float2 b) { return make_float2(a.x - b.x, a.y - b.y); }
+__device__ __forceinline__ float2 cmul(float2 a, float2 b)
+{
+    return make_float2(fmaf(a.x, b.x, -a.y * b.y), fmaf(a.x, b.y, a.y * b.x));
+}
+__device__ __forceinline__ float2 conjf2(float2 a) { return make_float2(a.x, -a.y); }
+
+constexpr int ilog2(int n) { return n <= 1 ? 0 : 1 + ilog2(n / 2); }
+
+constexpr int bitrev(int x, int bits)
+{
+    int r = 0;
+    for (int i = 0; i < bits; ++i)
+        r = (r << 1) | ((x >> i) & 1);
+    return r;
+}
+
+// In-place length-N DFT of a[] (N a power of two): forward with kernel
+// e^{-2 pi i jk/N}, inverse (INV) with e^{+2 pi i jk/N}, unscaled.
+// tw[j] = e^{-2 pi i j/N} for j < N/2 (LDS).  Iterative radix-2,
+// decimation in time: bit-reversed input order, then log2 N stages.
+template <int N, bool INV>
+__device__ __forceinline__ void fft_reg(float2 (&a)[N], const float2* tw)
+{
+    constexpr int L = ilog2(N);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int j = bitrev(i, L);
+        if (i < j) {
+            const float2 t = a[i];
+            a[i] = a[j];
+            a[j] = t;
+        }
+    }
+#pragma unroll
+    for (int len = 2; len <= N; len <<= 1) {
+        const int half = len >> 1;
+        const int step = N / len;
+#pragma unroll
+        for (int i = 0; i < N; i += len) {
+#pragma unroll
+            for (int j = 0; j < half; ++j) {
+                const float2 u = a[i + j];
+                float2 v = a[i + j + half];
+                if (j != 0) {
+                    float2 w = tw[j * step];
+                    if (INV)
+                        w.y = -w.y;
+                    v = cmul(v, w);
+                }
+                a[i + j] = cadd(u, v);
+                a[i + j + half] = csub(u, v);
+            }
+        }
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void load_twiddles(float2* tw)
+{
+    if ((int)threadIdx.x < N / 2) {
+        float s, c;
+        sincospif(2.0f * (float)threadIdx.x / (float)N, &s, &c);
+        tw[threadIdx.x] = make_float2(c, -s);
+    }
+}
+
+// Maps per block: T N = 512 rows for every supported N.
+template <int N> struct Tile { static constexpr int T = 512 / N; };
+
+// ---------------------------------------------------------------------------
+// Forward transforms: `batch` real m x m maps (row-major, contiguous),
+// zero-padded to N x N -> half spectra, bin-major.
+// ---------------------------------------------------------------------------
+
+template <int N>
+__global__ __launch_bounds__(kThreads) void r2c_kernel(const float* __restrict__ x, int batch,
+                                                       int m, float2* __restrict__ spec)
+{
+    constexpr int T = Tile<N>::T;
+    constexpr int H = N / 2 + 1;
+    constexpr int MS = N * H + 1;  // map stride in LDS, odd: no bank conflicts across maps
+    __shared__ float2 buf[T * MS];
+    __shared__ float2 tw[N / 2];
+    const int64_t b0 = (int64_t)blockIdx.x * T;
+    load_twiddles<N>(tw);
+    __syncthreads();
+
+    // Rows: job = (map, r).
+    for (int job = threadIdx.x; job < T * N; job += kThreads) {
+        const int map = job / N, r = job - map * N;
+        const int64_t b = b0 + map;
+        float2* out = buf + map * MS + r * H;
+        if (b >= batch || r >= m) {
+#pragma unroll
+            for (int v = 0; v < H; ++v)
+                out[v] = make_float2(0.0f, 0.0f);
+            continue;
+        }
+        const float* row = x + (b * m + r) * (int64_t)m;
+        float2 a[N];
+        if (m == N) {
+#pragma unroll
+            for (int c = 0; c < N; c += 4) {
+                const float4 q = *reinterpret_cast<const float4*>(row + c);
+                a[c] = make_float2(q.x, 0.0f);
+                a[c + 1] = make_float2(q.y, 0.0f);
+                a[c + 2] = make_float2(q.z, 0.0f);
+                a[c + 3] = make_float2(q.w, 0.0f);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < N; ++c)
+                a[c] = make_float2(c < m ? row[c] : 0.0f, 0.0f);
+        }
+        fft_reg<N, false>(a, tw);
+#pragma unroll
+        for (int v = 0; v < H; ++v)
+            out[v] = a[v];
+    }
+    __syncthreads();
+
+    // Columns: job = (map, v), consecutive threads on consecutive maps.
+    for (int job = threadIdx.x; job < T * H; job += kThreads) {
+        const int map = job % T, v = job / T;
+        const int64_t b = b0 + map;
+        float2 a[N];
+#pragma unroll
+        for (int u = 0; u < N; ++u)
+            a[u] = buf[map * MS + u * H + v];
+        fft_reg<N, false>(a, tw);
+        if (b < batch) {
+#pragma unroll
+            for (int u = 0; u < N; ++u)
+                spec[(int64_t)(u * H + v) * batch + b] = a[u];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Inverse transforms: half spectra (bin-major) -> the top-left m x m of the
+// real N x N maps, times scale.
+// ---------------------------------------------------------------------------
+
+template <int N>
+__global__ __launch_bounds__(kThreads) void c2r_kernel(const float2* __restrict__ spec, int batch,
+                                                       int m, float scale, float* __restrict__ y)
+{
+    constexpr int T = Tile<N>::T;
+    constexpr int H = N / 2 + 1;
+    constexpr int MS = N * H + 1;
+    __shared__ float2 buf[T * MS];
+    __shared__ float2 tw[N / 2];
+    const int64_t b0 = (int64_t)blockIdx.x * T;
+    load_twiddles<N>(tw);
+    __syncthreads();
+
+    // Columns: inverse along u; keep rows p < m.
+    for (int job = threadIdx.x; job < T * H; job += kThreads) {
+        const int map = job % T, v = job / T;
+        const int64_t b = b0 + map;
+        float2 a[N];
+        if (b < batch) {
+#pragma unroll
+            for (int u = 0; u < N; ++u)
+                a[u] = spec[(int64_t)(u * H + v) * batch + b];
+        } else {
+#pragma unroll
+            for (int u = 0; u < N; ++u)
+                a[u] = make_float2(0.0f, 0.0f);
+        }
+        fft_reg<N, true>(a, tw);
+#pragma unroll
+        for (int p = 0; p < N; ++p)
+            if (p < m)
+                buf[map * MS + p * H + v] = a[p];
+    }
+    __syncthreads();
+
+    // Rows p < m: the row is the half spectrum of a real signal.
+    for (int job = threadIdx.x; job < T * m; job += kThreads) {
+        const int map = job / m, p = job - map * m;
+        const int64_t b = b0 + map;
+        if (b >= batch)
+            continue;
+        const float2* in = buf + map * MS + p * H;
+        float2 a[N];
+#pragma unroll
+        for (int v = 0; v < H; ++v)
+            a[v] = in[v];
+#pragma unroll
+        for (int v = H; v < N; ++v)
+            a[v] = conjf2(in[N - v]);
+        fft_reg<N, true>(a, tw);
+        float* out = y + (b * m + p) * (int64_t)m;
+#pragma unroll
+        for (int q = 0; q < N; ++q)
+            if (q < m)
+                out[q] = a[q].x * scale;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per-bin complex matrix products.
+//   C[p][i][j] = sum_k A(p, i, k) B(p, k, j),  C row-major M x N per bin
+//   A(p,i,k) = A[p sAp + i lda + k] (AK: k contiguous) or A[p sAp + k lda + i]
+//   B(p,k,j) = B[p sBp + j ldb + k] (BK: k contiguous) or B[p sBp + k ldb + j]
+// with optional conjugation of A or B.
+// ---------------------------------------------------------------------------
+
+constexpr int kBM = 64, kBN = 64, kBK = 16;
+
+template <bool AK, bool BK, bool CA, bool CB>
+__global__ __launch_bounds__(kThreads) void cgemm_kernel(const float2* __restrict__ A,
+                                                         const float2* __restrict__ B,
+                                                         float2* __restrict__ C, int M, int N,
+                                                         int K, int64_t sAp, int64_t sBp,
+                                                         int lda, int ldb)
+{
+    __shared__ float2 As[kBK][kBM + 1];
+    __shared__ float2 Bs[kBK][kBN + 1];
+    const int p = blockIdx.z;
+    const int i0 = blockIdx.y * kBM, j0 = blockIdx.x * kBN;
+    const float2* Ap = A + p * sAp;
+    const float2* Bp = B + p * sBp;
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    float2 acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            acc[a][b] = make_float2(0.0f, 0.0f);
+
+    for (int k0 = 0; k0 < K; k0 += kBK) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int idx = threadIdx.x + r * kThreads;
+            int i, k;
+            if (AK) {
+                i = idx / kBK;
+                k = idx % kBK;
+            } else {
+                k = idx / kBM;
+                i = idx % kBM;
+            }
+            float2 v = make_float2(0.0f, 0.0f);
+            if (i0 + i < M && k0 + k < K)
+                v = AK ? Ap[(int64_t)(i0 + i) * lda + (k0 + k)] : Ap[(int64_t)(k0 + k) * lda + (i0 + i)];
+            As[k][i] = CA ? conjf2(v) : v;
+            int j;
+            if (BK) {
+                j = idx / kBK;
+                k = idx % kBK;
+            } else {
+                k = idx / kBN;
+                j = idx % kBN;
+            }
+            float2 w = make_float2(0.0f, 0.0f);
+            if (j0 + j < N && k0 + k < K)
+                w = BK ? Bp[(int64_t)(j0 + j) * ldb + (k0 + k)] : Bp[(int64_t)(k0 + k) * ldb + (j0 + j)];
+            Bs[k][j] = CB ? conjf2(w) : w;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kBK; ++k) {
+            float2 a[4], b[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                a[r] = As[k][ty * 4 + r];
+                b[r] = Bs[k][tx * 4 + r];
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    acc[r][c].x = fmaf(a[r].x, b[c].x, acc[r][c].x);
+                    acc[r][c].x = fmaf(-a[r].y, b[c].y, acc[r][c].x);
+                    acc[r][c].y = fmaf(a[r].x, b[c].y, acc[r][c].y);
+                    acc[r][c].y = fmaf(a[r].y, b[c].x, acc[r][c].y);
+                }
+        }
+        __syncthreads();
+    }
+    float2* Cp = C + (int64_t)p * M * N;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = i0 + ty * 4 + r;
+        if (i >= M)
+            continue;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int j = j0 + tx * 4 + c;
+            if (j < N)
+                Cp[(int64_t)i * N + j] = acc[r][c];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+
+static bool n_ok(int n) { return n == 8 || n == 16 || n == 32 || n == 64; }
+
+static int64_t bins(int n) { return (int64_t)n * (n / 2 + 1); }
+
+static bool overlaps(const void* a, size_t na, const void* b, size_t nb)
+{
+    uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+    return na && nb && pa < pb + nb && pb < pa + na;
+}
+
+static int status_of(hipError_t e) { return e == hipSuccess ? MESWISH_OK : MESWISH_EHIP; }
+
+static int launch_r2c(const float* x, int batch, int m, int n, float2* spec, hipStream_t s)
+{
+    const int T = 512 / n;
+    const unsigned grid = (unsigned)((batch + T - 1) / T);
+    switch (n) {
+    case 8: hipLaunchKernelGGL(r2c_kernel<8>, dim3(grid), dim3(kThreads), 0, s, x, batch, m, spec); break;
+    case 16: hipLaunchKernelGGL(r2c_kernel<16>, dim3(grid), dim3(kThreads), 0, s, x, batch, m, spec); break;
+    case 32: hipLaunchKernelGGL(r2c_kernel<32>, dim3(grid), dim3(kThreads), 0, s, x, batch, m, spec); break;
+    default: hipLaunchKernelGGL(r2c_kernel<64>, dim3(grid), dim3(kThreads), 0, s, x, batch, m, spec); break;
+    }
+    return status_of(hipGetLastError());
+}
+
+static int launch_c2r(const float2* spec, int batch, int n, int m, float scale, float* y, hipStream_t s)
+{
+    const int T = 512 / n;
+    const unsigned grid = (unsigned)((batch + T - 1) / T);
+    switch (n) {
+    case 8: hipLaunchKernelGGL(c2r_kernel<8>, dim3(grid), dim3(kThreads), 0, s, spec, batch, m, scale, y); break;
+    case 16: hipLaunchKernelGGL(c2r_kernel<16>, dim3(grid), dim3(kThreads), 0, s, spec, batch, m, scale, y); break;
+    case 32: hipLaunchKernelGGL(c2r_kernel<32>, dim3(grid), dim3(kThreads), 0, s, spec, batch, m, scale, y); break;
+    default: hipLaunchKernelGGL(c2r_kernel<64>, dim3(grid), dim3(kThreads), 0, s, spec, batch, m, scale, y); break;
+    }
+    return status_of(hipGetLastError());
+}
+
+// op 0: C[s][f'] = sum_f A[s][f] conj(B[f'][f]); 1: C[s][f] = sum_f' A[s][f'] B[f'][f];
+// 2: C[f'][f] = sum_s conj(A[s][f']) B[s][f].
+static int launch_cmul(int op, const float2* a, const float2* b, float2* c, int S, int f, int fo,
+                       int nbins, hipStream_t s)
+{
+    int M, N, K;
+    int64_t sAp, sBp;
+    int lda, ldb;
+    if (op == 0) {
+        M = S; N = fo; K = f; sAp = (int64_t)S * f; sBp = (int64_t)fo * f; lda = f; ldb = f;
+    } else if (op == 1) {
+        M = S; N = f; K = fo; sAp = (int64_t)S * fo; sBp = (int64_t)fo * f; lda = fo; ldb = f;
+    } else {
+        M = fo; N = f; K = S; sAp = (int64_t)S * fo; sBp = (int64_t)S * f; lda = fo; ldb = f;
+    }
+    dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM), (unsigned)nbins);
+    if (op == 0)
+        hipLaunchKernelGGL((cgemm_kernel<true, true, false, true>), grid, dim3(kThreads), 0, s, a, b,
+                           c, M, N, K, sAp, sBp, lda, ldb);
+    else if (op == 1)
+        hipLaunchKernelGGL((cgemm_kernel<true, false, false, false>), grid, dim3(kThreads), 0, s, a,
+                           b, c, M, N, K, sAp, sBp, lda, ldb);
+    else
+        hipLaunchKernelGGL((cgemm_kernel<false, false, true, false>), grid, dim3(kThreads), 0, s, a,
+                           b, c, M, N, K, sAp, sBp, lda, ldb);
+    return status_of(hipGetLastError());
+}
+
+static bool sizes_ok(int S, int f, int fo, int n, int k)
+{
+    if (!n_ok(n) || S < 1 || f < 1 || fo < 1 || k < 1 || k > n)
+        return false;
+    const int64_t P = bins(n);
+    const int64_t maps[3] = {(int64_t)S * f, (int64_t)S * fo, (int64_t)fo * f};
+    for (int64_t b : maps)
+        if (b >= (1ll << 31) || b * P >= (1ll << 31))
+            return false;
+    return true;
+}
+
+}  // namespace fftconv
+
+using namespace fftconv;
+
+extern "C" size_t fftconv_buffer_bytes(int S, int f, int fo, int n)
+{
+    if (!sizes_ok(S, f, fo, n, 1))
+        return 0;
+    const int64_t maps = (int64_t)S * f + (int64_t)S * fo + (int64_t)fo * f;
+    return (size_t)(maps * bins(n)) * sizeof(float2);
+}
+
+extern "C" int fftconv_r2c(const float* x, int batch, int m, int n, void* spec, void* stream)
+{
+    if (!n_ok(n) || batch < 0 || m < 1 || m > n || (batch > 0 && (!x || !spec)))
+        return MESWISH_EINVAL;
+    if ((int64_t)batch * bins(n) >= (1ll << 31))
+        return MESWISH_EINVAL;
+    if (batch == 0)
+        return MESWISH_OK;
+    if (((uintptr_t)x & 15u) || ((uintptr_t)spec & 7u))
+        return MESWISH_EINVAL;
+    if (overlaps(x, (size_t)batch * m * m * 4, spec, (size_t)batch * bins(n) * 8))
+        return MESWISH_EALIAS;
+    return launch_r2c(x, batch, m, n, static_cast<float2*>(spec), static_cast<hipStream_t>(stream));
+}
+
+extern "C" int fftconv_c2r(const void* spec, int batch, int n, int m, float scale, float* y,
+                           void* stream)
+{
+    if (!n_ok(n) || batch < 0 || m < 1 || m > n || !isfinite(scale) ||
+        (batch > 0 && (!y || !spec)))
+        return MESWISH_EINVAL;
+    if ((int64_t)batch * bins(n) >= (1ll << 31))
+        return MESWISH_EINVAL;
+    if (batch == 0)
+        return MESWISH_OK;
+    if (((uintptr_t)y & 3u) || ((uintptr_t)spec & 7u))
+        return MESWISH_EINVAL;
+    if (overlaps(y, (size_t)batch * m * m * 4, spec, (size_t)batch * bins(n) * 8))
+        return MESWISH_EALIAS;
+    return launch_c2r(static_cast<const float2*>(spec), batch, n, m, scale, y,
+                      static_cast<hipStream_t>(stream));
+}
+
+extern "C" int fftconv_cmul(int op, const void* a, const void* b, void* c, int S, int f, int fo,
+                            int nbins, void* stream)
+{
+    if (op < 0 || op > 2 || S < 1 || f < 1 || fo < 1 || nbins < 1 || nbins > 65535 || !a || !b || !c)
+        return MESWISH_EINVAL;
+    if (((uintptr_t)a & 7u) || ((uintptr_t)b & 7u) || ((uintptr_t)c & 7u))
+        return MESWISH_EINVAL;
+    const int64_t sa = op == 0 ? (int64_t)S * f : (int64_t)S * fo;
+    const int64_t sb = op == 2 ? (int64_t)S * f : (int64_t)fo * f;
+    const int64_t sc = op == 0 ? (int64_t)S * fo : op == 1 ? (int64_t)S * f : (int64_t)fo * f;
+    if (sa * nbins >= (1ll << 31) || sb * nbins >= (1ll << 31) || sc * nbins >= (1ll << 31))
+        return MESWISH_EINVAL;
+    const size_t cb = (size_t)(sc * nbins) * 8;
+    if (overlaps(c, cb, a, (size_t)(sa * nbins) * 8) || overlaps(c, cb, b, (size_t)(sb * nbins) * 8))
+        return MESWISH_EALIAS;
+    return launch_cmul(op, static_cast<const float2*>(a), static_cast<const float2*>(b),
+                       static_cast<float2*>(c), S, f, fo, nbins, static_cast<hipStream_t>(stream));
+}
+
+// The three operations.  The frequency buffer holds, in order, the spectra
+// of the operation's two inputs and of its result.
+static int run_op(int op, const float* in1, const float* in2, float* out, int S, int f, int fo,
+                  int n, int k, void* freq, size_t freq_bytes, hipStream_t s)
+{
+    if (!sizes_ok(S, f, fo, n, k) || !in1 || !in2 || !out || !freq)
+        return MESWISH_EINVAL;
+    if (freq_bytes < fftconv_buffer_bytes(S, f, fo, n))
+        return MESWISH_EINVAL;
+    if (((uintptr_t)in1 & 15u) || ((uintptr_t)in2 & 15u) || ((uintptr_t)out & 3u) ||
+        ((uintptr_t)freq & 7u))
+        return MESWISH_EINVAL;
+    const int m = n - k + 1;
+    const int64_t P = bins(n);
+    // Map counts and sizes of the two inputs and the output.
+    int64_t b1, b2, bo;
+    int m1, m2, mo;
+    if (op == 0) {        // x, w -> y
+        b1 = (int64_t)S * f; m1 = n; b2 = (int64_t)fo * f; m2 = k; bo = (int64_t)S * fo; mo = m;
+    } else if (op == 1) { // g, w -> gx
+        b1 = (int64_t)S * fo; m1 = m; b2 = (int64_t)fo * f; m2 = k; bo = (int64_t)S * f; mo = n;
+    } else {              // g, x -> gw (A = G, B = X)
+        b1 = (int64_t)S * fo; m1 = m; b2 = (int64_t)S * f; m2 = n; bo = (int64_t)fo * f; mo = k;
+    }
+    const size_t fb = fftconv_buffer_bytes(S, f, fo, n);
+    const size_t ob = (size_t)bo * mo * mo * 4;
+    if (overlaps(out, ob, in1, (size_t)b1 * m1 * m1 * 4) ||
+        overlaps(out, ob, in2, (size_t)b2 * m2 * m2 * 4) || overlaps(out, ob, freq, fb) ||
+        overlaps(freq, fb, in1, (size_t)b1 * m1 * m1 * 4) ||
+        overlaps(freq, fb, in2, (size_t)b2 * m2 * m2 * 4))
+        return MESWISH_EALIAS;
+    float2* s1 = static_cast<float2*>(freq);
+    float2* s2 = s1 + b1 * P;
+    float2* so = s2 + b2 * P;
+    int st = launch_r2c(in1, (int)b1, m1, n, s1, s);
+    if (st == MESWISH_OK)
+        st = launch_r2c(in2, (int)b2, m2, n, s2, s);
+    if (st == MESWISH_OK)
+        st = launch_cmul(op, s1, s2, so, S, f, fo, (int)P, s);
+    if (st == MESWISH_OK)
+        st = launch_c2r(so, (int)bo, n, mo, 1.0f / (float)(n * n), out, s);
+    return st;
+}
+
+extern "C" int fftconv_fprop(const float* x, const float* w, float* y, int S, int f, int fo, int n,
+                             int k, void* freq, size_t freq_bytes, void* stream)
+{
+    return run_op(0, x, w, y, S, f, fo, n, k, freq, freq_bytes, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int fftconv_bprop(const float* g, const float* w, float* gx, int S, int f, int fo, int n,
+                             int k, void* freq, size_t freq_bytes, void* stream)
+{
+    return run_op(1, g, w, gx, S, f, fo, n, k, freq, freq_bytes, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int fftconv_accgrad(const float* x, const float* g, float* gw, int S, int f, int fo,
+                               int n, int k, void* freq, size_t freq_bytes, void* stream)
+{
+    return run_op(2, g, x, gw, S, f, fo, n, k, freq, freq_bytes, static_cast<hipStream_t>(stream));
+}

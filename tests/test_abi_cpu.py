@@ -1,6 +1,6 @@
 """The C-ABI library: it loads, it exports every symbol include/meswish.h and
-include/dense_bn.h declare, and its host-side argument checks answer without
-a GPU.
+include/dense_bn.h and include/fft_conv.h declare, and its host-side
+argument checks answer without a GPU.
 
 No compute call is made here: every call below is rejected (or is a no-op)
 before anything is launched.
@@ -14,7 +14,7 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("meswish.h", "dense_bn.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("meswish.h", "dense_bn.h", "fft_conv.h")]
 LIB = os.path.join(ROOT, "memory_efficient_activation_amd", "libmeswish.so")
 
 
@@ -48,7 +48,9 @@ def test_header_declares_the_boundary():
         "meswish_act_bwd", "meswish_act_fwd",
         "meswish_copy", "meswish_plan", "meswish_strerror", "meswish_version", "swish_bwd",
         "swish_bwd_grouped", "swish_fwd", "swish_fwd_grouped",
-        "dense_bn_workspace_bytes", "dense_bn_stats", "dense_bn_relu_fwd", "dense_bn_relu_bwd"])
+        "dense_bn_workspace_bytes", "dense_bn_stats", "dense_bn_relu_fwd", "dense_bn_relu_bwd",
+        "fftconv_buffer_bytes", "fftconv_fprop", "fftconv_bprop", "fftconv_accgrad",
+        "fftconv_r2c", "fftconv_c2r", "fftconv_cmul"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -219,3 +221,43 @@ def test_dense_alias_rejections_without_gpu(lib):
     # Statistics on top of the source.
     assert lib.dense_bn_stats(base, n, c, hw, _lib.F32, base + 64, base + 0x700000, 1 << 16,
                               None) == _lib.EALIAS
+
+
+def test_fft_buffer_size_and_rejections(lib):
+    """fftconv_*: frequency-buffer sizing ((S f + S f' + f f') n (n/2 + 1)
+    complex binary32 values) and the checks that run before any launch."""
+    from memory_efficient_activation_amd import _lib
+    assert lib.fftconv_buffer_bytes(128, 96, 256, 32) == (128 * 96 + 128 * 256 + 256 * 96) * 32 * 17 * 8
+    assert lib.fftconv_buffer_bytes(1, 1, 1, 8) == 3 * 8 * 5 * 8
+    for n in (4, 12, 128, 0):
+        assert lib.fftconv_buffer_bytes(2, 2, 2, n) == 0
+    assert lib.fftconv_buffer_bytes(0, 2, 2, 8) == 0
+    g = 0x10000000
+    big = 1 << 40
+    # n not a supported power of two; k > n; null pointers; too small a buffer.
+    assert lib.fftconv_fprop(g, g + 4096, g + 8192, 2, 2, 2, 12, 3, g + big, big, None) == _lib.EINVAL
+    assert lib.fftconv_fprop(g, g + 4096, g + 8192, 2, 2, 2, 8, 9, g + big, big, None) == _lib.EINVAL
+    assert lib.fftconv_fprop(None, g, g, 2, 2, 2, 8, 3, g, big, None) == _lib.EINVAL
+    assert lib.fftconv_bprop(g, g, g, 2, 2, 2, 8, 3, g, 16, None) == _lib.EINVAL
+    # Stage calls: bad op, m > n, empty batch (no-op).
+    assert lib.fftconv_cmul(3, g, g, g, 1, 1, 1, 10, None) == _lib.EINVAL
+    assert lib.fftconv_r2c(g, 4, 9, 8, g + big, None) == _lib.EINVAL
+    assert lib.fftconv_r2c(None, 0, 3, 8, None, None) == _lib.OK
+    assert lib.fftconv_c2r(None, 0, 8, 3, 1.0, None, None) == _lib.OK
+    assert lib.fftconv_c2r(g, 2, 8, 3, float("nan"), g + big, None) == _lib.EINVAL
+
+
+def test_fft_alias_rejections_without_gpu(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("covered with real device buffers by the GPU tests")
+    from memory_efficient_activation_amd import _lib
+    g = 0x10000000
+    fb = lib.fftconv_buffer_bytes(2, 3, 4, 8)
+    # Output on top of the frequency buffer; buffer on top of an input.
+    assert lib.fftconv_fprop(g, g + 0x10000, g + 0x200000 + 64, 2, 3, 4, 8, 3, g + 0x200000, fb,
+                             None) == _lib.EALIAS
+    assert lib.fftconv_fprop(g, g + 0x10000, g + 0x20000, 2, 3, 4, 8, 3, g + 256, fb,
+                             None) == _lib.EALIAS
+    # Stage calls: spectrum output over the input maps.
+    assert lib.fftconv_r2c(g, 4, 8, 8, g + 64, None) == _lib.EALIAS
