@@ -38,6 +38,13 @@ configuration): per training step of that layer, the statistics of its
 newest source, the forward, the backward's re-population of the shared
 buffer, and the backward (reduction + apply).  ``--dense-dtype`` picks
 binary32 (default) or bfloat16 feature maps.
+
+``--fft`` measures the FFT convolution layer ("Fast Training of
+Convolutional Networks through FFTs") on S=128, f=96, f'=256, n=32, k=7:
+one step = forward + input gradient + weight gradient, each transforming
+its inputs into one reused frequency buffer, multiplying per frequency
+bin, and transforming back.  Reported against PyTorch's direct convolution
+(MIOpen) on the same layer.
 """
 
 from __future__ import annotations
@@ -88,6 +95,8 @@ def parse_args():
     p.add_argument("--dense", action="store_true",
                    help="measure the shared-buffer DenseNet layer stage instead")
     p.add_argument("--dense-dtype", default="f32", choices=["f32", "bf16"])
+    p.add_argument("--fft", action="store_true",
+                   help="measure the FFT convolution layer instead")
     return p.parse_args()
 
 
@@ -474,6 +483,164 @@ def measure_dense(args, lib, torch, dev):
     return result
 
 
+# Dense binary32 matrix-core (MFMA) throughput of MI355X, AMD's published
+# figure.  (The vector ALUs without packed instructions, which this build
+# disables, give 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz = 78.6.)
+PEAK_FP32_MFMA_TFLOPS = 157.3
+
+
+def measure_fft(args, lib, torch, dev):
+    """The FFT convolution layer: see the module docstring (``--fft``)."""
+    from memory_efficient_activation_amd import _lib, fft, fft_inputs
+
+    L = fft_inputs.bench_layer()
+    S, f, fo, n, k, m = L.S, L.f, L.fo, L.n, L.k, L.m
+    P = fft.bins(n)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    x, w, g = (torch.from_numpy(a).to(dev) for a in (L.x, L.w, L.g))
+    y = torch.empty((S, fo, m, m), device=dev)
+    gx = torch.empty((S, f, n, n), device=dev)
+    gw = torch.empty((fo, f, k, k), device=dev)
+    fb = lib.fftconv_buffer_bytes(S, f, fo, n)
+    freq = torch.empty(fb, dtype=torch.uint8, device=dev)
+    fp = freq.data_ptr()
+
+    def op_f(_):
+        _lib.check(lib.fftconv_fprop(x.data_ptr(), w.data_ptr(), y.data_ptr(), S, f, fo, n, k, fp,
+                                     fb, sh), "fftconv_fprop")
+
+    def op_b(_):
+        _lib.check(lib.fftconv_bprop(g.data_ptr(), w.data_ptr(), gx.data_ptr(), S, f, fo, n, k, fp,
+                                     fb, sh), "fftconv_bprop")
+
+    def op_a(_):
+        _lib.check(lib.fftconv_accgrad(x.data_ptr(), g.data_ptr(), gw.data_ptr(), S, f, fo, n, k,
+                                       fp, fb, sh), "fftconv_accgrad")
+
+    def step(i):
+        op_f(i)
+        op_b(i)
+        op_a(i)
+
+    # The forward's stages on the same buffer layout: X, W, then Y.
+    sx = fp
+    sw = sx + S * f * P * 8
+    sy = sw + fo * f * P * 8
+
+    def st_r2c_x(_):
+        _lib.check(lib.fftconv_r2c(x.data_ptr(), S * f, n, n, sx, sh), "fftconv_r2c")
+
+    def st_r2c_w(_):
+        _lib.check(lib.fftconv_r2c(w.data_ptr(), fo * f, k, n, sw, sh), "fftconv_r2c")
+
+    def st_cmul(_):
+        _lib.check(lib.fftconv_cmul(0, sx, sw, sy, S, f, fo, P, sh), "fftconv_cmul")
+
+    def st_c2r(_):
+        _lib.check(lib.fftconv_c2r(sy, S * fo, n, m, 1.0 / (n * n), y.data_ptr(), sh), "fftconv_c2r")
+
+    def region(fn, count):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        a.record(stream)
+        for i in range(count):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, a.elapsed_time(b)
+
+    K = max(5, args.steps // 10)
+    for i in range(max(2, args.warmup // 10)):
+        step(i)
+    wall, _ = region(step, K)
+    log(f"[bench] fft: timed {K} layer steps: wall {wall * 1e3:.2f} ms")
+    ops = {}
+    for name, fn in (("fprop", op_f), ("bprop", op_b), ("accgrad", op_a)):
+        _, ms = region(fn, K)
+        ops[name] = round(ms / K, 4)
+    stage_bytes = {"r2c_x": S * f * (n * n * 4 + P * 8), "r2c_w": fo * f * (k * k * 4 + P * 8),
+                   "c2r_y": S * fo * (P * 8 + m * m * 4)}
+    stages = {}
+    for name, fn in (("r2c_x", st_r2c_x), ("r2c_w", st_r2c_w), ("cmul", st_cmul), ("c2r_y", st_c2r)):
+        _, ms = region(fn, K)
+        us = ms * 1e3 / K
+        stages[name] = {"mean_us": round(us, 2)}
+        if name in stage_bytes:
+            stages[name]["bytes"] = stage_bytes[name]
+            stages[name]["GBps"] = round(stage_bytes[name] / (us * 1e-6) / 1e9, 1)
+    cm_flops = 8 * S * fo * f * P
+    cm_us = stages["cmul"]["mean_us"]
+    cm_tf = cm_flops / (cm_us * 1e-6) / 1e12
+    stages["cmul"].update({"flops": cm_flops, "TFLOPs": round(cm_tf, 2),
+                           "bytes": P * 8 * (S * f + fo * f + S * fo)})
+
+    # PyTorch's direct convolution (MIOpen) on the same layer: forward and
+    # both gradients.
+    tx = x.clone().requires_grad_(True)
+    tw = w.clone().requires_grad_(True)
+
+    def torch_step(_):
+        ty = torch.nn.functional.conv2d(tx, tw)
+        ty.backward(g)
+
+    for i in range(3):
+        torch_step(i)
+    twall, _ = region(torch_step, K)
+    direct_flops = 2 * S * fo * f * m * m * k * k   # per operation
+    step_ms = wall * 1e3 / K
+
+    result = {
+        "metric": f"layer steps/s (fprop + bprop + accgrad), FFT convolution S={S} f={f} f'={fo} "
+                  f"n={n} k={k} fp32, 1 MI355X",
+        "value": round(1e3 / step_ms, 2),
+        "unit": "layer steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": max(2, args.warmup // 10),
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"FFT convolution layer, minibatch {S}, {f} -> {fo} feature maps, "
+                               f"{n}x{n} inputs, {k}x{k} kernels, fp32",
+                   "S": S, "f": f, "fo": fo, "n": n, "k": k, "bins": P,
+                   "frequency_buffer_bytes": fb},
+        "ms_per_operation": ops,
+        "stages_fprop": stages,
+        "direct_equivalent_TFLOPs": round(3 * direct_flops / (step_ms * 1e-3) / 1e12, 2),
+        "roofline": {"kernel": "cgemm_mfma_kernel (per-bin complex products, forward)",
+                     "bound": "mfma", "achieved": round(cm_tf, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(cm_tf / PEAK_FP32_MFMA_TFLOPS, 4),
+                     "traffic": None, "traffic_note": "no counter summary for this kernel",
+                     "flops_per_launch": cm_flops, "mean_launch_us": cm_us},
+        "torch_direct_conv_same_layer": {"ms_per_step": round(twall * 1e3 / K, 4),
+                                         "note": "F.conv2d forward + autograd input and weight "
+                                                 "gradients (MIOpen), fp32"},
+    }
+    if not args.no_cpu_baseline:
+        import numpy as np
+        from oracle import fft_oracle
+        sub = 2
+        c0 = time.perf_counter()
+        fft_oracle.fprop_fft(L.x[:sub], L.w)
+        fft_oracle.bprop_fft(L.g[:sub], L.w, n)
+        fft_oracle.accgrad_fft(L.x[:sub], L.g[:sub], k)
+        ct = time.perf_counter() - c0
+        est_ms = ct * 1e3 * S / sub
+        result["cpu_baseline"] = {"value": round(1e3 / est_ms, 4), "unit": "layer steps/s",
+                                  "cores": 1, "kind": "oracle",
+                                  "sample": f"{sub} of the {S} minibatch samples, numpy binary64 "
+                                            f"spectral path, {ct:.2f} s, scaled by {S // sub}"}
+        log(f"[bench] fft: cpu baseline {ct:.2f} s for {sub} samples")
+        del np
+    return result
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -495,6 +662,9 @@ def main():
     lib = _lib.library()
     if args.dense:
         print(json.dumps(measure_dense(args, lib, torch, dev)), flush=True)
+        return
+    if args.fft:
+        print(json.dumps(measure_fft(args, lib, torch, dev)), flush=True)
         return
 
     t_gen = time.perf_counter()

@@ -11,8 +11,9 @@
 // Design for MI355X (CDNA4):
 //   * Transforms.  The page's point is that a GPU FFT library parallelises
 //     within one large transform, while this workload is many small ones.
-//     Here one block of 256 threads transforms T maps of n x n at once
-//     (T n = 512 rows): every thread runs whole length-n transforms in
+//     Here one block transforms T maps of n x n at once (T (n/2 + 1)
+//     threads: one column transform per thread): every thread runs whole
+//     length-n transforms in
 //     registers (radix-2 Cooley-Tukey, fully unrolled: no data-dependent
 //     indexing, no scratch), first over rows, then -- through LDS -- over
 //     the n/2 + 1 columns of the half spectrum.  Twiddles e^{-2 pi i j/n}
@@ -22,8 +23,11 @@
 //     matrices of the contraction are contiguous and the column pass writes
 //     T consecutive maps of one bin together.
 //   * Contraction.  For every bin, a complex matrix product (M x K) (K x N)
-//     -- S x f by f x f' for the forward.  Tiles of 64 x 64 complex outputs,
-//     K in steps of 16 through LDS, 4 x 4 complex outputs per thread.
+//     -- S x f by f x f' for the forward: a dense contraction, so it runs on
+//     the matrix cores (v_mfma_f32_32x32x2f32, binary32 in and out), the
+//     complex product expanded into a real one of twice the depth and
+//     width.  Tiles of 64 x 64 complex outputs, K in steps of 16 through
+//     LDS; a vector-ALU version of the same tiling is kept for comparison.
 //   * Inverse.  Column transforms first, keeping only the rows that survive
 //     the crop, then row transforms of the Hermitian half rows; only the
 //     kept m x m corner is written, scaled by 1/n^2.
@@ -111,8 +115,15 @@ __device__ __forceinline__ void load_twiddles(float2* tw)
     }
 }
 
-// Maps per block: T N = 512 rows for every supported N.
-template <int N> struct Tile { static constexpr int T = 512 / N; };
+// Maps per block (a power of two: the T maps of one bin fill whole 128-byte
+// lines) and threads per block: one column transform per thread, and the
+// T N rows in two rounds.
+template <int N> struct Tile {
+    static constexpr int T = N <= 8 ? 64 : N == 16 ? 32 : N == 32 ? 16 : 8;
+    // n = 64 stays at 4 waves (its length-64 transforms need the register
+    // file of a single wave per SIMD); its 264 column jobs take two rounds.
+    static constexpr int kThreads = N == 64 ? 256 : T * (N / 2 + 1);
+};
 
 // ---------------------------------------------------------------------------
 // Forward transforms: `batch` real m x m maps (row-major, contiguous),
@@ -120,7 +131,7 @@ template <int N> struct Tile { static constexpr int T = 512 / N; };
 // ---------------------------------------------------------------------------
 
 template <int N>
-__global__ __launch_bounds__(kThreads) void r2c_kernel(const float* __restrict__ x, int batch,
+__global__ __launch_bounds__(Tile<N>::kThreads) void r2c_kernel(const float* __restrict__ x, int batch,
                                                        int m, float2* __restrict__ spec)
 {
     constexpr int T = Tile<N>::T;
@@ -133,7 +144,8 @@ __global__ __launch_bounds__(kThreads) void r2c_kernel(const float* __restrict__
     __syncthreads();
 
     // Rows: job = (map, r).
-    for (int job = threadIdx.x; job < T * N; job += kThreads) {
+    constexpr int NT = Tile<N>::kThreads;
+    for (int job = threadIdx.x; job < T * N; job += NT) {
         const int map = job / N, r = job - map * N;
         const int64_t b = b0 + map;
         float2* out = buf + map * MS + r * H;
@@ -167,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void r2c_kernel(const float* __restrict__
     __syncthreads();
 
     // Columns: job = (map, v), consecutive threads on consecutive maps.
-    for (int job = threadIdx.x; job < T * H; job += kThreads) {
+    for (int job = threadIdx.x; job < T * H; job += NT) {
         const int map = job % T, v = job / T;
         const int64_t b = b0 + map;
         float2 a[N];
@@ -176,9 +188,12 @@ __global__ __launch_bounds__(kThreads) void r2c_kernel(const float* __restrict__
             a[u] = buf[map * MS + u * H + v];
         fft_reg<N, false>(a, tw);
         if (b < batch) {
+            // Bin (u, v) of map b: a per-thread base plus a block-uniform step.
+            float2* col = spec + (int64_t)v * batch + b;
+            const int64_t step = (int64_t)H * batch;
 #pragma unroll
             for (int u = 0; u < N; ++u)
-                spec[(int64_t)(u * H + v) * batch + b] = a[u];
+                col[u * step] = a[u];
         }
     }
 }
@@ -189,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void r2c_kernel(const float* __restrict__
 // ---------------------------------------------------------------------------
 
 template <int N>
-__global__ __launch_bounds__(kThreads) void c2r_kernel(const float2* __restrict__ spec, int batch,
+__global__ __launch_bounds__(Tile<N>::kThreads) void c2r_kernel(const float2* __restrict__ spec, int batch,
                                                        int m, float scale, float* __restrict__ y)
 {
     constexpr int T = Tile<N>::T;
@@ -202,14 +217,17 @@ __global__ __launch_bounds__(kThreads) void c2r_kernel(const float2* __restrict_
     __syncthreads();
 
     // Columns: inverse along u; keep rows p < m.
-    for (int job = threadIdx.x; job < T * H; job += kThreads) {
+    constexpr int NT = Tile<N>::kThreads;
+    for (int job = threadIdx.x; job < T * H; job += NT) {
         const int map = job % T, v = job / T;
         const int64_t b = b0 + map;
         float2 a[N];
         if (b < batch) {
+            const float2* col = spec + (int64_t)v * batch + b;
+            const int64_t step = (int64_t)H * batch;
 #pragma unroll
             for (int u = 0; u < N; ++u)
-                a[u] = spec[(int64_t)(u * H + v) * batch + b];
+                a[u] = col[u * step];
         } else {
 #pragma unroll
             for (int u = 0; u < N; ++u)
@@ -224,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void c2r_kernel(const float2* __restrict_
     __syncthreads();
 
     // Rows p < m: the row is the half spectrum of a real signal.
-    for (int job = threadIdx.x; job < T * m; job += kThreads) {
+    for (int job = threadIdx.x; job < T * m; job += NT) {
         const int map = job / m, p = job - map * m;
         const int64_t b = b0 + map;
         if (b >= batch)
@@ -239,10 +257,19 @@ __global__ __launch_bounds__(kThreads) void c2r_kernel(const float2* __restrict_
             a[v] = conjf2(in[N - v]);
         fft_reg<N, true>(a, tw);
         float* out = y + (b * m + p) * (int64_t)m;
+        if ((m & 1) == 0 && ((uintptr_t)y & 7u) == 0) {
+            // Even m: every row starts 8-byte aligned; store pairs.
 #pragma unroll
-        for (int q = 0; q < N; ++q)
-            if (q < m)
-                out[q] = a[q].x * scale;
+            for (int q = 0; q < N; q += 2)
+                if (q < m)
+                    *reinterpret_cast<float2*>(out + q) =
+                        make_float2(a[q].x * scale, a[q + 1].x * scale);
+        } else {
+#pragma unroll
+            for (int q = 0; q < N; ++q)
+                if (q < m)
+                    out[q] = a[q].x * scale;
+        }
     }
 }
 
@@ -342,9 +369,100 @@ __global__ __launch_bounds__(kThreads) void cgemm_kernel(const float2* __restric
     }
 }
 
+// The same product on the matrix cores.  A complex K-sum is a real sum over
+// 2K terms: with A' = [Re A, Im A] interleaved along k and, for every
+// complex B[k][n], the real 2 x 2 block [[Re B, Im B], [-Im B, Re B]] at
+// rows (2k, 2k+1) and columns (2n, 2n+1) of B', the real product A' B'
+// holds Re C at even and Im C at odd columns.  Each wave owns 32 rows and
+// 32 complex columns (two 32 x 32 real tiles of v_mfma_f32_32x32x2f32);
+// lane l feeds A'[l%32][l/32] and B'[l/32][l%32] and receives, in
+// accumulator v, C'[8 (v/4) + 4 (l/32) + v%4][l%32].
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <bool AK, bool BK, bool CA, bool CB>
+__global__ __launch_bounds__(kThreads) void cgemm_mfma_kernel(const float2* __restrict__ A,
+                                                              const float2* __restrict__ B,
+                                                              float2* __restrict__ C, int M,
+                                                              int N, int K, int64_t sAp,
+                                                              int64_t sBp, int lda, int ldb)
+{
+    __shared__ float2 As[kBK][kBM + 1];
+    __shared__ float2 Bs[kBK][kBN + 1];
+    const int p = blockIdx.z;
+    const int i0 = blockIdx.y * kBM, j0 = blockIdx.x * kBN;
+    const float2* Ap = A + p * sAp;
+    const float2* Bp = B + p * sBp;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int r = lane & 31, h = lane >> 5;
+    f32x16 acc0 = {0}, acc1 = {0};
+
+    for (int k0 = 0; k0 < K; k0 += kBK) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int idx = threadIdx.x + q * kThreads;
+            int i, k;
+            if (AK) {
+                i = idx / kBK;
+                k = idx % kBK;
+            } else {
+                k = idx / kBM;
+                i = idx % kBM;
+            }
+            float2 v = make_float2(0.0f, 0.0f);
+            if (i0 + i < M && k0 + k < K)
+                v = AK ? Ap[(int64_t)(i0 + i) * lda + (k0 + k)] : Ap[(int64_t)(k0 + k) * lda + (i0 + i)];
+            As[k][i] = CA ? conjf2(v) : v;
+            int j;
+            if (BK) {
+                j = idx / kBK;
+                k = idx % kBK;
+            } else {
+                k = idx / kBN;
+                j = idx % kBN;
+            }
+            float2 w = make_float2(0.0f, 0.0f);
+            if (j0 + j < N && k0 + k < K)
+                w = BK ? Bp[(int64_t)(j0 + j) * ldb + (k0 + k)] : Bp[(int64_t)(k0 + k) * ldb + (j0 + j)];
+            Bs[k][j] = CB ? conjf2(w) : w;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < kBK; ++kk) {
+            const float2 a = As[kk][wm * 32 + r];
+            const float av = h ? a.y : a.x;
+            const float2 b0 = Bs[kk][wn * 32 + (r >> 1)];
+            const float2 b1 = Bs[kk][wn * 32 + 16 + (r >> 1)];
+            const float bv0 = h ? ((r & 1) ? b0.x : -b0.y) : ((r & 1) ? b0.y : b0.x);
+            const float bv1 = h ? ((r & 1) ? b1.x : -b1.y) : ((r & 1) ? b1.y : b1.x);
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv0, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv1, acc1, 0, 0, 0);
+        }
+        __syncthreads();
+    }
+    float* Cf = reinterpret_cast<float*>(C + (int64_t)p * M * N);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int i = i0 + wm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (i >= M)
+            continue;
+        const int n0 = j0 + wn * 32 + (r >> 1);
+        const int n1 = n0 + 16;
+        if (n0 < N)
+            Cf[2 * ((int64_t)i * N + n0) + (r & 1)] = acc0[v];
+        if (n1 < N)
+            Cf[2 * ((int64_t)i * N + n1) + (r & 1)] = acc1[v];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
+
+// 1: per-bin products on the matrix cores; 0: on the vector ALUs.
+#ifndef FFTCONV_MFMA
+#define FFTCONV_MFMA 1
+#endif
 
 static bool n_ok(int n) { return n == 8 || n == 16 || n == 32 || n == 64; }
 
@@ -358,28 +476,39 @@ static bool overlaps(const void* a, size_t na, const void* b, size_t nb)
 
 static int status_of(hipError_t e) { return e == hipSuccess ? MESWISH_OK : MESWISH_EHIP; }
 
+template <int N>
+static void r2c_launch(const float* x, int batch, int m, float2* spec, hipStream_t s)
+{
+    const unsigned grid = (unsigned)((batch + Tile<N>::T - 1) / Tile<N>::T);
+    hipLaunchKernelGGL(r2c_kernel<N>, dim3(grid), dim3(Tile<N>::kThreads), 0, s, x, batch, m, spec);
+}
+
+template <int N>
+static void c2r_launch(const float2* spec, int batch, int m, float scale, float* y, hipStream_t s)
+{
+    const unsigned grid = (unsigned)((batch + Tile<N>::T - 1) / Tile<N>::T);
+    hipLaunchKernelGGL(c2r_kernel<N>, dim3(grid), dim3(Tile<N>::kThreads), 0, s, spec, batch, m,
+                       scale, y);
+}
+
 static int launch_r2c(const float* x, int batch, int m, int n, float2* spec, hipStream_t s)
 {
-    const int T = 512 / n;
-    const unsigned grid = (unsigned)((batch + T - 1) / T);
     switch (n) {
-    case 8: hipLaunchKernelGGL(r2c_kernel<8>, dim3(grid), dim3(kThreads), 0, s, x, batch, m, spec); break;
-    case 16: hipLaunchKernelGGL(r2c_kernel<16>, dim3(grid), dim3(kThreads), 0, s, x, batch, m, spec); break;
-    case 32: hipLaunchKernelGGL(r2c_kernel<32>, dim3(grid), dim3(kThreads), 0, s, x, batch, m, spec); break;
-    default: hipLaunchKernelGGL(r2c_kernel<64>, dim3(grid), dim3(kThreads), 0, s, x, batch, m, spec); break;
+    case 8: r2c_launch<8>(x, batch, m, spec, s); break;
+    case 16: r2c_launch<16>(x, batch, m, spec, s); break;
+    case 32: r2c_launch<32>(x, batch, m, spec, s); break;
+    default: r2c_launch<64>(x, batch, m, spec, s); break;
     }
     return status_of(hipGetLastError());
 }
 
 static int launch_c2r(const float2* spec, int batch, int n, int m, float scale, float* y, hipStream_t s)
 {
-    const int T = 512 / n;
-    const unsigned grid = (unsigned)((batch + T - 1) / T);
     switch (n) {
-    case 8: hipLaunchKernelGGL(c2r_kernel<8>, dim3(grid), dim3(kThreads), 0, s, spec, batch, m, scale, y); break;
-    case 16: hipLaunchKernelGGL(c2r_kernel<16>, dim3(grid), dim3(kThreads), 0, s, spec, batch, m, scale, y); break;
-    case 32: hipLaunchKernelGGL(c2r_kernel<32>, dim3(grid), dim3(kThreads), 0, s, spec, batch, m, scale, y); break;
-    default: hipLaunchKernelGGL(c2r_kernel<64>, dim3(grid), dim3(kThreads), 0, s, spec, batch, m, scale, y); break;
+    case 8: c2r_launch<8>(spec, batch, m, scale, y, s); break;
+    case 16: c2r_launch<16>(spec, batch, m, scale, y, s); break;
+    case 32: c2r_launch<32>(spec, batch, m, scale, y, s); break;
+    default: c2r_launch<64>(spec, batch, m, scale, y, s); break;
     }
     return status_of(hipGetLastError());
 }
@@ -400,15 +529,21 @@ static int launch_cmul(int op, const float2* a, const float2* b, float2* c, int 
         M = fo; N = f; K = S; sAp = (int64_t)S * fo; sBp = (int64_t)S * f; lda = fo; ldb = f;
     }
     dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM), (unsigned)nbins);
+#if FFTCONV_MFMA
+#define FFTCONV_GEMM cgemm_mfma_kernel
+#else
+#define FFTCONV_GEMM cgemm_kernel
+#endif
     if (op == 0)
-        hipLaunchKernelGGL((cgemm_kernel<true, true, false, true>), grid, dim3(kThreads), 0, s, a, b,
+        hipLaunchKernelGGL((FFTCONV_GEMM<true, true, false, true>), grid, dim3(kThreads), 0, s, a, b,
                            c, M, N, K, sAp, sBp, lda, ldb);
     else if (op == 1)
-        hipLaunchKernelGGL((cgemm_kernel<true, false, false, false>), grid, dim3(kThreads), 0, s, a,
+        hipLaunchKernelGGL((FFTCONV_GEMM<true, false, false, false>), grid, dim3(kThreads), 0, s, a,
                            b, c, M, N, K, sAp, sBp, lda, ldb);
     else
-        hipLaunchKernelGGL((cgemm_kernel<false, false, true, false>), grid, dim3(kThreads), 0, s, a,
+        hipLaunchKernelGGL((FFTCONV_GEMM<false, false, true, false>), grid, dim3(kThreads), 0, s, a,
                            b, c, M, N, K, sAp, sBp, lda, ldb);
+#undef FFTCONV_GEMM
     return status_of(hipGetLastError());
 }
 
