@@ -571,6 +571,20 @@ def measure_fft(args, lib, torch, dev):
         if name in stage_bytes:
             stages[name]["bytes"] = stage_bytes[name]
             stages[name]["GBps"] = round(stage_bytes[name] / (us * 1e-6) / 1e9, 1)
+    # Copy kernel over the input maps (read + write), same run: the HBM
+    # ceiling at this size, and the calibration of the traffic counters.
+    cbytes = S * f * n * n * 4
+    csrc = torch.empty(cbytes, dtype=torch.uint8, device=dev)
+    cdst = torch.empty(cbytes, dtype=torch.uint8, device=dev)
+
+    def k_copy(_):
+        _lib.check(lib.meswish_copy(csrc.data_ptr(), cdst.data_ptr(), cbytes, sh), "meswish_copy")
+
+    for i in range(3):
+        k_copy(i)
+    _, cms = region(k_copy, K)
+    copy_us = cms * 1e3 / K
+    del csrc, cdst
     cm_flops = 8 * S * fo * f * P
     cm_us = stages["cmul"]["mean_us"]
     cm_tf = cm_flops / (cm_us * 1e-6) / 1e12
@@ -618,6 +632,8 @@ def measure_fft(args, lib, torch, dev):
                      "unit": "TFLOP/s", "frac": round(cm_tf / PEAK_FP32_MFMA_TFLOPS, 4),
                      "traffic": None, "traffic_note": "no counter summary for this kernel",
                      "flops_per_launch": cm_flops, "mean_launch_us": cm_us},
+        "copy_ceiling": {"bytes": 2 * cbytes, "mean_us": round(copy_us, 2),
+                         "GBps": round(2 * cbytes / (copy_us * 1e-6) / 1e9, 1)},
         "torch_direct_conv_same_layer": {"ms_per_step": round(twall * 1e3 / K, 4),
                                          "note": "F.conv2d forward + autograd input and weight "
                                                  "gradients (MIOpen), fp32"},

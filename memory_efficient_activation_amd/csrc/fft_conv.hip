@@ -379,17 +379,29 @@ __global__ __launch_bounds__(kThreads) void cgemm_kernel(const float2* __restric
 // accumulator v, C'[8 (v/4) + 4 (l/32) + v%4][l%32].
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+//
+// Grid: one dimension, XCD-aware.  The dispatcher deals consecutive blocks to
+// the 8 XCDs in turn, and each XCD has its own L2.  The tiles of one bin
+// share their A and B operands, so all of them go to one XCD: block L has
+// XCD x = L % 8 and q = L / 8; it computes tile q % tiles of bin
+// (q / tiles) * 8 + x.  Bins past the last (padding to a multiple of 8)
+// exit at once.
 template <bool AK, bool BK, bool CA, bool CB>
 __global__ __launch_bounds__(kThreads) void cgemm_mfma_kernel(const float2* __restrict__ A,
                                                               const float2* __restrict__ B,
                                                               float2* __restrict__ C, int M,
                                                               int N, int K, int64_t sAp,
-                                                              int64_t sBp, int lda, int ldb)
+                                                              int64_t sBp, int lda, int ldb,
+                                                              int tiles_n, int tiles, int nbins)
 {
     __shared__ float2 As[kBK][kBM + 1];
     __shared__ float2 Bs[kBK][kBN + 1];
-    const int p = blockIdx.z;
-    const int i0 = blockIdx.y * kBM, j0 = blockIdx.x * kBN;
+    const int xcd = (int)(blockIdx.x & 7u), q = (int)(blockIdx.x >> 3);
+    const int p = (q / tiles) * 8 + xcd;
+    if (p >= nbins)
+        return;
+    const int tile = q % tiles;
+    const int i0 = (tile / tiles_n) * kBM, j0 = (tile % tiles_n) * kBN;
     const float2* Ap = A + p * sAp;
     const float2* Bp = B + p * sBp;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -397,7 +409,11 @@ __global__ __launch_bounds__(kThreads) void cgemm_mfma_kernel(const float2* __re
     const int r = lane & 31, h = lane >> 5;
     f32x16 acc0 = {0}, acc1 = {0};
 
-    for (int k0 = 0; k0 < K; k0 += kBK) {
+    // Global -> register staging of one K-tile (4 A and 4 B values per
+    // thread); the next tile's loads are issued before the current tile's
+    // products, so their latency overlaps the matrix-core work.
+    float2 ra[4], rb[4];
+    auto fetch = [&](int k0) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int idx = threadIdx.x + q * kThreads;
@@ -412,7 +428,7 @@ __global__ __launch_bounds__(kThreads) void cgemm_mfma_kernel(const float2* __re
             float2 v = make_float2(0.0f, 0.0f);
             if (i0 + i < M && k0 + k < K)
                 v = AK ? Ap[(int64_t)(i0 + i) * lda + (k0 + k)] : Ap[(int64_t)(k0 + k) * lda + (i0 + i)];
-            As[k][i] = CA ? conjf2(v) : v;
+            ra[q] = CA ? conjf2(v) : v;
             int j;
             if (BK) {
                 j = idx / kBK;
@@ -424,9 +440,30 @@ __global__ __launch_bounds__(kThreads) void cgemm_mfma_kernel(const float2* __re
             float2 w = make_float2(0.0f, 0.0f);
             if (j0 + j < N && k0 + k < K)
                 w = BK ? Bp[(int64_t)(j0 + j) * ldb + (k0 + k)] : Bp[(int64_t)(k0 + k) * ldb + (j0 + j)];
-            Bs[k][j] = CB ? conjf2(w) : w;
+            rb[q] = CB ? conjf2(w) : w;
         }
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int idx = threadIdx.x + q * kThreads;
+            if (AK)
+                As[idx % kBK][idx / kBK] = ra[q];
+            else
+                As[idx / kBM][idx % kBM] = ra[q];
+            if (BK)
+                Bs[idx % kBK][idx / kBK] = rb[q];
+            else
+                Bs[idx / kBN][idx % kBN] = rb[q];
+        }
+    };
+
+    fetch(0);
+    for (int k0 = 0; k0 < K; k0 += kBK) {
+        stash();
         __syncthreads();
+        if (k0 + kBK < K)
+            fetch(k0 + kBK);
 #pragma unroll
         for (int kk = 0; kk < kBK; ++kk) {
             const float2 a = As[kk][wm * 32 + r];
@@ -528,22 +565,34 @@ static int launch_cmul(int op, const float2* a, const float2* b, float2* c, int 
     } else {
         M = fo; N = f; K = S; sAp = (int64_t)S * fo; sBp = (int64_t)S * f; lda = fo; ldb = f;
     }
-    dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM), (unsigned)nbins);
+    const int tiles_n = (N + kBN - 1) / kBN, tiles_m = (M + kBM - 1) / kBM;
 #if FFTCONV_MFMA
-#define FFTCONV_GEMM cgemm_mfma_kernel
-#else
-#define FFTCONV_GEMM cgemm_kernel
-#endif
+    const int tiles = tiles_n * tiles_m;
+    const int64_t blocks = (int64_t)((nbins + 7) / 8) * 8 * tiles;
+    if (blocks > 0x7FFFFFFF)
+        return MESWISH_EINVAL;
+    dim3 grid((unsigned)blocks);
     if (op == 0)
-        hipLaunchKernelGGL((FFTCONV_GEMM<true, true, false, true>), grid, dim3(kThreads), 0, s, a, b,
+        hipLaunchKernelGGL((cgemm_mfma_kernel<true, true, false, true>), grid, dim3(kThreads), 0, s,
+                           a, b, c, M, N, K, sAp, sBp, lda, ldb, tiles_n, tiles, nbins);
+    else if (op == 1)
+        hipLaunchKernelGGL((cgemm_mfma_kernel<true, false, false, false>), grid, dim3(kThreads), 0,
+                           s, a, b, c, M, N, K, sAp, sBp, lda, ldb, tiles_n, tiles, nbins);
+    else
+        hipLaunchKernelGGL((cgemm_mfma_kernel<false, false, true, false>), grid, dim3(kThreads), 0,
+                           s, a, b, c, M, N, K, sAp, sBp, lda, ldb, tiles_n, tiles, nbins);
+#else
+    dim3 grid((unsigned)tiles_n, (unsigned)tiles_m, (unsigned)nbins);
+    if (op == 0)
+        hipLaunchKernelGGL((cgemm_kernel<true, true, false, true>), grid, dim3(kThreads), 0, s, a, b,
                            c, M, N, K, sAp, sBp, lda, ldb);
     else if (op == 1)
-        hipLaunchKernelGGL((FFTCONV_GEMM<true, false, false, false>), grid, dim3(kThreads), 0, s, a,
+        hipLaunchKernelGGL((cgemm_kernel<true, false, false, false>), grid, dim3(kThreads), 0, s, a,
                            b, c, M, N, K, sAp, sBp, lda, ldb);
     else
-        hipLaunchKernelGGL((FFTCONV_GEMM<false, false, true, false>), grid, dim3(kThreads), 0, s, a,
+        hipLaunchKernelGGL((cgemm_kernel<false, false, true, false>), grid, dim3(kThreads), 0, s, a,
                            b, c, M, N, K, sAp, sBp, lda, ldb);
-#undef FFTCONV_GEMM
+#endif
     return status_of(hipGetLastError());
 }
 

@@ -6,6 +6,8 @@ Usage (after the rocprofv3 runs listed in each summary's header):
     python -m memory_efficient_activation_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR
     python -m memory_efficient_activation_amd.rocprof_summary dense-trace DIR f32|bf16
     python -m memory_efficient_activation_amd.rocprof_summary dense-traffic FETCH_DIR WRITE_DIR f32|bf16
+    python -m memory_efficient_activation_amd.rocprof_summary fft-trace DIR
+    python -m memory_efficient_activation_amd.rocprof_summary fft-traffic FETCH_DIR WRITE_DIR
 
 ``trace``   reads ``*_kernel_stats.csv`` and ``*_kernel_trace.csv`` from a
             ``--kernel-trace --stats --output-format csv`` run and prints the
@@ -22,6 +24,10 @@ Usage (after the rocprofv3 runs listed in each summary's header):
             layer 16: 204 channels of 64 x 32 x 32; its newest source has 12):
             forward 2 C M b bytes per launch, backward reduction 2 C M b,
             backward apply 3 C M b, statistics 12 M b, copy 2 C M b.
+``fft-*``   the same for ``bench.py --fft`` (S=128, f=96, f'=256, n=32, k=7):
+            each launch is attributed to its stage by kernel and grid size;
+            transforms count their real maps and half spectra (8 bytes per
+            bin), products their three spectrum arrays and 8 M N K P flops.
 """
 
 from __future__ import annotations
@@ -228,6 +234,108 @@ def dense_traffic(fetch_dir: str, write_dir: str, dtype: str) -> str:
     return "\n".join(out)
 
 
+FFT = {"S": 128, "f": 96, "fo": 256, "n": 32, "k": 7}
+FFT_SOURCES = [os.path.join(HERE, "csrc", "fft_conv.hip")]
+
+
+def fft_stages():
+    """(kernel key, maps) -> (stage, algorithmic bytes, flops) for the bench layer."""
+    S, f, fo, n, k = FFT["S"], FFT["f"], FFT["fo"], FFT["n"], FFT["k"]
+    m, P = n - k + 1, n * (n // 2 + 1)
+    st = {}
+    for name, B, mm in (("r2c x", S * f, n), ("r2c w", fo * f, k), ("r2c g", S * fo, m)):
+        st[("r2c", B)] = (name, B * mm * mm * 4 + B * P * 8, 0)
+    for name, B, mm in (("c2r y (forward)", S * fo, m), ("c2r gx (input gradient)", S * f, n),
+                        ("c2r gw (weight gradient)", fo * f, k)):
+        st[("c2r", B)] = (name, B * P * 8 + B * mm * mm * 4, 0)
+    flops = 8 * S * f * fo * P
+    st[("cmul", 0)] = ("products, forward", P * 8 * (S * f + fo * f + S * fo), flops)
+    st[("cmul", 1)] = ("products, input gradient", P * 8 * (S * fo + fo * f + S * f), flops)
+    st[("cmul", 2)] = ("products, weight gradient", P * 8 * (S * fo + S * f + fo * f), flops)
+    return st
+
+
+def fft_key(r: dict):
+    name = r["Kernel_Name"]
+    if "copy16_kernel" in name:
+        return ("copy", 0)
+    maps_per_block = {8: 64, 16: 32, 32: 16, 64: 8}
+    for kind in ("r2c", "c2r"):
+        mm = re.search(kind + r"_kernel<(\d+)>", name)
+        if mm:
+            # Kernel traces give Grid_Size_X / Workgroup_Size_X, counter
+            # collections Grid_Size / Workgroup_Size (1-D grids here).
+            grid = int(r.get("Grid_Size_X") or r["Grid_Size"])
+            blocks = grid // int(r.get("Workgroup_Size_X") or r["Workgroup_Size"])
+            B = blocks * maps_per_block[int(mm.group(1))]
+            # The last block may be partial: match the stage whose map count rounds up to B.
+            for key in fft_stages():
+                if key[0] == kind and -(-key[1] // maps_per_block[int(mm.group(1))]) == blocks:
+                    return key
+            return (kind, B)
+    mm = re.search(r"cgemm(?:_mfma)?_kernel<(true|false), (true|false), (true|false), (true|false)>", name)
+    if mm:
+        flags = tuple(x == "true" for x in mm.groups())
+        return ("cmul", {(True, True, False, True): 0, (True, False, False, False): 1,
+                         (False, False, True, False): 2}.get(flags, -1))
+    return ("other", 0)
+
+
+def fft_trace(d: str) -> str:
+    st = fft_stages()
+    stats = list(csv.DictReader(open(_one(os.path.join(d, "*_kernel_stats.csv")))))
+    rows = list(csv.DictReader(open(_one(os.path.join(d, "*_kernel_trace.csv")))))
+    out = ["| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+    for r in stats:
+        out.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    acc: dict = {}
+    for r in rows:
+        key = fft_key(r)
+        if key in st:
+            acc.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out += ["", "| stage | launches | mean (us) | algorithmic bytes | GB/s | TFLOP/s |",
+            "|---|---|---|---|---|---|"]
+    for key, (name, nb, fl) in st.items():
+        if key in acc:
+            t = statistics.fmean(acc[key])
+            tf = f"{fl / t / 1e3:.1f}" if fl else "-"
+            out.append(f"| {name} | {len(acc[key])} | {t / 1e3:.2f} | {nb} | {nb / t:.0f} | {tf} |")
+    return "\n".join(out)
+
+
+def fft_traffic(fetch_dir: str, write_dir: str) -> str:
+    st = fft_stages()
+
+    def counter(d, cname):
+        rows = list(csv.DictReader(open(_one(os.path.join(d, "*_counter_collection.csv")))))
+        acc: dict = {}
+        for r in rows:
+            if r["Counter_Name"] == cname:
+                acc.setdefault(fft_key(r), []).append(float(r["Counter_Value"]))
+        return {k: statistics.fmean(v) for k, v in acc.items()}
+
+    f, w = counter(fetch_dir, "FETCH_SIZE"), counter(write_dir, "WRITE_SIZE")
+    cbytes = FFT["S"] * FFT["f"] * FFT["n"] ** 2 * 4
+    cf, cw = cbytes / 1024 / f[("copy", 0)], cbytes / 1024 / w[("copy", 0)]
+    h = hashlib.sha256()
+    for path in FFT_SOURCES:
+        h.update(open(path, "rb").read())
+    out = [f"calibration (copy kernel, {cbytes} B read and written per launch): "
+           f"FETCH_SIZE factor {cf:.5f}, WRITE_SIZE factor {cw:.5f}", "",
+           "| stage | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM bytes (calibrated) | "
+           "algorithmic bytes | ratio |", "|---|---|---|---|---|---|"]
+    per = {}
+    for key, (name, nb, _) in st.items():
+        if key in f and key in w:
+            b = (f[key] * cf + w[key] * cw) * 1024
+            per[key] = b
+            out.append(f"| {name} | {f[key]:.1f} | {w[key]:.1f} | {b:.0f} | {nb} | {b / nb:.5f} |")
+    out += ["", f"traffic_bytes_per_launch: {per.get(('cmul', 0), 0):.0f}",
+            f"kernel_source_sha256: {h.hexdigest()}"]
+    return "\n".join(out)
+
+
 def main(argv):
     if len(argv) >= 2 and argv[0] == "trace":
         print(trace(argv[1]))
@@ -237,6 +345,10 @@ def main(argv):
         print(dense_trace(argv[1], argv[2]))
     elif len(argv) >= 4 and argv[0] == "dense-traffic":
         print(dense_traffic(argv[1], argv[2], argv[3]))
+    elif len(argv) >= 2 and argv[0] == "fft-trace":
+        print(fft_trace(argv[1]))
+    elif len(argv) >= 3 and argv[0] == "fft-traffic":
+        print(fft_traffic(argv[1], argv[2]))
     else:
         raise SystemExit(__doc__)
 
