@@ -489,6 +489,29 @@ def measure_dense(args, lib, torch, dev):
 PEAK_FP32_MFMA_TFLOPS = 157.3
 
 
+FFT_SOURCES = [os.path.join(ROOT, "memory_efficient_activation_amd", "csrc", "fft_conv.hip")]
+
+
+def fft_traffic_from_profile():
+    """HBM bytes per launch of the forward's per-bin products, from the
+    committed rocprofv3 counter summary, if taken on the current source."""
+    path = os.path.join(ROOT, "profiles", "fft_conv_s128_f96_f256_n32_k7_traffic.md")
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    text = open(path).read()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_sha and m_b):
+        return None, "counter summary unreadable"
+    h = hashlib.sha256()
+    for f in FFT_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    if m_sha.group(1) != h.hexdigest():
+        return None, "kernel changed since counters were taken"
+    return float(m_b.group(1)), "rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated"
+
+
 def measure_fft(args, lib, torch, dev):
     """The FFT convolution layer: see the module docstring (``--fft``)."""
     from memory_efficient_activation_amd import _lib, fft, fft_inputs
@@ -585,6 +608,7 @@ def measure_fft(args, lib, torch, dev):
     _, cms = region(k_copy, K)
     copy_us = cms * 1e3 / K
     del csrc, cdst
+    fft_traffic = fft_traffic_from_profile()
     cm_flops = 8 * S * fo * f * P
     cm_us = stages["cmul"]["mean_us"]
     cm_tf = cm_flops / (cm_us * 1e-6) / 1e12
@@ -630,7 +654,8 @@ def measure_fft(args, lib, torch, dev):
         "roofline": {"kernel": "cgemm_mfma_kernel (per-bin complex products, forward)",
                      "bound": "mfma", "achieved": round(cm_tf, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(cm_tf / PEAK_FP32_MFMA_TFLOPS, 4),
-                     "traffic": None, "traffic_note": "no counter summary for this kernel",
+                     "traffic": fft_traffic[0], "traffic_note": fft_traffic[1],
+                     "bytes_per_launch": stages["cmul"]["bytes"],
                      "flops_per_launch": cm_flops, "mean_launch_us": cm_us},
         "copy_ceiling": {"bytes": 2 * cbytes, "mean_us": round(copy_us, 2),
                          "GBps": round(2 * cbytes / (copy_us * 1e-6) / 1e9, 1)},
