@@ -17,7 +17,7 @@
 //     registers (radix-2 Cooley-Tukey, fully unrolled: no data-dependent
 //     indexing, no scratch), first over rows, then -- through LDS -- over
 //     the n/2 + 1 columns of the half spectrum.  Twiddles e^{-2 pi i j/n}
-//     come from sincospi once per block into LDS.  Zero rows of padded maps
+//     are compile-time constants.  Zero rows of padded maps
 //     (kernels, output gradients) skip their row transform.
 //   * Spectra are stored bin-major (bin p, then map b), so the per-bin
 //     matrices of the contraction are contiguous and the column pass writes
@@ -65,12 +65,35 @@ constexpr int bitrev(int x, int bits)
     return r;
 }
 
-// In-place length-N DFT of a[] (N a power of two): forward with kernel
-// e^{-2 pi i jk/N}, inverse (INV) with e^{+2 pi i jk/N}, unscaled.
-// tw[j] = e^{-2 pi i j/N} for j < N/2 (LDS).  Iterative radix-2,
-// decimation in time: bit-reversed input order, then log2 N stages.
+// Twiddle factors e^{-2 pi i j / 64} = kCos64[j] - i kSin64[j], j < 32,
+// rounded to binary32 (gen_fft_twiddles.py); a length-n transform uses
+// entry j * 64 / n.  Indices are compile-time constants after unrolling, so
+// the factors become instruction operands: no loads, no registers held.
+constexpr float kCos64[32] = {
+    1.000000000e+00f, 9.951847196e-01f, 9.807852507e-01f, 9.569403529e-01f,
+    9.238795042e-01f, 8.819212914e-01f, 8.314695954e-01f, 7.730104327e-01f,
+    7.071067691e-01f, 6.343932748e-01f, 5.555702448e-01f, 4.713967443e-01f,
+    3.826834261e-01f, 2.902846634e-01f, 1.950903237e-01f, 9.801714122e-02f,
+    0.000000000e+00f, -9.801714122e-02f, -1.950903237e-01f, -2.902846634e-01f,
+    -3.826834261e-01f, -4.713967443e-01f, -5.555702448e-01f, -6.343932748e-01f,
+    -7.071067691e-01f, -7.730104327e-01f, -8.314695954e-01f, -8.819212914e-01f,
+    -9.238795042e-01f, -9.569403529e-01f, -9.807852507e-01f, -9.951847196e-01f};
+constexpr float kSin64[32] = {
+    0.000000000e+00f, 9.801714122e-02f, 1.950903237e-01f, 2.902846634e-01f,
+    3.826834261e-01f, 4.713967443e-01f, 5.555702448e-01f, 6.343932748e-01f,
+    7.071067691e-01f, 7.730104327e-01f, 8.314695954e-01f, 8.819212914e-01f,
+    9.238795042e-01f, 9.569403529e-01f, 9.807852507e-01f, 9.951847196e-01f,
+    1.000000000e+00f, 9.951847196e-01f, 9.807852507e-01f, 9.569403529e-01f,
+    9.238795042e-01f, 8.819212914e-01f, 8.314695954e-01f, 7.730104327e-01f,
+    7.071067691e-01f, 6.343932748e-01f, 5.555702448e-01f, 4.713967443e-01f,
+    3.826834261e-01f, 2.902846634e-01f, 1.950903237e-01f, 9.801714122e-02f};
+
+// In-place length-N DFT of a[] (N a power of two, N <= 64): forward with
+// kernel e^{-2 pi i jk/N}, inverse (INV) with e^{+2 pi i jk/N}, unscaled.
+// Iterative radix-2, decimation in time: bit-reversed input order, then
+// log2 N stages.
 template <int N, bool INV>
-__device__ __forceinline__ void fft_reg(float2 (&a)[N], const float2* tw)
+__device__ __forceinline__ void fft_reg(float2 (&a)[N])
 {
     constexpr int L = ilog2(N);
 #pragma unroll
@@ -93,9 +116,8 @@ __device__ __forceinline__ void fft_reg(float2 (&a)[N], const float2* tw)
                 const float2 u = a[i + j];
                 float2 v = a[i + j + half];
                 if (j != 0) {
-                    float2 w = tw[j * step];
-                    if (INV)
-                        w.y = -w.y;
+                    const int t = j * step * (64 / N);
+                    const float2 w = make_float2(kCos64[t], INV ? kSin64[t] : -kSin64[t]);
                     v = cmul(v, w);
                 }
                 a[i + j] = cadd(u, v);
@@ -105,21 +127,20 @@ __device__ __forceinline__ void fft_reg(float2 (&a)[N], const float2* tw)
     }
 }
 
-template <int N>
-__device__ __forceinline__ void load_twiddles(float2* tw)
-{
-    if ((int)threadIdx.x < N / 2) {
-        float s, c;
-        sincospif(2.0f * (float)threadIdx.x / (float)N, &s, &c);
-        tw[threadIdx.x] = make_float2(c, -s);
-    }
-}
-
 // Maps per block (a power of two: the T maps of one bin fill whole 128-byte
 // lines) and threads per block: one column transform per thread, and the
 // T N rows in two rounds.
+// Maps per block for n = 32 and 16: longer runs per bin (256 and 512 bytes)
+// measured faster than 128-byte runs (n = 32: transforms of the inputs and
+// kernels 25 -> 22 and 39 -> 29 us on the measured layer).
+#ifndef FFTCONV_MAPS_32
+#define FFTCONV_MAPS_32 32
+#endif
+#ifndef FFTCONV_MAPS_16
+#define FFTCONV_MAPS_16 64
+#endif
 template <int N> struct Tile {
-    static constexpr int T = N <= 8 ? 64 : N == 16 ? 32 : N == 32 ? 16 : 8;
+    static constexpr int T = N <= 8 ? 64 : N == 16 ? FFTCONV_MAPS_16 : N == 32 ? FFTCONV_MAPS_32 : 8;
     // n = 64 stays at 4 waves (its length-64 transforms need the register
     // file of a single wave per SIMD); its 264 column jobs take two rounds.
     static constexpr int kThreads = N == 64 ? 256 : T * (N / 2 + 1);
@@ -138,10 +159,7 @@ __global__ __launch_bounds__(Tile<N>::kThreads) void r2c_kernel(const float* __r
     constexpr int H = N / 2 + 1;
     constexpr int MS = N * H + 1;  // map stride in LDS, odd: no bank conflicts across maps
     __shared__ float2 buf[T * MS];
-    __shared__ float2 tw[N / 2];
     const int64_t b0 = (int64_t)blockIdx.x * T;
-    load_twiddles<N>(tw);
-    __syncthreads();
 
     // Rows: job = (map, r).
     constexpr int NT = Tile<N>::kThreads;
@@ -171,7 +189,7 @@ __global__ __launch_bounds__(Tile<N>::kThreads) void r2c_kernel(const float* __r
             for (int c = 0; c < N; ++c)
                 a[c] = make_float2(c < m ? row[c] : 0.0f, 0.0f);
         }
-        fft_reg<N, false>(a, tw);
+        fft_reg<N, false>(a);
 #pragma unroll
         for (int v = 0; v < H; ++v)
             out[v] = a[v];
@@ -186,7 +204,7 @@ __global__ __launch_bounds__(Tile<N>::kThreads) void r2c_kernel(const float* __r
 #pragma unroll
         for (int u = 0; u < N; ++u)
             a[u] = buf[map * MS + u * H + v];
-        fft_reg<N, false>(a, tw);
+        fft_reg<N, false>(a);
         if (b < batch) {
             // Bin (u, v) of map b: a per-thread base plus a block-uniform step.
             float2* col = spec + (int64_t)v * batch + b;
@@ -211,10 +229,7 @@ __global__ __launch_bounds__(Tile<N>::kThreads) void c2r_kernel(const float2* __
     constexpr int H = N / 2 + 1;
     constexpr int MS = N * H + 1;
     __shared__ float2 buf[T * MS];
-    __shared__ float2 tw[N / 2];
     const int64_t b0 = (int64_t)blockIdx.x * T;
-    load_twiddles<N>(tw);
-    __syncthreads();
 
     // Columns: inverse along u; keep rows p < m.
     constexpr int NT = Tile<N>::kThreads;
@@ -233,7 +248,7 @@ __global__ __launch_bounds__(Tile<N>::kThreads) void c2r_kernel(const float2* __
             for (int u = 0; u < N; ++u)
                 a[u] = make_float2(0.0f, 0.0f);
         }
-        fft_reg<N, true>(a, tw);
+        fft_reg<N, true>(a);
 #pragma unroll
         for (int p = 0; p < N; ++p)
             if (p < m)
@@ -255,7 +270,7 @@ __global__ __launch_bounds__(Tile<N>::kThreads) void c2r_kernel(const float2* __
 #pragma unroll
         for (int v = H; v < N; ++v)
             a[v] = conjf2(in[N - v]);
-        fft_reg<N, true>(a, tw);
+        fft_reg<N, true>(a);
         float* out = y + (b * m + p) * (int64_t)m;
         if ((m & 1) == 0 && ((uintptr_t)y & 7u) == 0) {
             // Even m: every row starts 8-byte aligned; store pairs.

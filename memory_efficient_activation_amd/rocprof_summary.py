@@ -259,7 +259,7 @@ def fft_key(r: dict):
     name = r["Kernel_Name"]
     if "copy16_kernel" in name:
         return ("copy", 0)
-    maps_per_block = {8: 64, 16: 32, 32: 16, 64: 8}
+    maps_per_block = {8: 64, 16: 64, 32: 32, 64: 8}
     for kind in ("r2c", "c2r"):
         mm = re.search(kind + r"_kernel<(\d+)>", name)
         if mm:
