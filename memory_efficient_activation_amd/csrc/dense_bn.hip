@@ -14,8 +14,8 @@
 //   * Every kernel streams feature maps once per pass at a few flops per
 //     element: HBM-bound, so no LDS tiling and no MFMA.  LDS holds only the
 //     per-wave partial sums of a block reduction.
-//   * Work unit = (channel, chunk): one block handles kChunk elements of one
-//     channel.  The channel's parameters (mean, 1/sqrt(var + eps), the ReLU
+//   * Work unit = (channel, chunk): one block handles 16 KiB of one channel
+//     (4096 binary32 or 8192 bfloat16 elements).  The channel's parameters (mean, 1/sqrt(var + eps), the ReLU
 //     threshold) are then uniform over the block and computed once per lane
 //     in binary64 -- after the block's loads are issued, so their latency
 //     hides the arithmetic.  A channel's n rows of hw elements sit at a

@@ -11,14 +11,13 @@
 // Design for MI355X (CDNA4):
 //   * Transforms.  The page's point is that a GPU FFT library parallelises
 //     within one large transform, while this workload is many small ones.
-//     Here one block transforms T maps of n x n at once (T (n/2 + 1)
-//     threads: one column transform per thread): every thread runs whole
-//     length-n transforms in
-//     registers (radix-2 Cooley-Tukey, fully unrolled: no data-dependent
-//     indexing, no scratch), first over rows, then -- through LDS -- over
-//     the n/2 + 1 columns of the half spectrum.  Twiddles e^{-2 pi i j/n}
-//     are compile-time constants.  Zero rows of padded maps
-//     (kernels, output gradients) skip their row transform.
+//     Here one block transforms T maps of n x n at once, with T (n/2 + 1)
+//     threads (one column transform each).  Every thread runs whole
+//     length-n transforms in registers (radix-2 Cooley-Tukey, fully
+//     unrolled: no data-dependent indexing, no scratch), first over rows,
+//     then -- through LDS -- over the n/2 + 1 columns of the half spectrum.
+//     Twiddles e^{-2 pi i j/n} are compile-time constants.  Zero rows of
+//     padded maps (kernels, output gradients) skip their row transform.
 //   * Spectra are stored bin-major (bin p, then map b), so the per-bin
 //     matrices of the contraction are contiguous and the column pass writes
 //     T consecutive maps of one bin together.
@@ -27,7 +26,9 @@
 //     the matrix cores (v_mfma_f32_32x32x2f32, binary32 in and out), the
 //     complex product expanded into a real one of twice the depth and
 //     width.  Tiles of 64 x 64 complex outputs, K in steps of 16 through
-//     LDS; a vector-ALU version of the same tiling is kept for comparison.
+//     LDS with the next step prefetched into registers; all tiles of one
+//     bin run on one XCD (shared operands stay in that XCD's L2).  A
+//     vector-ALU version of the same tiling is kept for comparison.
 //   * Inverse.  Column transforms first, keeping only the rows that survive
 //     the crop, then row transforms of the Hermitian half rows; only the
 //     kept m x m corner is written, scaled by 1/n^2.
