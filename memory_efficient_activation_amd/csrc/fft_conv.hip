@@ -508,13 +508,131 @@ __global__ __launch_bounds__(kThreads) void cgemm_mfma_kernel(const float2* __re
     }
 }
 
+// The planar form of the same product: real and imaginary parts in separate
+// LDS planes, and one MFMA k-step takes two complex k.  Per pair of k:
+//   Re C += Re A Re B - Im A Im B,   Im C += Re A Im B + Im A Re B
+// as four v_mfma_f32_32x32x2f32 on accumulators acc_re, acc_im; no
+// per-lane selects, a third of the LDS bytes of the interleaved form.  Lane
+// l supplies A[row l%32][k l/32] and B[k l/32][col l%32] of the pair.  WN
+// column subtiles per wave: 1 is used; 2 (A reused across two subtiles)
+// measured slower on the measured layer (178 VGPRs, half the tiles per bin).
+template <bool AK, bool BK, bool CA, bool CB, int WN>
+__global__ __launch_bounds__(kThreads) void cgemm_planar_kernel(const float2* __restrict__ A,
+                                                                const float2* __restrict__ B,
+                                                                float2* __restrict__ C, int M,
+                                                                int N, int K, int64_t sAp,
+                                                                int64_t sBp, int lda, int ldb,
+                                                                int tiles_n, int tiles, int nbins)
+{
+    // Block tile: 64 rows x 64 WN complex columns; each wave 32 x 32 WN.
+    constexpr int BN = kBN * WN;
+    __shared__ float Ar[kBK][kBM + 4], Ai[kBK][kBM + 4];
+    __shared__ float Br[kBK][BN + 4], Bi[kBK][BN + 4];
+    const int xcd = (int)(blockIdx.x & 7u), q = (int)(blockIdx.x >> 3);
+    const int p = (q / tiles) * 8 + xcd;
+    if (p >= nbins)
+        return;
+    const int tile = q % tiles;
+    const int i0 = (tile / tiles_n) * kBM, j0 = (tile % tiles_n) * BN;
+    const float2* Ap = A + p * sAp;
+    const float2* Bp = B + p * sBp;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int r = lane & 31, h = lane >> 5;
+    f32x16 acc_re[WN], acc_im[WN];
+#pragma unroll
+    for (int c = 0; c < WN; ++c) {
+        acc_re[c] = f32x16{0};
+        acc_im[c] = f32x16{0};
+    }
+
+    // Global -> register staging of one K-tile; the next tile's loads are
+    // issued before the current tile's products.
+    float2 ra[4], rb[4 * WN];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            const int idx = threadIdx.x + qq * kThreads;
+            const int k = AK ? idx % kBK : idx / kBM, i = AK ? idx / kBK : idx % kBM;
+            float2 v = make_float2(0.0f, 0.0f);
+            if (i0 + i < M && k0 + k < K)
+                v = AK ? Ap[(int64_t)(i0 + i) * lda + (k0 + k)] : Ap[(int64_t)(k0 + k) * lda + (i0 + i)];
+            ra[qq] = CA ? conjf2(v) : v;
+        }
+#pragma unroll
+        for (int qq = 0; qq < 4 * WN; ++qq) {
+            const int idx = threadIdx.x + qq * kThreads;
+            const int k = BK ? idx % kBK : idx / BN, j = BK ? idx / kBK : idx % BN;
+            float2 w = make_float2(0.0f, 0.0f);
+            if (j0 + j < N && k0 + k < K)
+                w = BK ? Bp[(int64_t)(j0 + j) * ldb + (k0 + k)] : Bp[(int64_t)(k0 + k) * ldb + (j0 + j)];
+            rb[qq] = CB ? conjf2(w) : w;
+        }
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            const int idx = threadIdx.x + qq * kThreads;
+            const int k = AK ? idx % kBK : idx / kBM, i = AK ? idx / kBK : idx % kBM;
+            Ar[k][i] = ra[qq].x;
+            Ai[k][i] = ra[qq].y;
+        }
+#pragma unroll
+        for (int qq = 0; qq < 4 * WN; ++qq) {
+            const int idx = threadIdx.x + qq * kThreads;
+            const int k = BK ? idx % kBK : idx / BN, j = BK ? idx / kBK : idx % BN;
+            Br[k][j] = rb[qq].x;
+            Bi[k][j] = rb[qq].y;
+        }
+    };
+
+    fetch(0);
+    for (int k0 = 0; k0 < K; k0 += kBK) {
+        stash();
+        __syncthreads();
+        if (k0 + kBK < K)
+            fetch(k0 + kBK);
+#pragma unroll
+        for (int kk = 0; kk < kBK; kk += 2) {
+            const float are = Ar[kk + h][wm * 32 + r], aim = Ai[kk + h][wm * 32 + r];
+#pragma unroll
+            for (int c = 0; c < WN; ++c) {
+                const int col = wn * 32 * WN + c * 32 + r;
+                const float bre = Br[kk + h][col], bim = Bi[kk + h][col];
+                acc_re[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(are, bre, acc_re[c], 0, 0, 0);
+                acc_im[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(are, bim, acc_im[c], 0, 0, 0);
+            }
+#pragma unroll
+            for (int c = 0; c < WN; ++c) {
+                const int col = wn * 32 * WN + c * 32 + r;
+                const float bre = Br[kk + h][col], bim = Bi[kk + h][col];
+                acc_re[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(-aim, bim, acc_re[c], 0, 0, 0);
+                acc_im[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(aim, bre, acc_im[c], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+    }
+    float2* Cp = C + (int64_t)p * M * N;
+#pragma unroll
+    for (int c = 0; c < WN; ++c) {
+        const int j = j0 + wn * 32 * WN + c * 32 + r;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int i = i0 + wm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+            if (i < M && j < N)
+                Cp[(int64_t)i * N + j] = make_float2(acc_re[c][v], acc_im[c][v]);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
 
-// 1: per-bin products on the matrix cores; 0: on the vector ALUs.
+// Per-bin products: 2 = matrix cores, planar operands; 1 = matrix cores,
+// interleaved 2 x 2 blocks; 0 = vector ALUs.
 #ifndef FFTCONV_MFMA
-#define FFTCONV_MFMA 1
+#define FFTCONV_MFMA 2
 #endif
 
 static bool n_ok(int n) { return n == 8 || n == 16 || n == 32 || n == 64; }
@@ -588,6 +706,19 @@ static int launch_cmul(int op, const float2* a, const float2* b, float2* c, int 
     if (blocks > 0x7FFFFFFF)
         return MESWISH_EINVAL;
     dim3 grid((unsigned)blocks);
+#if FFTCONV_MFMA == 2
+    if (op == 0)
+        hipLaunchKernelGGL((cgemm_planar_kernel<true, true, false, true, 1>), grid, dim3(kThreads),
+                           0, s, a, b, c, M, N, K, sAp, sBp, lda, ldb, tiles_n, tiles, nbins);
+    else if (op == 1)
+        hipLaunchKernelGGL((cgemm_planar_kernel<true, false, false, false, 1>), grid,
+                           dim3(kThreads), 0, s, a, b, c, M, N, K, sAp, sBp, lda, ldb, tiles_n,
+                           tiles, nbins);
+    else
+        hipLaunchKernelGGL((cgemm_planar_kernel<false, false, true, false, 1>), grid,
+                           dim3(kThreads), 0, s, a, b, c, M, N, K, sAp, sBp, lda, ldb, tiles_n,
+                           tiles, nbins);
+#else
     if (op == 0)
         hipLaunchKernelGGL((cgemm_mfma_kernel<true, true, false, true>), grid, dim3(kThreads), 0, s,
                            a, b, c, M, N, K, sAp, sBp, lda, ldb, tiles_n, tiles, nbins);
@@ -597,6 +728,7 @@ static int launch_cmul(int op, const float2* a, const float2* b, float2* c, int 
     else
         hipLaunchKernelGGL((cgemm_mfma_kernel<false, false, true, false>), grid, dim3(kThreads), 0,
                            s, a, b, c, M, N, K, sAp, sBp, lda, ldb, tiles_n, tiles, nbins);
+#endif
 #else
     dim3 grid((unsigned)tiles_n, (unsigned)tiles_m, (unsigned)nbins);
     if (op == 0)
