@@ -113,14 +113,17 @@ __device__ __forceinline__ void st16(void* p, const uint4& v)
 
 template <> struct Elem<float> {
     static constexpr int kVec = 4;  // elements per 16-byte vector
-    template <bool kNT>
-    __device__ static void load(const float* p, int64_t i, float (&f)[4])
+    __device__ static void unpack(const uint4& v, float (&f)[4])
     {
-        uint4 v = ld16<kNT>(p + i);
         f[0] = __uint_as_float(v.x);
         f[1] = __uint_as_float(v.y);
         f[2] = __uint_as_float(v.z);
         f[3] = __uint_as_float(v.w);
+    }
+    template <bool kNT>
+    __device__ static void load(const float* p, int64_t i, float (&f)[4])
+    {
+        unpack(ld16<kNT>(p + i), f);
     }
     template <bool kNT>
     __device__ static void store(float* p, int64_t i, const float (&f)[4])
@@ -136,16 +139,19 @@ template <> struct Elem<float> {
 
 template <> struct Elem<bf16_t> {
     static constexpr int kVec = 8;
-    template <bool kNT>
-    __device__ static void load(const bf16_t* p, int64_t i, float (&f)[8])
+    __device__ static void unpack(const uint4& v, float (&f)[8])
     {
-        uint4 v = ld16<kNT>(p + i);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             f[2 * k] = __uint_as_float(w[k] << 16);
             f[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
         }
+    }
+    template <bool kNT>
+    __device__ static void load(const bf16_t* p, int64_t i, float (&f)[8])
+    {
+        unpack(ld16<kNT>(p + i), f);
     }
     template <bool kNT>
     __device__ static void store(bf16_t* p, int64_t i, const float (&f)[8])
@@ -163,6 +169,27 @@ template <> struct Elem<bf16_t> {
     {
         p[i].bits = (uint16_t)(pack_bf16x2(f[0], 0.0f) & 0xFFFFu);
     }
+};
+
+// One vector's registers as loaded: the 16 bytes as they arrive, unpacked to
+// binary32 only where used (bfloat16 doubles in size when unpacked, so this
+// keeps fewer registers live across the loads); the element-wise path keeps
+// its one element.
+template <typename IO, int V> struct Raw {
+    uint4 u;
+    template <bool kNT> __device__ void fetch(const IO* p, int64_t i) { u = ld16<kNT>(p + i); }
+    __device__ void unpack(float (&f)[V]) const { Elem<IO>::unpack(u, f); }
+};
+
+template <typename IO> struct Raw<IO, 1> {
+    float f0;
+    template <bool kNT> __device__ void fetch(const IO* p, int64_t i)
+    {
+        float f[1];
+        Elem<IO>::template load<kNT>(p, i, f);
+        f0 = f[0];
+    }
+    __device__ void unpack(float (&f)[1]) const { f[0] = f0; }
 };
 
 // ---------------------------------------------------------------------------
@@ -358,7 +385,7 @@ __global__ __launch_bounds__(kBlock) void stats_partial_kernel(const IO* __restr
     constexpr int kPer = kChunk / (kBlock * V);
     const int c = (int)blockIdx.x / geo.chunks;
     const int chunk = (int)blockIdx.x - c * geo.chunks;
-    float f[kPer][V];
+    Raw<IO, V> rx[kPer];
     bool ok[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -366,7 +393,7 @@ __global__ __launch_bounds__(kBlock) void stats_partial_kernel(const IO* __restr
                            threadIdx.x;
         ok[i] = v < geo.mv;
         if (ok[i])
-            Elem<IO>::template load<kNtX>(x, elem_offset(v, geo.pv, channels, c, V), f[i]);
+            rx[i].template fetch<kNtX>(x, elem_offset(v, geo.pv, channels, c, V));
     }
     float pivot[1];
     Elem<IO>::template load<false>(x, (int64_t)c * geo.pv.d * V, pivot);
@@ -376,9 +403,11 @@ __global__ __launch_bounds__(kBlock) void stats_partial_kernel(const IO* __restr
     for (int i = 0; i < kPer; ++i) {
         if (!ok[i])
             continue;
+        float f[V];
+        rx[i].unpack(f);
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-            const double d = (double)f[i][e] - k;
+            const double d = (double)f[e] - k;
             s1 += d;
             s2 = fma(d, d, s2);
         }
@@ -427,7 +456,7 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(Table t, Geom geo, int z_ch
     const Where w = locate(t, geo.chunks);
     const IO* x = static_cast<const IO*>(t.x[w.j]);
     const int cj = t.channels[w.j];
-    float f[kPer][V];
+    Raw<IO, V> rx[kPer];
     uint32_t vv[kPer];
     bool ok[kPer];
 #pragma unroll
@@ -435,18 +464,19 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(Table t, Geom geo, int z_ch
         vv[i] = (uint32_t)w.chunk * (uint32_t)(kChunk / V) + (uint32_t)(i * kBlock) + threadIdx.x;
         ok[i] = vv[i] < geo.mv;
         if (ok[i])
-            Elem<IO>::template load<kNtX>(x, elem_offset(vv[i], geo.pv, cj, w.cl, V), f[i]);
+            rx[i].template fetch<kNtX>(x, elem_offset(vv[i], geo.pv, cj, w.cl, V));
     }
     const Chan ch = chan_params(t.stats[w.j], w.cl, gamma[w.zc], beta[w.zc], eps);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         if (!ok[i])
             continue;
-        float y[V];
+        float f[V], y[V];
+        rx[i].unpack(f);
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-            const float h = fmaf(f[i][e] - ch.mu, ch.a, ch.beta);
-            y[e] = passes(f[i][e], ch) ? fmaxf(h, 0.0f) : 0.0f;
+            const float h = fmaf(f[e] - ch.mu, ch.a, ch.beta);
+            y[e] = passes(f[e], ch) ? fmaxf(h, 0.0f) : 0.0f;
         }
         Elem<IO>::template store<kNtOut>(z, elem_offset(vv[i], geo.pv, z_channels, w.zc, V), y);
     }
@@ -464,7 +494,7 @@ __global__ __launch_bounds__(kBlock) void bwd_reduce_kernel(Table t, Geom geo, i
     const Where w = locate(t, geo.chunks);
     const IO* x = static_cast<const IO*>(t.x[w.j]);
     const int cj = t.channels[w.j];
-    float f[kPer][V], d[kPer][V];
+    Raw<IO, V> rx[kPer], rd[kPer];
     bool ok[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -472,8 +502,8 @@ __global__ __launch_bounds__(kBlock) void bwd_reduce_kernel(Table t, Geom geo, i
             (uint32_t)w.chunk * (uint32_t)(kChunk / V) + (uint32_t)(i * kBlock) + threadIdx.x;
         ok[i] = v < geo.mv;
         if (ok[i]) {
-            Elem<IO>::template load<kNtX>(x, elem_offset(v, geo.pv, cj, w.cl, V), f[i]);
-            Elem<IO>::template load<kNtDz>(dz, elem_offset(v, geo.pv, z_channels, w.zc, V), d[i]);
+            rx[i].template fetch<kNtX>(x, elem_offset(v, geo.pv, cj, w.cl, V));
+            rd[i].template fetch<kNtDz>(dz, elem_offset(v, geo.pv, z_channels, w.zc, V));
         }
     }
     const Chan ch = chan_params(t.stats[w.j], w.cl, gamma[w.zc], beta[w.zc], eps);
@@ -482,10 +512,13 @@ __global__ __launch_bounds__(kBlock) void bwd_reduce_kernel(Table t, Geom geo, i
     for (int i = 0; i < kPer; ++i) {
         if (!ok[i])
             continue;
+        float f[V], d[V];
+        rx[i].unpack(f);
+        rd[i].unpack(d);
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-            const float g = passes(f[i][e], ch) ? d[i][e] : 0.0f;
-            const float xh = (f[i][e] - ch.mu) * ch.r;
+            const float g = passes(f[e], ch) ? d[e] : 0.0f;
+            const float xh = (f[e] - ch.mu) * ch.r;
             sg += (double)g;
             sgx = fma((double)g, (double)xh, sgx);
         }
@@ -512,7 +545,7 @@ __global__ __launch_bounds__(kBlock) void bwd_apply_kernel(Table t, Geom geo, in
     const IO* x = static_cast<const IO*>(t.x[w.j]);
     IO* dx = static_cast<IO*>(t.dx[w.j]);
     const int cj = t.channels[w.j];
-    float f[kPer][V], d[kPer][V];
+    Raw<IO, V> rx[kPer], rd[kPer];
     int64_t off[kPer];
     bool ok[kPer];
 #pragma unroll
@@ -522,8 +555,8 @@ __global__ __launch_bounds__(kBlock) void bwd_apply_kernel(Table t, Geom geo, in
         ok[i] = v < geo.mv;
         if (ok[i]) {
             off[i] = elem_offset(v, geo.pv, cj, w.cl, V);
-            Elem<IO>::template load<kNtX>(x, off[i], f[i]);
-            Elem<IO>::template load<kNtDz>(dz, elem_offset(v, geo.pv, z_channels, w.zc, V), d[i]);
+            rx[i].template fetch<kNtX>(x, off[i]);
+            rd[i].template fetch<kNtDz>(dz, elem_offset(v, geo.pv, z_channels, w.zc, V));
         }
     }
     // This channel's sums over all its blocks' partials.
@@ -545,11 +578,13 @@ __global__ __launch_bounds__(kBlock) void bwd_apply_kernel(Table t, Geom geo, in
     for (int i = 0; i < kPer; ++i) {
         if (!ok[i])
             continue;
-        float out[V];
+        float f[V], d[V], out[V];
+        rx[i].unpack(f);
+        rd[i].unpack(d);
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-            const float g = passes(f[i][e], ch) ? d[i][e] : 0.0f;
-            const float xh = (f[i][e] - ch.mu) * ch.r;
+            const float g = passes(f[e], ch) ? d[e] : 0.0f;
+            const float xh = (f[e] - ch.mu) * ch.r;
             out[e] = ch.a * (g - fmaf(xh, k2, k1));
         }
         Elem<IO>::template store<kNtOut>(dx, off[i], out);
