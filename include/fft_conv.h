@@ -31,7 +31,8 @@
  * allocation or synchronisation, asynchronous on `stream` (a hipStream_t,
  * NULL = default stream), status codes from meswish_status, nothing
  * launched on an error.  Outputs must not overlap inputs or the frequency
- * buffer.  n must be 8, 16, 32 or 64; 1 <= k <= n; S, f, f' >= 1 with
+ * buffer.  Alignment (else MESWISH_EINVAL): real-map inputs 16 bytes, real
+ * outputs 4 bytes, spectra and the frequency buffer 8 bytes.  n must be 8, 16, 32 or 64; 1 <= k <= n; S, f, f' >= 1 with
  * every map count below 2^31 and every spectrum array below 2^31
  * complex values.  Arithmetic is binary32.
  */

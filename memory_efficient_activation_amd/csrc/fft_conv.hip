@@ -140,12 +140,47 @@ __device__ __forceinline__ void fft_reg(float2 (&a)[N])
 #ifndef FFTCONV_MAPS_16
 #define FFTCONV_MAPS_16 64
 #endif
-template <int N> struct Tile {
-    static constexpr int T = N <= 8 ? 64 : N == 16 ? FFTCONV_MAPS_16 : N == 32 ? FFTCONV_MAPS_32 : 8;
+#ifndef FFTCONV_C2R_MAPS_32
+#define FFTCONV_C2R_MAPS_32 32
+#endif
+// Inverse transforms up to n = 32 can store their real maps through LDS as
+// whole 16-byte vectors over the block's contiguous range of maps, instead
+// of row by row from registers: 0 never, 1 for maps smaller than n x n (rows
+// that are not whole 16-byte multiples), 2 always.  (The same staging of the
+// forward transforms' loads measured slower on every map size.)
+#ifndef FFTCONV_STAGE_POLICY
+#define FFTCONV_STAGE_POLICY 1
+#endif
+
+static bool staged(int n, int m)
+{
+    return n <= 32 && (FFTCONV_STAGE_POLICY == 2 || (FFTCONV_STAGE_POLICY == 1 && m < n));
+}
+
+// Block-wide copy of `count` floats from LDS to global memory, in 16-byte
+// vectors where the global side is 16-byte aligned (the LDS side always
+// is), then the remainder element by element.
+template <int NT>
+__device__ __forceinline__ void global_from_lds(float* g, const float* lds, int count)
+{
+    int head = 0;
+    if (((uintptr_t)g & 15u) == 0) {
+        head = count & ~3;
+        for (int i = 4 * (int)threadIdx.x; i < head; i += 4 * NT)
+            *reinterpret_cast<float4*>(g + i) = *reinterpret_cast<const float4*>(lds + i);
+    }
+    for (int i = head + (int)threadIdx.x; i < count; i += NT)
+        g[i] = lds[i];
+}
+
+template <int N, bool kInverse = false> struct Tile {
+    static constexpr int T = N <= 8 ? 64 : N == 16 ? FFTCONV_MAPS_16
+                           : N == 32 ? (kInverse ? FFTCONV_C2R_MAPS_32 : FFTCONV_MAPS_32) : 8;
     // n = 64 stays at 4 waves (its length-64 transforms need the register
     // file of a single wave per SIMD); its 264 column jobs take two rounds.
     static constexpr int kThreads = N == 64 ? 256 : T * (N / 2 + 1);
 };
+template <int N> using InvTile = Tile<N, true>;
 
 // ---------------------------------------------------------------------------
 // Forward transforms: `batch` real m x m maps (row-major, contiguous),
@@ -159,7 +194,7 @@ __global__ __launch_bounds__(Tile<N>::kThreads) void r2c_kernel(const float* __r
     constexpr int T = Tile<N>::T;
     constexpr int H = N / 2 + 1;
     constexpr int MS = N * H + 1;  // map stride in LDS, odd: no bank conflicts across maps
-    __shared__ float2 buf[T * MS];
+    __shared__ __align__(16) float2 buf[T * MS];
     const int64_t b0 = (int64_t)blockIdx.x * T;
 
     // Rows: job = (map, r).
@@ -222,18 +257,19 @@ __global__ __launch_bounds__(Tile<N>::kThreads) void r2c_kernel(const float* __r
 // real N x N maps, times scale.
 // ---------------------------------------------------------------------------
 
-template <int N>
-__global__ __launch_bounds__(Tile<N>::kThreads) void c2r_kernel(const float2* __restrict__ spec, int batch,
-                                                       int m, float scale, float* __restrict__ y)
+template <int N, bool kStaged>
+__global__ __launch_bounds__(InvTile<N>::kThreads) void c2r_kernel(const float2* __restrict__ spec,
+                                                             int batch, int m, float scale,
+                                                             float* __restrict__ y)
 {
-    constexpr int T = Tile<N>::T;
+    constexpr int T = InvTile<N>::T;
     constexpr int H = N / 2 + 1;
     constexpr int MS = N * H + 1;
-    __shared__ float2 buf[T * MS];
+    __shared__ __align__(16) float2 buf[T * MS];
     const int64_t b0 = (int64_t)blockIdx.x * T;
 
     // Columns: inverse along u; keep rows p < m.
-    constexpr int NT = Tile<N>::kThreads;
+    constexpr int NT = InvTile<N>::kThreads;
     for (int job = threadIdx.x; job < T * H; job += NT) {
         const int map = job % T, v = job / T;
         const int64_t b = b0 + map;
@@ -258,33 +294,78 @@ __global__ __launch_bounds__(Tile<N>::kThreads) void c2r_kernel(const float2* __
     __syncthreads();
 
     // Rows p < m: the row is the half spectrum of a real signal.
-    for (int job = threadIdx.x; job < T * m; job += NT) {
-        const int map = job / m, p = job - map * m;
-        const int64_t b = b0 + map;
-        if (b >= batch)
-            continue;
-        const float2* in = buf + map * MS + p * H;
-        float2 a[N];
+    if constexpr (kStaged && N <= 32) {
+        // The block's outputs (maps b0 .. b0 + T - 1, m x m each) are one
+        // contiguous range of y: keep each row in registers, rebuild the
+        // range in LDS once every row has been read, and store it with
+        // whole 16-byte vectors.
+        constexpr int R = (N + H - 1) / H;  // rows per thread: T m <= T N jobs over T H threads
+        float keep[R][N];
 #pragma unroll
-        for (int v = 0; v < H; ++v)
-            a[v] = in[v];
+        for (int r = 0; r < R; ++r) {
+            const int job = (int)threadIdx.x + r * NT;
+            const int map = job / m;
+            if (job >= T * m || b0 + map >= batch)
+                continue;
+            const float2* in = buf + map * MS + (job - map * m) * H;
+            float2 a[N];
 #pragma unroll
-        for (int v = H; v < N; ++v)
-            a[v] = conjf2(in[N - v]);
-        fft_reg<N, true>(a);
-        float* out = y + (b * m + p) * (int64_t)m;
-        if ((m & 1) == 0 && ((uintptr_t)y & 7u) == 0) {
-            // Even m: every row starts 8-byte aligned; store pairs.
+            for (int v = 0; v < H; ++v)
+                a[v] = in[v];
 #pragma unroll
-            for (int q = 0; q < N; q += 2)
-                if (q < m)
-                    *reinterpret_cast<float2*>(out + q) =
-                        make_float2(a[q].x * scale, a[q + 1].x * scale);
-        } else {
+            for (int v = H; v < N; ++v)
+                a[v] = conjf2(in[N - v]);
+            fft_reg<N, true>(a);
+#pragma unroll
+            for (int q = 0; q < N; ++q)
+                keep[r][q] = a[q].x * scale;
+        }
+        __syncthreads();
+        float* stage = reinterpret_cast<float*>(buf);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int job = (int)threadIdx.x + r * NT;
+            const int map = job / m;
+            if (job >= T * m || b0 + map >= batch)
+                continue;
+            float* row = stage + job * m;  // = map m^2 + p m
 #pragma unroll
             for (int q = 0; q < N; ++q)
                 if (q < m)
-                    out[q] = a[q].x * scale;
+                    row[q] = keep[r][q];
+        }
+        __syncthreads();
+        const int maps = (int)min<int64_t>(T, batch - b0);
+        global_from_lds<NT>(y + b0 * m * m, stage, maps * m * m);
+    } else {
+        for (int job = threadIdx.x; job < T * m; job += NT) {
+            const int map = job / m, p = job - map * m;
+            const int64_t b = b0 + map;
+            if (b >= batch)
+                continue;
+            const float2* in = buf + map * MS + p * H;
+            float2 a[N];
+#pragma unroll
+            for (int v = 0; v < H; ++v)
+                a[v] = in[v];
+#pragma unroll
+            for (int v = H; v < N; ++v)
+                a[v] = conjf2(in[N - v]);
+            fft_reg<N, true>(a);
+            float* out = y + (b * m + p) * (int64_t)m;
+            if ((m & 1) == 0 && ((uintptr_t)y & 7u) == 0) {
+                // Even m: every row starts 8-byte aligned; store pairs.
+#pragma unroll
+                for (int q = 0; q < N; q += 2)
+                    if (q < m)
+                        *reinterpret_cast<float2*>(out + q) =
+                            make_float2(a[q].x * scale, a[q + 1].x * scale);
+            } else {
+#pragma unroll
+                for (int q = 0; q < N; ++q)
+                    if (q < m)
+                        out[q] = a[q].x * scale;
+            }
         }
     }
 }
@@ -657,9 +738,14 @@ static void r2c_launch(const float* x, int batch, int m, float2* spec, hipStream
 template <int N>
 static void c2r_launch(const float2* spec, int batch, int m, float scale, float* y, hipStream_t s)
 {
-    const unsigned grid = (unsigned)((batch + Tile<N>::T - 1) / Tile<N>::T);
-    hipLaunchKernelGGL(c2r_kernel<N>, dim3(grid), dim3(Tile<N>::kThreads), 0, s, spec, batch, m,
-                       scale, y);
+    using Tl = InvTile<N>;
+    const unsigned grid = (unsigned)((batch + Tl::T - 1) / Tl::T);
+    if (staged(N, m))
+        hipLaunchKernelGGL((c2r_kernel<N, N <= 32>), dim3(grid), dim3(Tl::kThreads), 0, s, spec,
+                           batch, m, scale, y);
+    else
+        hipLaunchKernelGGL((c2r_kernel<N, false>), dim3(grid), dim3(Tl::kThreads), 0, s, spec,
+                           batch, m, scale, y);
 }
 
 static int launch_r2c(const float* x, int batch, int m, int n, float2* spec, hipStream_t s)

@@ -71,6 +71,29 @@ def test_c2r_matches_the_inverse(n):
         assert r <= RTOL
 
 
+@pytest.mark.parametrize("n,m", [(8, 7), (16, 9), (32, 26), (32, 7), (32, 32)])
+def test_inverse_into_an_unaligned_output(n, m, oracle):
+    """Outputs need only 4-byte alignment: an inverse written one float past
+    a 16-byte boundary takes the element-wise store path and gives the same
+    values (the round trip through both transforms), writing nothing outside
+    its range.  Inputs must be 16-byte aligned and are rejected otherwise."""
+    B = 2 * (512 // n) + 3
+    x = np.random.default_rng(7 * n + m).standard_normal((B, m, m)).astype(np.float32)
+    spec = fft.r2c(_dev(x), n)
+    lib = fft._lib.library()
+    out = torch.full((B * m * m + 2,), 7.0, dtype=torch.float32, device="cuda")
+    fft._lib.check(lib.fftconv_c2r(spec.data_ptr(), B, n, m, 1.0 / (n * n), out.data_ptr() + 4, None),
+                   "fftconv_c2r")
+    torch.cuda.synchronize()
+    o = _host(out)
+    r = float(np.abs(o[1:-1].reshape(B, m, m) - x).max() / np.abs(x).max())
+    say(f"[fft] c2r into an output 4 bytes past alignment, n={n} m={m} B={B}: round trip {r:.2e}")
+    assert r <= RTOL
+    assert o[0] == 7.0 and o[-1] == 7.0
+    xs = torch.zeros(B * m * m + 1, dtype=torch.float32, device="cuda")
+    assert lib.fftconv_r2c(xs.data_ptr() + 4, B, m, n, spec.data_ptr(), None) == fft._lib.EINVAL
+
+
 @pytest.mark.parametrize("op", [0, 1, 2])
 @pytest.mark.parametrize("S,f,fo,P", [(3, 5, 7, 9), (70, 33, 65, 5), (128, 96, 130, 3)])
 def test_cmul_matches_the_per_bin_products(op, S, f, fo, P):
