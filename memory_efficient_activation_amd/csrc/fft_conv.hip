@@ -594,19 +594,23 @@ __global__ __launch_bounds__(kThreads) void cgemm_mfma_kernel(const float2* __re
 //   Re C += Re A Re B - Im A Im B,   Im C += Re A Im B + Im A Re B
 // as four v_mfma_f32_32x32x2f32 on accumulators acc_re, acc_im; no
 // per-lane selects, a third of the LDS bytes of the interleaved form.  Lane
-// l supplies A[row l%32][k l/32] and B[k l/32][col l%32] of the pair.  WN
-// column subtiles per wave: 1 is used; 2 (A reused across two subtiles)
-// measured slower on the measured layer (178 VGPRs, half the tiles per bin).
-template <bool AK, bool BK, bool CA, bool CB, int WN>
-__global__ __launch_bounds__(kThreads) void cgemm_planar_kernel(const float2* __restrict__ A,
-                                                                const float2* __restrict__ B,
-                                                                float2* __restrict__ C, int M,
-                                                                int N, int K, int64_t sAp,
-                                                                int64_t sBp, int lda, int ldb,
-                                                                int tiles_n, int tiles, int nbins)
+// l supplies A[row l%32][k l/32] and B[k l/32][col l%32] of the pair.
+// Block tile: 64 rows x 32 WC columns, 2 WC waves of 32 x 32 each.  WC = 2
+// in general; WC = 1 where 64-column tiles would pad the product (96
+// columns take 3 tiles of 32 instead of 2 of 64, a quarter of them empty).
+// (Two column subtiles per wave, reusing A, measured slower: 178 VGPRs.)
+template <bool AK, bool BK, bool CA, bool CB, int WC>
+__global__ __launch_bounds__(128 * WC) void cgemm_planar_kernel(const float2* __restrict__ A,
+                                                               const float2* __restrict__ B,
+                                                               float2* __restrict__ C, int M,
+                                                               int N, int K, int64_t sAp,
+                                                               int64_t sBp, int lda, int ldb,
+                                                               int tiles_n, int tiles, int nbins)
 {
-    // Block tile: 64 rows x 64 WN complex columns; each wave 32 x 32 WN.
-    constexpr int BN = kBN * WN;
+    constexpr int NT = 128 * WC;        // threads
+    constexpr int BN = 32 * WC;         // block tile columns
+    constexpr int LA = kBM * kBK / NT;  // A values per thread per K-tile
+    constexpr int LB = BN * kBK / NT;   // B values per thread per K-tile (4)
     __shared__ float Ar[kBK][kBM + 4], Ai[kBK][kBM + 4];
     __shared__ float Br[kBK][BN + 4], Bi[kBK][BN + 4];
     const int xcd = (int)(blockIdx.x & 7u), q = (int)(blockIdx.x >> 3);
@@ -618,22 +622,17 @@ __global__ __launch_bounds__(kThreads) void cgemm_planar_kernel(const float2* __
     const float2* Ap = A + p * sAp;
     const float2* Bp = B + p * sBp;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WC, wn = wave % WC;
     const int r = lane & 31, h = lane >> 5;
-    f32x16 acc_re[WN], acc_im[WN];
-#pragma unroll
-    for (int c = 0; c < WN; ++c) {
-        acc_re[c] = f32x16{0};
-        acc_im[c] = f32x16{0};
-    }
+    f32x16 acc_re = f32x16{0}, acc_im = f32x16{0};
 
     // Global -> register staging of one K-tile; the next tile's loads are
     // issued before the current tile's products.
-    float2 ra[4], rb[4 * WN];
+    float2 ra[LA], rb[LB];
     auto fetch = [&](int k0) {
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-            const int idx = threadIdx.x + qq * kThreads;
+        for (int qq = 0; qq < LA; ++qq) {
+            const int idx = threadIdx.x + qq * NT;
             const int k = AK ? idx % kBK : idx / kBM, i = AK ? idx / kBK : idx % kBM;
             float2 v = make_float2(0.0f, 0.0f);
             if (i0 + i < M && k0 + k < K)
@@ -641,8 +640,8 @@ __global__ __launch_bounds__(kThreads) void cgemm_planar_kernel(const float2* __
             ra[qq] = CA ? conjf2(v) : v;
         }
 #pragma unroll
-        for (int qq = 0; qq < 4 * WN; ++qq) {
-            const int idx = threadIdx.x + qq * kThreads;
+        for (int qq = 0; qq < LB; ++qq) {
+            const int idx = threadIdx.x + qq * NT;
             const int k = BK ? idx % kBK : idx / BN, j = BK ? idx / kBK : idx % BN;
             float2 w = make_float2(0.0f, 0.0f);
             if (j0 + j < N && k0 + k < K)
@@ -652,15 +651,15 @@ __global__ __launch_bounds__(kThreads) void cgemm_planar_kernel(const float2* __
     };
     auto stash = [&]() {
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-            const int idx = threadIdx.x + qq * kThreads;
+        for (int qq = 0; qq < LA; ++qq) {
+            const int idx = threadIdx.x + qq * NT;
             const int k = AK ? idx % kBK : idx / kBM, i = AK ? idx / kBK : idx % kBM;
             Ar[k][i] = ra[qq].x;
             Ai[k][i] = ra[qq].y;
         }
 #pragma unroll
-        for (int qq = 0; qq < 4 * WN; ++qq) {
-            const int idx = threadIdx.x + qq * kThreads;
+        for (int qq = 0; qq < LB; ++qq) {
+            const int idx = threadIdx.x + qq * NT;
             const int k = BK ? idx % kBK : idx / BN, j = BK ? idx / kBK : idx % BN;
             Br[k][j] = rb[qq].x;
             Bi[k][j] = rb[qq].y;
@@ -676,33 +675,21 @@ __global__ __launch_bounds__(kThreads) void cgemm_planar_kernel(const float2* __
 #pragma unroll
         for (int kk = 0; kk < kBK; kk += 2) {
             const float are = Ar[kk + h][wm * 32 + r], aim = Ai[kk + h][wm * 32 + r];
-#pragma unroll
-            for (int c = 0; c < WN; ++c) {
-                const int col = wn * 32 * WN + c * 32 + r;
-                const float bre = Br[kk + h][col], bim = Bi[kk + h][col];
-                acc_re[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(are, bre, acc_re[c], 0, 0, 0);
-                acc_im[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(are, bim, acc_im[c], 0, 0, 0);
-            }
-#pragma unroll
-            for (int c = 0; c < WN; ++c) {
-                const int col = wn * 32 * WN + c * 32 + r;
-                const float bre = Br[kk + h][col], bim = Bi[kk + h][col];
-                acc_re[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(-aim, bim, acc_re[c], 0, 0, 0);
-                acc_im[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(aim, bre, acc_im[c], 0, 0, 0);
-            }
+            const float bre = Br[kk + h][wn * 32 + r], bim = Bi[kk + h][wn * 32 + r];
+            acc_re = __builtin_amdgcn_mfma_f32_32x32x2f32(are, bre, acc_re, 0, 0, 0);
+            acc_im = __builtin_amdgcn_mfma_f32_32x32x2f32(are, bim, acc_im, 0, 0, 0);
+            acc_re = __builtin_amdgcn_mfma_f32_32x32x2f32(-aim, bim, acc_re, 0, 0, 0);
+            acc_im = __builtin_amdgcn_mfma_f32_32x32x2f32(aim, bre, acc_im, 0, 0, 0);
         }
         __syncthreads();
     }
     float2* Cp = C + (int64_t)p * M * N;
+    const int j = j0 + wn * 32 + r;
 #pragma unroll
-    for (int c = 0; c < WN; ++c) {
-        const int j = j0 + wn * 32 * WN + c * 32 + r;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int i = i0 + wm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-            if (i < M && j < N)
-                Cp[(int64_t)i * N + j] = make_float2(acc_re[c][v], acc_im[c][v]);
-        }
+    for (int v = 0; v < 16; ++v) {
+        const int i = i0 + wm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (i < M && j < N)
+            Cp[(int64_t)i * N + j] = make_float2(acc_re[v], acc_im[v]);
     }
 }
 
@@ -786,25 +773,40 @@ static int launch_cmul(int op, const float2* a, const float2* b, float2* c, int 
         M = fo; N = f; K = S; sAp = (int64_t)S * fo; sBp = (int64_t)S * f; lda = fo; ldb = f;
     }
     const int tiles_n = (N + kBN - 1) / kBN, tiles_m = (M + kBM - 1) / kBM;
-#if FFTCONV_MFMA
+#if FFTCONV_MFMA == 2
+    // 32-column block tiles where they pad less than 64-column ones.
+#ifndef FFTCONV_PLANAR_WC
+    const int wc = ((N + 63) / 64 * 64 - N > (N + 31) / 32 * 32 - N) ? 1 : 2;
+#else
+    const int wc = FFTCONV_PLANAR_WC;
+#endif
+    const int ptn = (N + 32 * wc - 1) / (32 * wc), ptiles = ptn * tiles_m;
+    const int64_t pblocks = (int64_t)((nbins + 7) / 8) * 8 * ptiles;
+    if (pblocks > 0x7FFFFFFF)
+        return MESWISH_EINVAL;
+    const dim3 pgrid((unsigned)pblocks), pthreads(128 * wc);
+#define FFTCONV_PLANAR(AK, BK, CA, CB)                                                            \
+    do {                                                                                          \
+        if (wc == 1)                                                                              \
+            hipLaunchKernelGGL((cgemm_planar_kernel<AK, BK, CA, CB, 1>), pgrid, pthreads, 0, s, a, \
+                               b, c, M, N, K, sAp, sBp, lda, ldb, ptn, ptiles, nbins);            \
+        else                                                                                      \
+            hipLaunchKernelGGL((cgemm_planar_kernel<AK, BK, CA, CB, 2>), pgrid, pthreads, 0, s, a, \
+                               b, c, M, N, K, sAp, sBp, lda, ldb, ptn, ptiles, nbins);            \
+    } while (0)
+    if (op == 0)
+        FFTCONV_PLANAR(true, true, false, true);
+    else if (op == 1)
+        FFTCONV_PLANAR(true, false, false, false);
+    else
+        FFTCONV_PLANAR(false, false, true, false);
+#undef FFTCONV_PLANAR
+#elif FFTCONV_MFMA == 1
     const int tiles = tiles_n * tiles_m;
     const int64_t blocks = (int64_t)((nbins + 7) / 8) * 8 * tiles;
     if (blocks > 0x7FFFFFFF)
         return MESWISH_EINVAL;
     dim3 grid((unsigned)blocks);
-#if FFTCONV_MFMA == 2
-    if (op == 0)
-        hipLaunchKernelGGL((cgemm_planar_kernel<true, true, false, true, 1>), grid, dim3(kThreads),
-                           0, s, a, b, c, M, N, K, sAp, sBp, lda, ldb, tiles_n, tiles, nbins);
-    else if (op == 1)
-        hipLaunchKernelGGL((cgemm_planar_kernel<true, false, false, false, 1>), grid,
-                           dim3(kThreads), 0, s, a, b, c, M, N, K, sAp, sBp, lda, ldb, tiles_n,
-                           tiles, nbins);
-    else
-        hipLaunchKernelGGL((cgemm_planar_kernel<false, false, true, false, 1>), grid,
-                           dim3(kThreads), 0, s, a, b, c, M, N, K, sAp, sBp, lda, ldb, tiles_n,
-                           tiles, nbins);
-#else
     if (op == 0)
         hipLaunchKernelGGL((cgemm_mfma_kernel<true, true, false, true>), grid, dim3(kThreads), 0, s,
                            a, b, c, M, N, K, sAp, sBp, lda, ldb, tiles_n, tiles, nbins);
@@ -814,7 +816,6 @@ static int launch_cmul(int op, const float2* a, const float2* b, float2* c, int 
     else
         hipLaunchKernelGGL((cgemm_mfma_kernel<false, false, true, false>), grid, dim3(kThreads), 0,
                            s, a, b, c, M, N, K, sAp, sBp, lda, ldb, tiles_n, tiles, nbins);
-#endif
 #else
     dim3 grid((unsigned)tiles_n, (unsigned)tiles_m, (unsigned)nbins);
     if (op == 0)
