@@ -23,15 +23,17 @@
 //     T consecutive maps of one bin together.
 //   * Contraction.  For every bin, a complex matrix product (M x K) (K x N)
 //     -- S x f by f x f' for the forward: a dense contraction, so it runs on
-//     the matrix cores (v_mfma_f32_32x32x2f32, binary32 in and out), the
-//     complex product expanded into a real one of twice the depth and
-//     width.  Tiles of 64 x 64 complex outputs, K in steps of 16 through
-//     LDS with the next step prefetched into registers; all tiles of one
-//     bin run on one XCD (shared operands stay in that XCD's L2).  A
-//     vector-ALU version of the same tiling is kept for comparison.
+//     the matrix cores (v_mfma_f32_32x32x2f32, binary32 in and out), real
+//     and imaginary parts in separate LDS planes, four real products per
+//     pair of complex k.  Tiles of 64 x 64 (or 64 x 32 where that pads
+//     less) complex outputs, K in steps of 8 through LDS with the next step
+//     prefetched into registers; all tiles of one bin run on one XCD
+//     (shared operands stay in that XCD's L2).  An interleaved matrix-core
+//     version and a vector-ALU version are kept for comparison.
 //   * Inverse.  Column transforms first, keeping only the rows that survive
 //     the crop, then row transforms of the Hermitian half rows; only the
-//     kept m x m corner is written, scaled by 1/n^2.
+//     kept m x m corner is written, scaled by 1/n^2, through LDS as whole
+//     16-byte vectors when the rows are cropped.
 
 #include <hip/hip_runtime.h>
 
@@ -599,6 +601,14 @@ __global__ __launch_bounds__(kThreads) void cgemm_mfma_kernel(const float2* __re
 // in general; WC = 1 where 64-column tiles would pad the product (96
 // columns take 3 tiles of 32 instead of 2 of 64, a quarter of them empty).
 // (Two column subtiles per wave, reusing A, measured slower: 178 VGPRs.)
+// Complex k per K-tile of the planar kernel: 8 measured fastest on the
+// measured layer (16: +2 %, 32: +6 %, registers 174-226).  Two LDS buffers
+// per K-tile (one barrier instead of two) measured slower at 8 and 16.
+#ifndef FFTCONV_PLANAR_KT
+#define FFTCONV_PLANAR_KT 8
+#endif
+constexpr int kPK = FFTCONV_PLANAR_KT;
+
 template <bool AK, bool BK, bool CA, bool CB, int WC>
 __global__ __launch_bounds__(128 * WC) void cgemm_planar_kernel(const float2* __restrict__ A,
                                                                const float2* __restrict__ B,
@@ -609,10 +619,10 @@ __global__ __launch_bounds__(128 * WC) void cgemm_planar_kernel(const float2* __
 {
     constexpr int NT = 128 * WC;        // threads
     constexpr int BN = 32 * WC;         // block tile columns
-    constexpr int LA = kBM * kBK / NT;  // A values per thread per K-tile
-    constexpr int LB = BN * kBK / NT;   // B values per thread per K-tile (4)
-    __shared__ float Ar[kBK][kBM + 4], Ai[kBK][kBM + 4];
-    __shared__ float Br[kBK][BN + 4], Bi[kBK][BN + 4];
+    constexpr int LA = kBM * kPK / NT;  // A values per thread per K-tile
+    constexpr int LB = BN * kPK / NT;   // B values per thread per K-tile
+    __shared__ float Ar[kPK][kBM + 4], Ai[kPK][kBM + 4];
+    __shared__ float Br[kPK][BN + 4], Bi[kPK][BN + 4];
     const int xcd = (int)(blockIdx.x & 7u), q = (int)(blockIdx.x >> 3);
     const int p = (q / tiles) * 8 + xcd;
     if (p >= nbins)
@@ -633,7 +643,7 @@ __global__ __launch_bounds__(128 * WC) void cgemm_planar_kernel(const float2* __
 #pragma unroll
         for (int qq = 0; qq < LA; ++qq) {
             const int idx = threadIdx.x + qq * NT;
-            const int k = AK ? idx % kBK : idx / kBM, i = AK ? idx / kBK : idx % kBM;
+            const int k = AK ? idx % kPK : idx / kBM, i = AK ? idx / kPK : idx % kBM;
             float2 v = make_float2(0.0f, 0.0f);
             if (i0 + i < M && k0 + k < K)
                 v = AK ? Ap[(int64_t)(i0 + i) * lda + (k0 + k)] : Ap[(int64_t)(k0 + k) * lda + (i0 + i)];
@@ -642,7 +652,7 @@ __global__ __launch_bounds__(128 * WC) void cgemm_planar_kernel(const float2* __
 #pragma unroll
         for (int qq = 0; qq < LB; ++qq) {
             const int idx = threadIdx.x + qq * NT;
-            const int k = BK ? idx % kBK : idx / BN, j = BK ? idx / kBK : idx % BN;
+            const int k = BK ? idx % kPK : idx / BN, j = BK ? idx / kPK : idx % BN;
             float2 w = make_float2(0.0f, 0.0f);
             if (j0 + j < N && k0 + k < K)
                 w = BK ? Bp[(int64_t)(j0 + j) * ldb + (k0 + k)] : Bp[(int64_t)(k0 + k) * ldb + (j0 + j)];
@@ -653,27 +663,27 @@ __global__ __launch_bounds__(128 * WC) void cgemm_planar_kernel(const float2* __
 #pragma unroll
         for (int qq = 0; qq < LA; ++qq) {
             const int idx = threadIdx.x + qq * NT;
-            const int k = AK ? idx % kBK : idx / kBM, i = AK ? idx / kBK : idx % kBM;
+            const int k = AK ? idx % kPK : idx / kBM, i = AK ? idx / kPK : idx % kBM;
             Ar[k][i] = ra[qq].x;
             Ai[k][i] = ra[qq].y;
         }
 #pragma unroll
         for (int qq = 0; qq < LB; ++qq) {
             const int idx = threadIdx.x + qq * NT;
-            const int k = BK ? idx % kBK : idx / BN, j = BK ? idx / kBK : idx % BN;
+            const int k = BK ? idx % kPK : idx / BN, j = BK ? idx / kPK : idx % BN;
             Br[k][j] = rb[qq].x;
             Bi[k][j] = rb[qq].y;
         }
     };
 
     fetch(0);
-    for (int k0 = 0; k0 < K; k0 += kBK) {
+    for (int k0 = 0; k0 < K; k0 += kPK) {
         stash();
         __syncthreads();
-        if (k0 + kBK < K)
-            fetch(k0 + kBK);
+        if (k0 + kPK < K)
+            fetch(k0 + kPK);
 #pragma unroll
-        for (int kk = 0; kk < kBK; kk += 2) {
+        for (int kk = 0; kk < kPK; kk += 2) {
             const float are = Ar[kk + h][wm * 32 + r], aim = Ai[kk + h][wm * 32 + r];
             const float bre = Br[kk + h][wn * 32 + r], bim = Bi[kk + h][wn * 32 + r];
             acc_re = __builtin_amdgcn_mfma_f32_32x32x2f32(are, bre, acc_re, 0, 0, 0);
