@@ -347,29 +347,18 @@ struct LeakyReluOp {
 // Q a degree-9 polynomial; fractional error below 1.2e-7 for every z >= 0,
 // and erfc(-|z|) = 2 - erfc(|z|).  z^2 = x^2 / 2 is taken from the exact
 // x^2 (hi+lo).  phi(x) = e^(-x^2/2) / sqrt(2 pi) with C = -log2(e) / 2.
-// For x < -6 the rare branch applies e^(-x^2/2) by powers of two.
+// With bfloat16 I/O the tail erfc(|z|) / 2 is instead one exponential of a
+// short polynomial (tail_short).  For x < -6 the rare branch applies
+// e^(-x^2/2) by powers of two.
 // ---------------------------------------------------------------------------
 struct GeluErfOp {
     static constexpr bool kHasRare = true;
     static constexpr float kRareBelow = -6.0f;
     static constexpr float kLog2ef = 1.44269504088896341f;
 
-    // Q(t) of the erfc form above (t in (0, 1]).  FULL false: a degree-4
-    // polynomial with relative erfc error below 7.1e-5 on the fast path's
-    // range x >= -6 replaces the degree-9 fit -- Chebyshev interpolation of
-    // the exact Q, computed by gen_gelu_bf16_poly.py.  Only the bfloat16
-    // forward uses it: the backward's Phi + x phi cancels near its zero
-    // (x = -0.75), where only the full fit keeps bfloat16 within 1 ulp.
-    template <bool FULL>
+    // Q(t) of the erfc form above (t in (0, 1]), degree 9.
     __device__ static float q_poly(float t)
     {
-        if (!FULL) {
-            float r = 0.05114523f;
-            r = fmaf(t, r, -0.5033026f);
-            r = fmaf(t, r, 0.86044306f);
-            r = fmaf(t, r, 0.83762014f);
-            return fmaf(t, r, -1.2459551f);
-        }
         float p = 0.17087277f;
         p = fmaf(t, p, -0.82215223f);
         p = fmaf(t, p, 1.48851587f);
@@ -382,34 +371,63 @@ struct GeluErfOp {
         return fmaf(t, p, -1.26551223f);
     }
 
-    // erfc(|x| / sqrt 2) / 2 and, through e2 (if not NULL), e^(-x^2/2).
+    // Binary32 I/O: erfc(|x| / sqrt 2) / 2 and, through e2, e^(-x^2/2).
     // Both are below 2^-2900 beyond |x| = 64: clamping keeps x^2 finite (a
     // NaN x still reaches the caller's result through its own factor x).
-    template <bool P, bool FULL>
     __device__ static float half_erfc_abs(float x, const Coef& k, float* e2)
     {
         float a = fminf(fabsf(x), 64.0f);
         float t = rcp_hw(fmaf(0.5f * kInvSqrt2f, a, 1.0f));
-        float q = q_poly<FULL>(t);
+        float q = q_poly(t);
         float x2 = a * a;
         float vh = x2 * k.c_hi;  // -x^2 log2(e) / 2
-        float vl = 0.0f;
-        if (P)
-            vl = fmaf(x2, k.c_lo, fmaf(x2, k.c_hi, -vh)) + fmaf(a, a, -x2) * k.c_hi;
+        float vl = fmaf(x2, k.c_lo, fmaf(x2, k.c_hi, -vh)) + fmaf(a, a, -x2) * k.c_hi;
         float eq = exp2_hw(fmaf(q, kLog2ef, vh + vl));  // e^(-z^2 + Q(t))
         if (e2) {
             float e = exp2_hw(vh);
-            if (P)
-                e = fmaf(e, vl * kLn2f, e);
-            *e2 = e;
+            *e2 = fmaf(e, vl * kLn2f, e);
         }
         return 0.5f * t * eq;
+    }
+
+    // Bfloat16 I/O: the same tail as 2^L(s), s = a / 3 - 1, a = |x| clamped
+    // to [0, 6] (beyond 6 the tail is below every binary32 ulp of 1 - h),
+    // L the Chebyshev interpolant of log2 h on that range computed by
+    // gen_gelu_bf16_poly.py: degree 6 for the forward (relative error
+    // 5e-5), degree 9 for the backward (3.4e-6; Phi + x phi cancels near
+    // x = -0.752).  One exponential and no reciprocal.
+    template <bool BWD>
+    __device__ static float tail_short(float x)
+    {
+        const float s = fmaf(fminf(fabsf(x), 6.0f), 1.0f / 3.0f, -1.0f);
+        float p;
+        if (BWD) {
+            p = 0.0008011838f;
+            p = fmaf(s, p, -0.0000443616f);
+            p = fmaf(s, p, -0.005935571f);
+            p = fmaf(s, p, 0.016855113f);
+            p = fmaf(s, p, -0.03940879f);
+            p = fmaf(s, p, 0.09169615f);
+            p = fmaf(s, p, -0.2043446f);
+            p = fmaf(s, p, -6.033987f);
+            p = fmaf(s, p, -14.20953f);
+            p = fmaf(s, p, -9.532935f);
+        } else {
+            p = 0.016779546f;
+            p = fmaf(s, p, -0.048049062f);
+            p = fmaf(s, p, 0.09174274f);
+            p = fmaf(s, p, -0.20028456f);
+            p = fmaf(s, p, -6.034002f);
+            p = fmaf(s, p, -14.210027f);
+            p = fmaf(s, p, -9.532934f);
+        }
+        return exp2_hw(p);
     }
 
     template <bool P>
     __device__ static float fwd(float x, const Coef& k, bool& rare)
     {
-        float h = half_erfc_abs<P, P>(x, k, nullptr);
+        float h = P ? half_erfc_abs(x, k, nullptr) : tail_short<false>(x);
         float cdf = x < 0.0f ? h : 1.0f - h;
         rare |= x < kRareBelow;
         return x * cdf;
@@ -418,8 +436,14 @@ struct GeluErfOp {
     template <bool P>
     __device__ static float bwd(float x, float dy, const Coef& k, bool& rare)
     {
-        float e2;
-        float h = half_erfc_abs<P, true>(x, k, &e2);
+        float e2, h;
+        if (P) {
+            h = half_erfc_abs(x, k, &e2);
+        } else {
+            h = tail_short<true>(x);
+            const float a = fminf(fabsf(x), 64.0f);
+            e2 = exp2_hw(a * a * k.c_hi);
+        }
         float cdf = x < 0.0f ? h : 1.0f - h;
         rare |= x < kRareBelow;
         return dy * fmaf(x, e2 * kInvSqrt2Pif, cdf);
@@ -438,7 +462,7 @@ struct GeluErfOp {
     {
         float a = fabsf(x);
         float t = rcp_hw(fmaf(0.5f * kInvSqrt2f, a, 1.0f));
-        g = 0.5f * t * exp2_hw(q_poly<true>(t) * kLog2ef);
+        g = 0.5f * t * exp2_hw(q_poly(t) * kLog2ef);
         float x2 = a * a;
         float vh = x2 * k.c_hi;
         float vl = fmaf(x2, k.c_lo, fmaf(x2, k.c_hi, -vh)) + fmaf(a, a, -x2) * k.c_hi;
