@@ -261,7 +261,7 @@ def fft_key(r: dict):
         return ("copy", 0)
     maps_per_block = {8: 64, 16: 64, 32: 32, 64: 8}
     for kind in ("r2c", "c2r"):
-        mm = re.search(kind + r"_kernel<(\d+)>", name)
+        mm = re.search(kind + r"_kernel<(\d+)(?:, (?:true|false))?>", name)
         if mm:
             # Kernel traces give Grid_Size_X / Workgroup_Size_X, counter
             # collections Grid_Size / Workgroup_Size (1-D grids here).
