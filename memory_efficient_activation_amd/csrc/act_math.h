@@ -7,6 +7,9 @@
 //   is_rare<BWD, P>(x, k)    true exactly where the fast path sets `rare`
 //   fwd_rare(x, k), bwd_rare(x, dy, k)   the rare branch, taken per wave
 //
+// x = +-inf gives the limits as x -> +-inf with the parameter fixed (a zero
+// Swish alpha or LeakyReLU slope leaves 0 * inf = NaN); NaN gives NaN.
+//
 // P (precise) is true for binary32 I/O, where results must agree with the
 // exact value to 1e-5 relative; bfloat16 I/O needs only 2^-9, so its fast
 // paths skip the extra-precision terms.  The fast paths set `rare` exactly
@@ -157,7 +160,7 @@ struct SwishOp {
         int kf;
         lin_exponent(x, k, vh, vl);  // = |t| log2 e
         if (-vh < kZeroExp)
-            return x * 0.0f;
+            return copysignf(0.0f, x);  // also the limit at x = +-inf
         pow2_split(-vh, -vl, ef, kf);
         return scale_pow2(x, 1.0f, ef, kf);
     }
@@ -295,7 +298,8 @@ struct TanhOp {
 };
 
 // ---------------------------------------------------------------------------
-// ReLU and LeakyReLU (slope a = k.p): compare and select; NaN propagates.
+// ReLU and LeakyReLU (slope a = k.p): compare and select; NaN propagates,
+// and x = -inf gives the limits (0, and the slope a in the backward).
 // ---------------------------------------------------------------------------
 struct ReluOp {
     static constexpr bool kHasRare = false;
@@ -303,13 +307,13 @@ struct ReluOp {
     template <bool P>
     __device__ static float fwd(float x, const Coef&, bool&)
     {
-        return x > 0.0f ? x : x * 0.0f;
+        return x > 0.0f ? x : (x <= 0.0f ? 0.0f : x);
     }
 
     template <bool P>
     __device__ static float bwd(float x, float dy, const Coef&, bool&)
     {
-        return dy * (x > 0.0f ? 1.0f : x * 0.0f);
+        return dy * (x > 0.0f ? 1.0f : (x <= 0.0f ? 0.0f : x));
     }
 
     template <bool BWD, bool P>
@@ -330,7 +334,7 @@ struct LeakyReluOp {
     template <bool P>
     __device__ static float bwd(float x, float dy, const Coef& k, bool&)
     {
-        return dy * (x > 0.0f ? 1.0f : fmaf(0.0f, x, k.p));
+        return dy * (x > 0.0f ? 1.0f : (x <= 0.0f ? k.p : x));
     }
 
     template <bool BWD, bool P>
@@ -446,7 +450,8 @@ struct GeluErfOp {
         }
         float cdf = x < 0.0f ? h : 1.0f - h;
         rare |= x < kRareBelow;
-        return dy * fmaf(x, e2 * kInvSqrt2Pif, cdf);
+        // x = +inf: the limit 1 (the product x phi would be inf * 0).
+        return x == INFINITY ? dy : dy * fmaf(x, e2 * kInvSqrt2Pif, cdf);
     }
 
     template <bool BWD, bool P>
@@ -477,7 +482,7 @@ struct GeluErfOp {
         int kf;
         bool zero;
         split(x, k, g, ef, kf, zero);
-        return zero ? x * 0.0f : scale_pow2(x, g, ef, kf);
+        return zero ? copysignf(0.0f, x) : scale_pow2(x, g, ef, kf);  // -0 at -inf
     }
 
     // dx = dy (Phi + x phi) = dy e^(-x^2/2) (g + x / sqrt(2 pi)).
@@ -565,7 +570,7 @@ struct GeluTanhOp {
             return x;  // sigmoid(2u) rounds to 1
         if (vh > kMaxExp) {
             if (-vh < kZeroExp)
-                return x * 0.0f;
+                return copysignf(0.0f, x);  // also the limit at x = -inf
             float ef;
             int kf;
             pow2_split(-vh, -vl, ef, kf);  // sigmoid(2u) = e^2u

@@ -23,8 +23,8 @@ What it computes (cited by page title and section):
 Every function here is pinned by ``tests/test_oracle_pins.py`` against facts
 that do not come from the oracle itself (closed forms, finite differences,
 PyTorch fp64 autograd of the naive module, library sigmoid, exact rational
-rounding, the worked numbers of page 3).  No function is "parity unpinned"
-except for infinite inputs, which are outside the contract.
+rounding, the worked numbers of page 3).  No function is "parity unpinned";
+infinite inputs give the limits as x -> +-inf, pinned by their closed forms.
 """
 
 from __future__ import annotations

@@ -37,6 +37,9 @@
  *     for binary32 and for bfloat16 alike.
  *   - bfloat16 is rounded directly from the binary64 value (never through
  *     binary32), so the oracle never rounds twice.
+ *   - x = +-inf: the limits as x -> +-inf, with the parameter fixed (a
+ *     zero alpha of Swish or zero slope of LeakyReLU keeps IEEE 0 * inf =
+ *     NaN); see swish_limit below.
  *
  * Data layout: contiguous 1-D arrays.  dtype 0 = binary32 (float),
  * dtype 1 = bfloat16 stored as its 16-bit pattern (the upper half of the
@@ -145,10 +148,37 @@ double oracle_sigmoid(double t)
     return 1.0 / (1.0 + exp(-t));
 }
 
+/* Infinite inputs (reading of the pages, which define the functions on the
+ * reals only): the value and dy times the derivative at x = +-inf are their
+ * limits as x -> +-inf with the parameter held fixed.  Written out because
+ * the finite formulas form 0 * inf there.  For Swish, with t = alpha x:
+ *   t -> +inf: Sigmoid(t) -> 1, the value tends to x and the derivative
+ *              s (1 + t (1 - s)) to 1 (t e^-t -> 0);
+ *   t -> -inf: the value x e^t and the derivative e^t (1 + t) tend to 0,
+ *              with the sign of x and a negative sign respectively.
+ * alpha = 0 leaves t = 0 * inf, which stays NaN as in IEEE arithmetic. */
+static double swish_limit(double x, double alpha)
+{
+    double t = alpha * x;
+    if (isnan(t))
+        return t;
+    return t > 0.0 ? x : copysign(0.0, x);
+}
+
+static double swish_grad_limit(double x, double dy, double alpha)
+{
+    double t = alpha * x;
+    if (isnan(t))
+        return t;
+    return t > 0.0 ? dy : dy * -0.0;
+}
+
 /* Swish with slope alpha: x * Sigmoid(alpha x)  ([P1] "How is Swish
  * implemented?"). */
 double oracle_swish(double x, double alpha)
 {
+    if (isinf(x))
+        return swish_limit(x, alpha);
     return x * oracle_sigmoid(alpha * x);
 }
 
@@ -163,6 +193,12 @@ double oracle_swish(double x, double alpha)
  * error scale where 1 + t (1 - s) cancels). */
 double oracle_swish_grad(double x, double dy, double alpha, double *scale)
 {
+    if (isinf(x)) {
+        double g = swish_grad_limit(x, dy, alpha);
+        if (scale)
+            *scale = fabs(g);
+        return g;
+    }
     double t = alpha * x;
     double s = oracle_sigmoid(t);
     double one_minus_s = 1.0 - s;
@@ -227,8 +263,12 @@ double oracle_act_f64(int act, double x, double p)
     case ORACLE_ACT_TANH:
         return tanh(x);
     case ORACLE_ACT_GELU_ERF:
+        if (isinf(x))  /* limits: x, and x Phi(x) -> -0 */
+            return x > 0.0 ? x : -0.0;
         return x * std_normal_cdf(x);
     case ORACLE_ACT_GELU_TANH: {
+        if (isinf(x))  /* limits: x, and x sigmoid(2u) -> -0 */
+            return x > 0.0 ? x : -0.0;
         double u = kSqrt2OverPi * (x + kGeluTanhCubic * x * x * x);
         return x * oracle_sigmoid(2.0 * u);
     }
@@ -270,12 +310,22 @@ double oracle_act_grad_f64(int act, double x, double dy, double p, double *scale
         break;
     }
     case ORACLE_ACT_GELU_ERF: {
+        if (isinf(x)) {  /* limits of Phi + x phi: 1 at +inf, -0 at -inf */
+            g = x > 0.0 ? dy : dy * -0.0;
+            m = fabs(g);
+            break;
+        }
         double cdf = std_normal_cdf(x), pdf = std_normal_pdf(x);
         g = dy * (cdf + x * pdf);
         m = fabs(dy) * (cdf + fabs(x) * pdf);
         break;
     }
     case ORACLE_ACT_GELU_TANH: {
+        if (isinf(x)) {  /* limits of s (1 + x (1 - s) 2u'): 1 and -0 */
+            g = x > 0.0 ? dy : dy * -0.0;
+            m = fabs(g);
+            break;
+        }
         double u = kSqrt2OverPi * (x + kGeluTanhCubic * x * x * x);
         double du = kSqrt2OverPi * (1.0 + 3.0 * kGeluTanhCubic * x * x);
         double s = oracle_sigmoid(2.0 * u), c = oracle_sigmoid(-2.0 * u);

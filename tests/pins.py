@@ -522,4 +522,52 @@ def pin_family_array_drivers(o):
         assert math.isnan(o.act_grad_f64(act, 1.0, float("nan"), 0.01)[0])
 
 
+
+def pin_infinite_inputs(o):
+    """x = +-inf gives the limits as x -> +-inf (parameter fixed), written
+    as closed forms: Swish and both GELUs tend to x at +inf and to a zero of
+    the sign of x at -inf, their derivatives to 1 and to -0; ReLU's value
+    and slope tend to 0 at -inf, LeakyReLU's to -inf and its slope; sigmoid
+    and tanh tend to their asymptotes with vanishing slope.  A zero
+    parameter keeps IEEE 0 * inf = NaN.  The limits also agree with the
+    oracle far out on the finite axis."""
+    inf = float("inf")
+
+    def same(a, b):
+        return (math.isnan(a) and math.isnan(b)) or (a == b and math.copysign(1, a) == math.copysign(1, b))
+
+    dy = -2.5
+    want = {
+        # act: (param, f(+inf), f(-inf), dy f'(+inf), dy f'(-inf))
+        "swish": (1.0, inf, -0.0, dy, dy * -0.0),
+        "relu": (0.0, inf, 0.0, dy, dy * 0.0),
+        "leaky_relu": (0.01, inf, -inf, dy, dy * 0.01),
+        "sigmoid": (0.0, 1.0, 0.0, dy * 0.0, dy * 0.0),
+        "tanh": (0.0, 1.0, -1.0, dy * 0.0, dy * 0.0),
+        "gelu_erf": (0.0, inf, -0.0, dy, dy * -0.0),
+        "gelu_tanh": (0.0, inf, -0.0, dy, dy * -0.0),
+    }
+    for act, (p, fp, fm, gp, gm) in want.items():
+        assert same(o.act_f64(act, inf, p), fp), act
+        assert same(o.act_f64(act, -inf, p), fm), act
+        assert same(o.act_grad_f64(act, inf, dy, p)[0], gp), act
+        assert same(o.act_grad_f64(act, -inf, dy, p)[0], gm), act
+        # Far out on the finite axis the values already sit at the limits.
+        for x, lim in ((1e4, fp), (-1e4, fm)):
+            v = o.act_f64(act, x, p)
+            if math.isinf(lim):  # grows without bound, with the limit's sign
+                assert math.copysign(1, v) == math.copysign(1, lim) and abs(v) >= 1e-2 * abs(x), (act, x, v)
+            else:
+                assert abs(v - lim) < 1e-12, (act, x, v)
+    # Swish with a negative slope mirrors the limits; a zero slope is NaN.
+    assert same(o.swish_f64(inf, -1.0), 0.0) and same(o.swish_f64(-inf, -1.0), -inf)
+    assert same(o.grad_f64(inf, 1.0, -1.0)[0], -0.0) and same(o.grad_f64(-inf, 1.0, -1.0)[0], 1.0)
+    assert math.isnan(o.swish_f64(inf, 0.0)) and math.isnan(o.grad_f64(-inf, 1.0, 0.0)[0])
+    assert math.isnan(o.act_f64("leaky_relu", -inf, 0.0))
+    # The array drivers round the limits like any other value.
+    x = np.array([inf, -inf], dtype=np.float32)
+    y = o.act_fwd("gelu_erf", x, 0.0)
+    assert y[0] == inf and y[1] == 0.0 and math.copysign(1, y[1]) < 0
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

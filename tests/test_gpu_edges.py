@@ -8,7 +8,8 @@
   (subnormal and underflowing results), tiny and huge alpha;
 * lengths 0..67 and misaligned pointers (vector, head/tail and element-wise
   paths), in-place calls, NaN propagation, bitwise determinism, the alias
-  and limit checks, and grouped == single bit for bit.
+  and limit checks, and grouped == single bit for bit;
+* x = +-inf for every activation: the limits, signs of zeros included.
 """
 
 import os
@@ -112,6 +113,56 @@ def test_lengths_and_misalignment(dtype, oracle):
                 assert r["ok"], (n, ox, oo, r)
                 checked += 1
     say(f"[edges] {dtype}: {checked} (length, offset) cases")
+
+
+INF_CASES = [("swish", 1.0), ("swish", -1.5), ("swish", 0.0), ("relu", 0.0),
+             ("leaky_relu", 0.01), ("leaky_relu", 0.0), ("sigmoid", 0.0), ("tanh", 0.0),
+             ("gelu", 0.0), ("gelu_tanh", 0.0)]
+
+
+def _zero_sign(a, dtype):
+    if dtype == "bf16":
+        a = np.asarray(a, np.uint16)
+        return (a & 0x7FFF) == 0, (a & 0x8000) != 0
+    a = np.asarray(a, np.float32)
+    return a == 0, np.signbit(a)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kind,param", INF_CASES)
+def test_infinite_inputs_give_the_limits(kind, param, dtype, oracle):
+    """x = +-inf among finite values: the limits as x -> +-inf, as the
+    oracle defines them (a zero parameter gives NaN on both sides), through
+    the vector path and, one element in, the element-wise path; zero
+    results must also carry the oracle's sign."""
+    n = 1000 + 7
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(n) * 4
+    x[::5] = np.inf
+    x[1::5] = -np.inf
+    dy = rng.standard_normal(n)
+    xh, dyh = inputs.encode(x, dtype), inputs.encode(dy, dtype)
+    xd, dyd = to_dev(xh), to_dev(dyh)
+    oname = {"gelu": "gelu_erf"}.get(kind, kind)
+    for off in (0, 1):
+        y = mea.act_fwd(kind, xd[off:], param)
+        dx = mea.act_bwd(kind, xd[off:], dyd[off:], param)
+        torch.cuda.synchronize()
+        oy = oracle.act_fwd(oname, xh[off:], param)
+        odx, m = oracle.act_bwd(oname, xh[off:], dyh[off:], param)
+        gy, gdx = to_host(y), to_host(dx)
+        if dtype == "bf16":
+            rf, rb = bf16_report(gy, oy), bf16_report(gdx, odx)
+        else:
+            rf, rb = f32_report(gy, oy), f32_report(gdx, odx, m)
+        say(f"[edges] +-inf {kind} p={param} {dtype} offset {off}: fwd {rf} bwd {rb}")
+        assert rf["ok"], rf
+        assert rb["ok"], rb
+        for got, want in ((gy, oy), (gdx, odx)):
+            wz, ws = _zero_sign(want, dtype)
+            gz, gs = _zero_sign(got, dtype)
+            assert np.array_equal(gz[wz], np.ones(int(wz.sum()), bool)), (kind, param, off)
+            assert np.array_equal(gs[wz], ws[wz]), (kind, param, off, "sign of zero")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
