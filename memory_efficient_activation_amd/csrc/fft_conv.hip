@@ -189,15 +189,29 @@ template <int N> using InvTile = Tile<N, true>;
 // zero-padded to N x N -> half spectra, bin-major.
 // ---------------------------------------------------------------------------
 
+// One set of maps to transform: `batch` maps of m x m at x -> spec.
+struct R2cJob {
+    const float* x;
+    int batch, m;
+    float2* spec;
+};
+
+// Blocks [0, blocks0) transform job a, the rest job b: the two inputs of a
+// layer operation share one launch, so the smaller one fills the partial
+// last round of the other.
 template <int N>
-__global__ __launch_bounds__(Tile<N>::kThreads) void r2c_kernel(const float* __restrict__ x, int batch,
-                                                       int m, float2* __restrict__ spec)
+__global__ __launch_bounds__(Tile<N>::kThreads) void r2c_kernel(R2cJob a, R2cJob b, int blocks0)
 {
     constexpr int T = Tile<N>::T;
     constexpr int H = N / 2 + 1;
     constexpr int MS = N * H + 1;  // map stride in LDS, odd: no bank conflicts across maps
     __shared__ __align__(16) float2 buf[T * MS];
-    const int64_t b0 = (int64_t)blockIdx.x * T;
+    const bool second = (int)blockIdx.x >= blocks0;
+    const float* __restrict__ x = second ? b.x : a.x;
+    float2* __restrict__ spec = second ? b.spec : a.spec;
+    const int batch = second ? b.batch : a.batch;
+    const int m = second ? b.m : a.m;
+    const int64_t b0 = (int64_t)((int)blockIdx.x - (second ? blocks0 : 0)) * T;
 
     // Rows: job = (map, r).
     constexpr int NT = Tile<N>::kThreads;
@@ -726,10 +740,12 @@ static bool overlaps(const void* a, size_t na, const void* b, size_t nb)
 static int status_of(hipError_t e) { return e == hipSuccess ? MESWISH_OK : MESWISH_EHIP; }
 
 template <int N>
-static void r2c_launch(const float* x, int batch, int m, float2* spec, hipStream_t s)
+static void r2c_launch(const R2cJob& a, const R2cJob& b, hipStream_t s)
 {
-    const unsigned grid = (unsigned)((batch + Tile<N>::T - 1) / Tile<N>::T);
-    hipLaunchKernelGGL(r2c_kernel<N>, dim3(grid), dim3(Tile<N>::kThreads), 0, s, x, batch, m, spec);
+    const int T = Tile<N>::T;
+    const int blocks0 = (a.batch + T - 1) / T, blocks1 = (b.batch + T - 1) / T;
+    hipLaunchKernelGGL(r2c_kernel<N>, dim3((unsigned)(blocks0 + blocks1)), dim3(Tile<N>::kThreads),
+                       0, s, a, b, blocks0);
 }
 
 template <int N>
@@ -745,13 +761,14 @@ static void c2r_launch(const float2* spec, int batch, int m, float scale, float*
                            batch, m, scale, y);
 }
 
-static int launch_r2c(const float* x, int batch, int m, int n, float2* spec, hipStream_t s)
+// Transforms of one or two sets of maps (b.batch = 0 for one) in one launch.
+static int launch_r2c(const R2cJob& a, const R2cJob& b, int n, hipStream_t s)
 {
     switch (n) {
-    case 8: r2c_launch<8>(x, batch, m, spec, s); break;
-    case 16: r2c_launch<16>(x, batch, m, spec, s); break;
-    case 32: r2c_launch<32>(x, batch, m, spec, s); break;
-    default: r2c_launch<64>(x, batch, m, spec, s); break;
+    case 8: r2c_launch<8>(a, b, s); break;
+    case 16: r2c_launch<16>(a, b, s); break;
+    case 32: r2c_launch<32>(a, b, s); break;
+    default: r2c_launch<64>(a, b, s); break;
     }
     return status_of(hipGetLastError());
 }
@@ -877,7 +894,8 @@ extern "C" int fftconv_r2c(const float* x, int batch, int m, int n, void* spec, 
         return MESWISH_EINVAL;
     if (overlaps(x, (size_t)batch * m * m * 4, spec, (size_t)batch * bins(n) * 8))
         return MESWISH_EALIAS;
-    return launch_r2c(x, batch, m, n, static_cast<float2*>(spec), static_cast<hipStream_t>(stream));
+    const R2cJob a{x, batch, m, static_cast<float2*>(spec)}, none{x, 0, m, nullptr};
+    return launch_r2c(a, none, n, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int fftconv_c2r(const void* spec, int batch, int n, int m, float scale, float* y,
@@ -951,9 +969,7 @@ static int run_op(int op, const float* in1, const float* in2, float* out, int S,
     float2* s1 = static_cast<float2*>(freq);
     float2* s2 = s1 + b1 * P;
     float2* so = s2 + b2 * P;
-    int st = launch_r2c(in1, (int)b1, m1, n, s1, s);
-    if (st == MESWISH_OK)
-        st = launch_r2c(in2, (int)b2, m2, n, s2, s);
+    int st = launch_r2c(R2cJob{in1, (int)b1, m1, s1}, R2cJob{in2, (int)b2, m2, s2}, n, s);
     if (st == MESWISH_OK)
         st = launch_cmul(op, s1, s2, so, S, f, fo, (int)P, s);
     if (st == MESWISH_OK)

@@ -245,6 +245,12 @@ def fft_stages():
     st = {}
     for name, B, mm in (("r2c x", S * f, n), ("r2c w", fo * f, k), ("r2c g", S * fo, m)):
         st[("r2c", B)] = (name, B * mm * mm * 4 + B * P * 8, 0)
+    # The layer operations transform both inputs in one launch.
+    for name, parts in (("r2c x+w (forward)", ((S * f, n), (fo * f, k))),
+                        ("r2c g+w (input gradient)", ((S * fo, m), (fo * f, k))),
+                        ("r2c g+x (weight gradient)", ((S * fo, m), (S * f, n)))):
+        B = sum(b for b, _ in parts)
+        st[("r2c", B)] = (name, sum(b * mm * mm * 4 + b * P * 8 for b, mm in parts), 0)
     for name, B, mm in (("c2r y (forward)", S * fo, m), ("c2r gx (input gradient)", S * f, n),
                         ("c2r gw (weight gradient)", fo * f, k)):
         st[("c2r", B)] = (name, B * P * 8 + B * mm * mm * 4, 0)
