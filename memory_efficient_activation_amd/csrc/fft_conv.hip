@@ -369,7 +369,15 @@ __global__ __launch_bounds__(InvTile<N>::kThreads) void c2r_kernel(const float2*
                 a[v] = conjf2(in[N - v]);
             fft_reg<N, true>(a);
             float* out = y + (b * m + p) * (int64_t)m;
-            if ((m & 1) == 0 && ((uintptr_t)y & 7u) == 0) {
+            if ((m & 3) == 0 && ((uintptr_t)y & 15u) == 0) {
+                // m a multiple of 4: every row starts 16-byte aligned; store quads.
+#pragma unroll
+                for (int q = 0; q < N; q += 4)
+                    if (q < m)
+                        *reinterpret_cast<float4*>(out + q) =
+                            make_float4(a[q].x * scale, a[q + 1].x * scale, a[q + 2].x * scale,
+                                        a[q + 3].x * scale);
+            } else if ((m & 1) == 0 && ((uintptr_t)y & 7u) == 0) {
                 // Even m: every row starts 8-byte aligned; store pairs.
 #pragma unroll
                 for (int q = 0; q < N; q += 2)
