@@ -236,6 +236,15 @@ __global__ __launch_bounds__(Tile<N>::kThreads) void r2c_kernel(R2cJob a, R2cJob
                 a[c + 2] = make_float2(q.z, 0.0f);
                 a[c + 3] = make_float2(q.w, 0.0f);
             }
+        } else if ((m & 1) == 0 && ((uintptr_t)x & 7u) == 0) {
+            // Even m: every row starts 8-byte aligned; load pairs.
+#pragma unroll
+            for (int c = 0; c < N; c += 2) {
+                const float2 q = c < m ? *reinterpret_cast<const float2*>(row + c)
+                                       : make_float2(0.0f, 0.0f);
+                a[c] = make_float2(q.x, 0.0f);
+                a[c + 1] = make_float2(q.y, 0.0f);
+            }
         } else {
 #pragma unroll
             for (int c = 0; c < N; ++c)
