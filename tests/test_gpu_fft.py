@@ -168,6 +168,35 @@ def test_bench_layer_at_full_size_on_sampled_maps():
     assert buf.nbytes == fft._lib.library().fftconv_buffer_bytes(L.S, L.f, L.fo, L.n)
 
 
+@pytest.mark.parametrize("S,f,fo,n,k", [(16, 32, 48, 64, 9), (64, 48, 80, 16, 5)])
+def test_larger_layers_on_sampled_maps(S, f, fo, n, k):
+    """n = 64 and n = 16 at sizes that span many blocks of every kernel
+    (and 64- and 32-column product tiles): 8 sampled output maps of each
+    operation against the direct definition."""
+    L = fft_inputs.conv_layer(S, f, fo, n, k, seed=7 * n + k)
+    buf = fft.FrequencyBuffer()
+    x, w, g = _dev(L.x), _dev(L.w), _dev(L.g)
+    y, gx, gw = fft.fprop(x, w, buf), fft.bprop(g, w, n, buf), fft.accgrad(x, g, k, buf)
+    torch.cuda.synchronize()
+    y, gx, gw = _host(y), _host(gx), _host(gw)
+    rng = np.random.default_rng(n)
+    worst = [0.0, 0.0, 0.0]
+    for _ in range(8):
+        s, fi, oi = rng.integers(S), rng.integers(f), rng.integers(fo)
+        want = fo_.fprop_direct(L.x[s:s + 1], L.w[oi:oi + 1])[0, 0]
+        worst[0] = max(worst[0], np.abs(y[s, oi] - want).max()
+                       / fo_.fprop_scale(L.x[s:s + 1], L.w[oi:oi + 1])[0, 0])
+        want = fo_.bprop_direct(L.g[s:s + 1], L.w[:, fi:fi + 1], n)[0, 0]
+        worst[1] = max(worst[1], np.abs(gx[s, fi] - want).max()
+                       / fo_.bprop_scale(L.g[s:s + 1], L.w[:, fi:fi + 1])[0, 0])
+        want = fo_.accgrad_direct(L.x[:, fi:fi + 1], L.g[:, oi:oi + 1], k)[0, 0]
+        worst[2] = max(worst[2], np.abs(gw[oi, fi] - want).max()
+                       / fo_.accgrad_scale(L.x[:, fi:fi + 1], L.g[:, oi:oi + 1])[0, 0])
+    say(f"[fft] layer {L.name}, 8 sampled maps each: fprop {worst[0]:.2e} bprop {worst[1]:.2e} "
+        f"accgrad {worst[2]:.2e}")
+    assert max(worst) <= RTOL
+
+
 def test_module_autograd_matches_torch_conv2d():
     torch.manual_seed(0)
     buf = fft.FrequencyBuffer()
