@@ -21,7 +21,7 @@ everything except the bottleneck's first stage:
 and report the bytes held after the forward, the peak over a training step,
 the step time, and the agreement of loss and gradients.
 
-    python -m memory_efficient_activation_amd.dense_experiment [--depth 100] [--batch 64]
+    python -m memory_efficient_activation_amd.dense_experiment [--depth 100] [--batch 64] [--graph]
 """
 
 from __future__ import annotations
@@ -177,6 +177,72 @@ def measure(depth: int = 100, batch: int = 64, growth: int = 12, reps: int = 5,
     return out
 
 
+def measure_graph(depth: int = 100, batch: int = 64, growth: int = 12, reps: int = 20,
+                  checks: int = 3, seed: int = 0) -> dict:
+    """The same training step (forward + backward) of both networks captured
+    once into a HIP graph and replayed: the step's GPU time without the
+    host's per-layer launch cost.  Every checked replay, with eager work and
+    synchronisations between replays, is compared with an eager step on the
+    same weights and batch (loss and every parameter's gradient)."""
+    dev = torch.device("cuda")
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    x = torch.randn(batch, 3, 32, 32, generator=g).to(dev)
+    y = torch.randint(0, 10, (batch,), generator=g).to(dev)
+    torch.manual_seed(seed)
+    plain = DenseNetBC(depth, growth, efficient=False).to(dev)
+    eff = DenseNetBC(depth, growth, efficient=True).to(dev)
+    with torch.no_grad():
+        pe = dict(eff.named_parameters())
+        for name, p in plain.named_parameters():
+            pe[name].copy_(p)
+    out = {"model": f"DenseNet-BC-{depth}, growth {growth}", "batch": batch, "dtype": "float32",
+           "replays_timed": reps, "replays_checked": checks}
+    for name, model in (("naive", plain), ("memory_efficient", eff)):
+        model.train()
+        model.zero_grad(set_to_none=True)
+        ref_loss = F.cross_entropy(model(x), y)
+        ref_loss.backward()
+        ref_loss = float(ref_loss.detach())
+        ref = {k: p.grad.detach().clone() for k, p in model.named_parameters()}
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # warm-up on a side stream, as capture requires
+            for _ in range(3):
+                model.zero_grad(set_to_none=True)
+                F.cross_entropy(model(x), y).backward()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        model.zero_grad(set_to_none=True)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            static_loss = F.cross_entropy(model(x), y)
+            static_loss.backward()
+        worst_loss, worst_grad = 0.0, 0.0
+        for _ in range(checks):
+            graph.replay()
+            torch.cuda.synchronize()
+            worst_loss = max(worst_loss, abs(float(static_loss) - ref_loss) / abs(ref_loss))
+            for k, p in model.named_parameters():
+                worst_grad = max(worst_grad, float((p.grad - ref[k]).abs().max()
+                                                   / ref[k].abs().max().clamp_min(1e-30)))
+            torch.randn(1 << 20, device=dev).sum().item()  # eager work between replays
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        graph.replay()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        out[name] = {"graph_step_ms": round(a.elapsed_time(b) / reps, 3),
+                     "replay_vs_eager_loss_rel": worst_loss,
+                     "replay_vs_eager_grad_rel": worst_grad}
+        del graph
+    out["graph_time_ratio_efficient_over_naive"] = round(
+        out["memory_efficient"]["graph_step_ms"] / out["naive"]["graph_step_ms"], 4)
+    return out
+
+
 def errors_vs_binary64(depth: int = 40, batch: int = 16, growth: int = 12, seed: int = 0) -> dict:
     """Per-parameter gradient error of the plain and the efficient network on
     the GPU against the plain network evaluated in binary64 on the CPU (same
@@ -217,8 +283,12 @@ def main():
     p.add_argument("--depth", type=int, default=100)
     p.add_argument("--batch", type=int, default=64)
     p.add_argument("--reps", type=int, default=5)
+    p.add_argument("--graph", action="store_true",
+                   help="also time the step captured into a HIP graph (replays checked)")
     a = p.parse_args()
     print(json.dumps(measure(a.depth, a.batch, reps=a.reps)), flush=True)
+    if a.graph:
+        print(json.dumps(measure_graph(a.depth, a.batch)), flush=True)
 
 
 if __name__ == "__main__":

@@ -40,3 +40,14 @@ def test_densenet_bc40_gradients_against_binary64():
     assert ef["loss_rel_err"] < 1e-6
     for k, e in ef["grad_rel_err"].items():
         assert e <= 1.5 * nv["grad_rel_err"][k] + 1e-4, (k, e, nv["grad_rel_err"][k])
+
+
+def test_densenet_bc40_step_under_graph_capture():
+    """The training step of both networks captured into a HIP graph: every
+    checked replay (eager work between replays) gives the eager step's loss
+    and gradients."""
+    r = dx.measure_graph(depth=40, batch=16, reps=5, checks=3)
+    say(f"[dense-model] graph-captured step: {r}")
+    for name in ("naive", "memory_efficient"):
+        assert r[name]["replay_vs_eager_loss_rel"] <= 1e-6, (name, r[name])
+        assert r[name]["replay_vs_eager_grad_rel"] <= 1e-4, (name, r[name])
