@@ -640,6 +640,7 @@ __global__ __launch_bounds__(kThreads) void cgemm_mfma_kernel(const float2* __re
 #endif
 constexpr int kPK = FFTCONV_PLANAR_KT;
 
+
 template <bool AK, bool BK, bool CA, bool CB, int WC>
 __global__ __launch_bounds__(128 * WC) void cgemm_planar_kernel(const float2* __restrict__ A,
                                                                const float2* __restrict__ B,
@@ -668,15 +669,19 @@ __global__ __launch_bounds__(128 * WC) void cgemm_planar_kernel(const float2* __
     f32x16 acc_re = f32x16{0}, acc_im = f32x16{0};
 
     // Global -> register staging of one K-tile; the next tile's loads are
-    // issued before the current tile's products.
+    // issued as soon as the current one is in LDS, before the barrier and
+    // the current tile's products.
     float2 ra[LA], rb[LB];
+    // Tiles wholly inside the matrices load without per-element checks.
+    const bool a_inside = i0 + kBM <= M, b_inside = j0 + BN <= N;
     auto fetch = [&](int k0) {
+        const bool k_inside = k0 + kPK <= K;
 #pragma unroll
         for (int qq = 0; qq < LA; ++qq) {
             const int idx = threadIdx.x + qq * NT;
             const int k = AK ? idx % kPK : idx / kBM, i = AK ? idx / kPK : idx % kBM;
             float2 v = make_float2(0.0f, 0.0f);
-            if (i0 + i < M && k0 + k < K)
+            if ((a_inside && k_inside) || (i0 + i < M && k0 + k < K))
                 v = AK ? Ap[(int64_t)(i0 + i) * lda + (k0 + k)] : Ap[(int64_t)(k0 + k) * lda + (i0 + i)];
             ra[qq] = CA ? conjf2(v) : v;
         }
@@ -685,7 +690,7 @@ __global__ __launch_bounds__(128 * WC) void cgemm_planar_kernel(const float2* __
             const int idx = threadIdx.x + qq * NT;
             const int k = BK ? idx % kPK : idx / BN, j = BK ? idx / kPK : idx % BN;
             float2 w = make_float2(0.0f, 0.0f);
-            if (j0 + j < N && k0 + k < K)
+            if ((b_inside && k_inside) || (j0 + j < N && k0 + k < K))
                 w = BK ? Bp[(int64_t)(j0 + j) * ldb + (k0 + k)] : Bp[(int64_t)(k0 + k) * ldb + (j0 + j)];
             rb[qq] = CB ? conjf2(w) : w;
         }
@@ -710,9 +715,9 @@ __global__ __launch_bounds__(128 * WC) void cgemm_planar_kernel(const float2* __
     fetch(0);
     for (int k0 = 0; k0 < K; k0 += kPK) {
         stash();
-        __syncthreads();
         if (k0 + kPK < K)
-            fetch(k0 + kPK);
+            fetch(k0 + kPK);  // the registers are free once stored
+        __syncthreads();
 #pragma unroll
         for (int kk = 0; kk < kPK; kk += 2) {
             const float are = Ar[kk + h][wm * 32 + r], aim = Ai[kk + h][wm * 32 + r];
