@@ -39,6 +39,10 @@ newest source, the forward, the backward's re-population of the shared
 buffer, and the backward (reduction + apply).  ``--dense-dtype`` picks
 binary32 (default) or bfloat16 feature maps.
 
+``--grouped`` measures the grouped launch (one kernel per direction) over
+the seven EfficientNet MBConv-shaped bf16 tensors of the grouped
+configuration, against seven single launches per direction.
+
 ``--fft`` measures the FFT convolution layer ("Fast Training of
 Convolutional Networks through FFTs") on S=128, f=96, f'=256, n=32, k=7:
 one step = forward + input gradient + weight gradient, each transforming
@@ -95,6 +99,8 @@ def parse_args():
     p.add_argument("--dense", action="store_true",
                    help="measure the shared-buffer DenseNet layer stage instead")
     p.add_argument("--dense-dtype", default="f32", choices=["f32", "bf16"])
+    p.add_argument("--grouped", action="store_true",
+                   help="grouped Swish over the 7 EfficientNet-shaped bf16 tensors (config 5)")
     p.add_argument("--fft", action="store_true",
                    help="measure the FFT convolution layer instead")
     return p.parse_args()
@@ -682,6 +688,115 @@ def measure_fft(args, lib, torch, dev):
     return result
 
 
+def measure_grouped(args, lib, torch, dev):
+    """Config 5: the grouped launch (one kernel per direction) over the seven
+    EfficientNet-shaped bf16 tensors, against seven single launches per
+    direction, on SETS rotating copies."""
+    from memory_efficient_activation_amd import _lib, inputs
+
+    w = inputs.make(5)
+    dt, alpha = _lib.BF16, float(w.alpha)
+
+    def to_dev(a):
+        return torch.from_numpy(a).view(torch.int16).view(torch.bfloat16).to(dev)
+
+    sets = []
+    for _ in range(SETS):
+        xs = [to_dev(a) for a in w.xs]
+        dys = [to_dev(a) for a in w.dys]
+        ys = [torch.empty_like(x) for x in xs]
+        dxs = [torch.empty_like(x) for x in xs]
+        fd = (_lib.FwdDesc * len(xs))(*[_lib.FwdDesc(x.data_ptr(), y.data_ptr(), x.numel())
+                                        for x, y in zip(xs, ys)])
+        bd = (_lib.BwdDesc * len(xs))(*[_lib.BwdDesc(x.data_ptr(), d.data_ptr(), g.data_ptr(),
+                                                     x.numel()) for x, d, g in zip(xs, dys, dxs)])
+        sets.append(dict(xs=xs, dys=dys, ys=ys, dxs=dxs, fd=fd, bd=bd))
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    count = len(w.xs)
+    total = sum(a.size for a in w.xs)
+    fwd_b, bwd_b = 2 * 2 * total, 3 * 2 * total
+
+    def g_fwd(j):
+        _lib.check(lib.swish_fwd_grouped(sets[j % SETS]["fd"], count, alpha, dt, sh), "grouped")
+
+    def g_bwd(j):
+        _lib.check(lib.swish_bwd_grouped(sets[j % SETS]["bd"], count, alpha, dt, sh), "grouped")
+
+    def s_fwd(j):
+        for d in sets[j % SETS]["fd"]:
+            _lib.check(lib.swish_fwd(d.x, d.y, d.n, alpha, dt, sh), "swish_fwd")
+
+    def s_bwd(j):
+        for d in sets[j % SETS]["bd"]:
+            _lib.check(lib.swish_bwd(d.x, d.dy, d.dx, d.n, alpha, dt, sh), "swish_bwd")
+
+    def region(fn, k):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        a.record(stream)
+        for i in range(k):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, a.elapsed_time(b)
+
+    K = args.steps
+    for i in range(args.warmup):
+        g_fwd(2 * i)
+        g_bwd(2 * i + 1)
+    wall, _ = region(lambda i: (g_fwd(2 * i), g_bwd(2 * i + 1)), K)
+    _, gb_ms = region(g_bwd, K)
+    _, gf_ms = region(g_fwd, K)
+    for i in range(3):
+        s_fwd(2 * i)
+        s_bwd(2 * i + 1)
+    swall, _ = region(lambda i: (s_fwd(2 * i), s_bwd(2 * i + 1)), K)
+    step_b = fwd_b + bwd_b
+    value = step_b * K / wall / 1e9
+    bwd_us = gb_ms * 1e3 / K
+    bwd_gbps = bwd_b / (bwd_us * 1e-6) / 1e9
+    result = {
+        "metric": "HBM GB/s + fraction of peak, grouped Swish fwd+bwd over 7 EfficientNet "
+                  "MBConv-shaped bf16 tensors (70M elements), 1 MI355X",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / K, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "io_dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "grouped Swish fwd+bwd, one launch per direction over 7 bf16 NHWC "
+                               "tensors at batch 32 (112^2x96, 56^2x144, 28^2x240, 14^2x480, "
+                               "14^2x672, 7^2x1152, 7^2x1280)",
+                   "tensors": count, "elements": total, "bytes_per_step": step_b,
+                   "buffer_sets": SETS},
+        "frac_peak": round(value / PEAK_HBM_GBPS, 4),
+        "fwd": {"bytes": fwd_b, "mean_us": round(gf_ms * 1e3 / K, 2),
+                "GBps": round(fwd_b / (gf_ms * 1e-3 / K) / 1e9, 1)},
+        "roofline": {"kernel": "act_group_kernel<bf16, bwd, swish> (grouped backward)",
+                     "bound": "hbm", "achieved": round(bwd_gbps, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(bwd_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "traffic_note": "counters taken for the single-tensor kernels",
+                     "bytes_per_launch": bwd_b, "mean_launch_us": round(bwd_us, 2)},
+        "single_launches_same_step": {"launches_per_step": 2 * count,
+                                      "ms_per_step": round(swall * 1e3 / K, 5),
+                                      "GBps": round(step_b * K / swall / 1e9, 1)},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import Oracle
+        orc = Oracle()
+        threads = len(os.sched_getaffinity(0))
+        c0 = time.perf_counter()
+        orc.fwd_grouped(w.xs, alpha, threads=threads)
+        orc.bwd_grouped(w.xs, w.dys, alpha, threads=threads, want_scale=False)
+        ct = time.perf_counter() - c0
+        result["cpu_baseline"] = {"value": round(step_b / ct / 1e9, 3), "unit": "GB/s",
+                                  "cores": threads, "kind": "oracle",
+                                  "sample": f"the full workload (7 tensors, {total} elements) "
+                                            f"fwd+bwd, binary64 C oracle, one run ({ct:.2f} s)"}
+    return result
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -706,6 +821,9 @@ def main():
         return
     if args.fft:
         print(json.dumps(measure_fft(args, lib, torch, dev)), flush=True)
+        return
+    if args.grouped:
+        print(json.dumps(measure_grouped(args, lib, torch, dev)), flush=True)
         return
 
     t_gen = time.perf_counter()
