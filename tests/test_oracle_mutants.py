@@ -61,6 +61,12 @@ MUTANTS = {
     "gelu_scale_drops_abs": ("m = fabs(dy) * (cdf + fabs(x) * pdf);", "m = fabs(dy) * (cdf + x * pdf);"),
     "family_nan_passthrough": ("    if (isnan(x))\n        return x;\n    switch (act) {",
                                "    switch (act) {"),
+    # Limits at +-inf (R8).
+    "swish_limit_wrong_zero_sign": ("return t > 0.0 ? x : copysign(0.0, x);", "return t > 0.0 ? x : 0.0;"),
+    "swish_grad_limit_dropped": ("    if (isinf(x)) {\n        double g = swish_grad_limit(x, dy, alpha);",
+                                 "    if (0) {\n        double g = swish_grad_limit(x, dy, alpha);"),
+    "gelu_limit_dropped": ("        if (isinf(x))  /* limits: x, and x Phi(x) -> -0 */\n            return x > 0.0 ? x : -0.0;\n",
+                           ""),
 }
 
 
