@@ -8,8 +8,11 @@ memory and in arithmetic" (Given; Step 1): bfloat16 [8, 2048, 4096] =
 
 One step = one forward launch (read x, write y) + one backward launch (read
 x and dy, write dx) through the C ABI of libmeswish.  Algorithmic bytes per
-step = 2 b n + 3 b n = 671,088,640 B (b = 2).  The timed region is K steps
-back to back between two device synchronisations; ``value`` is algorithmic
+step = 2 b n + 3 b n = 671,088,640 B (b = 2).  W untimed steps come first
+(default 500, about 50 ms): for some 20 ms after a sustained load starts,
+the GPU's clocks dip and recover, and the timed region is meant to measure
+the sustained rate.  The timed region is K steps back to back between two
+device synchronisations; ``value`` is algorithmic
 bytes over wall time, in decimal GB/s.  Four copies of the buffers are used
 in rotation so that no kernel can read its inputs from the 256 MB Infinity
 Cache: every counted byte crosses the HBM interface.
@@ -22,7 +25,8 @@ Also reported (one JSON line on stdout):
                 ``traffic`` = HBM bytes per launch from rocprofv3 counters
                 (profiles/), or null if the kernel source changed since.
   cpu_baseline  the CPU oracle (binary64 C, all host cores) on the same
-                workload, same algorithmic bytes.
+                workload, same algorithmic bytes; runs repeat until
+                --cpu-seconds (10 s) have passed, and the median run counts.
   copy_ceiling  a plain 16-byte copy kernel (read one tensor, write one).
   bytes_retained  bytes kept for the backward: x only, vs 3 maps (naive).
 
@@ -80,6 +84,17 @@ PAGE_FLOPS = {"swish": 6, "relu": 1, "leaky_relu": 2, "sigmoid": 4, "tanh": 6, "
               "gelu_tanh": 8}
 
 
+def time_cpu(run, args):
+    """Repeat run() until at least args.cpu_reps runs and args.cpu_seconds
+    of wall time; return (median seconds per run, runs, total seconds)."""
+    times = []
+    while len(times) < max(1, args.cpu_reps) or sum(times) < args.cpu_seconds:
+        c0 = time.perf_counter()
+        run()
+        times.append(time.perf_counter() - c0)
+    return statistics.median(times), len(times), sum(times)
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -88,14 +103,19 @@ def parse_args():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=500,
+                   help="untimed steps first (default 500: 25-50 ms of work, past the clock "
+                        "transient that follows the start of a sustained load)")
     p.add_argument("--act", default="swish", choices=FAMILY + ["all"],
                    help="activation to measure (default swish, the headline)")
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the CPU oracle timing (profiling runs)")
     p.add_argument("--no-extras", action="store_true",
                    help="skip the copy-ceiling measurement")
-    p.add_argument("--cpu-reps", type=int, default=3)
+    p.add_argument("--cpu-reps", type=int, default=3,
+                   help="least number of timed CPU oracle runs")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="keep repeating the CPU oracle run until this much time has passed")
     p.add_argument("--dense", action="store_true",
                    help="measure the shared-buffer DenseNet layer stage instead")
     p.add_argument("--dense-dtype", default="f32", choices=["f32", "bf16"])
@@ -262,19 +282,17 @@ def measure(args, act, rig, w, lib, torch):
         orc = oracle.Oracle()
         threads = len(os.sched_getaffinity(0))
         oname = ORACLE_NAME.get(act, act)
-        times = []
-        for _ in range(max(1, args.cpu_reps)):
-            c0 = time.perf_counter()
+        def run():
             orc.act_fwd(oname, w.xs[0], param, threads=threads)
             orc.act_bwd(oname, w.xs[0], w.dys[0], param, threads=threads, want_scale=False)
-            times.append(time.perf_counter() - c0)
-        ct = statistics.median(times)
+        ct, runs, total = time_cpu(run, args)
         result["cpu_baseline"] = {"value": round(step_b / ct / 1e9, 3), "unit": "GB/s",
                                   "cores": threads, "kind": "oracle",
                                   "sample": f"the full workload ({n} elements) fwd+bwd, binary64 C "
-                                            f"oracle, median of {len(times)} runs ({ct:.2f} s each)",
+                                            f"oracle, median of {runs} runs ({ct:.2f} s each, "
+                                            f"{total:.1f} s in all)",
                                   "elements_per_s": round(n / ct, 1)}
-        log(f"[bench] {act}: cpu baseline {ct:.2f} s with {threads} threads")
+        log(f"[bench] {act}: cpu baseline {ct:.2f} s x {runs} with {threads} threads")
     return result
 
 
@@ -474,17 +492,18 @@ def measure_dense(args, lib, torch, dev):
         from memory_efficient_activation_amd import inputs
         srcs = [inputs.decode(s_).astype(np.float64) for s_ in w.sources]
         dz64 = inputs.decode(w.dz).astype(np.float64)
-        c0 = time.perf_counter()
-        dense_oracle.forward(srcs, w.gamma, w.beta, eps)
-        dense_oracle.backward(srcs, dz64, w.gamma, w.beta, eps)
-        ct = time.perf_counter() - c0
+        def run():
+            dense_oracle.forward(srcs, w.gamma, w.beta, eps)
+            dense_oracle.backward(srcs, dz64, w.gamma, w.beta, eps)
+        ct, runs, total = time_cpu(run, args)
         # The oracle's backward recomputes the forward, as the method does:
         # count the same bytes as one GPU step without the statistics pass.
         cb = 2 * fwd_b + bwd_b
         result["cpu_baseline"] = {"value": round(cb / ct / 1e9, 3), "unit": "GB/s", "cores": 1,
                                   "kind": "oracle",
                                   "sample": f"the full layer ({C} x {n * hw} elements), numpy "
-                                            f"binary64 forward + backward, one run ({ct:.2f} s)"}
+                                            f"binary64 forward + backward, median of {runs} runs "
+                                            f"({ct:.2f} s each, {total:.1f} s in all)"}
         log(f"[bench] dense: cpu baseline {ct:.2f} s")
     return result
 
@@ -672,18 +691,25 @@ def measure_fft(args, lib, torch, dev):
     if not args.no_cpu_baseline:
         import numpy as np
         from oracle import fft_oracle
-        sub = 2
-        c0 = time.perf_counter()
-        fft_oracle.fprop_fft(L.x[:sub], L.w)
-        fft_oracle.bprop_fft(L.g[:sub], L.w, n)
-        fft_oracle.accgrad_fft(L.x[:sub], L.g[:sub], k)
-        ct = time.perf_counter() - c0
+        # Runs over successive pairs of minibatch samples, each a layer step
+        # on 2 of the S samples, until the time bound; scaled to all S.
+        sub, pos = 2, [0]
+
+        def run():
+            lo = pos[0] % S
+            pos[0] += sub
+            fft_oracle.fprop_fft(L.x[lo:lo + sub], L.w)
+            fft_oracle.bprop_fft(L.g[lo:lo + sub], L.w, n)
+            fft_oracle.accgrad_fft(L.x[lo:lo + sub], L.g[lo:lo + sub], k)
+        ct, runs, total = time_cpu(run, args)
         est_ms = ct * 1e3 * S / sub
         result["cpu_baseline"] = {"value": round(1e3 / est_ms, 4), "unit": "layer steps/s",
                                   "cores": 1, "kind": "oracle",
-                                  "sample": f"{sub} of the {S} minibatch samples, numpy binary64 "
-                                            f"spectral path, {ct:.2f} s, scaled by {S // sub}"}
-        log(f"[bench] fft: cpu baseline {ct:.2f} s for {sub} samples")
+                                  "sample": f"{runs} runs over {sub} of the {S} minibatch samples "
+                                            f"each, numpy binary64 spectral path, median "
+                                            f"{ct:.2f} s per run ({total:.1f} s in all), "
+                                            f"scaled by {S // sub}"}
+        log(f"[bench] fft: cpu baseline {ct:.2f} s per {sub} samples x {runs}")
         del np
     return result
 
@@ -786,14 +812,15 @@ def measure_grouped(args, lib, torch, dev):
         from oracle import Oracle
         orc = Oracle()
         threads = len(os.sched_getaffinity(0))
-        c0 = time.perf_counter()
-        orc.fwd_grouped(w.xs, alpha, threads=threads)
-        orc.bwd_grouped(w.xs, w.dys, alpha, threads=threads, want_scale=False)
-        ct = time.perf_counter() - c0
+        def run():
+            orc.fwd_grouped(w.xs, alpha, threads=threads)
+            orc.bwd_grouped(w.xs, w.dys, alpha, threads=threads, want_scale=False)
+        ct, runs, spent = time_cpu(run, args)
         result["cpu_baseline"] = {"value": round(step_b / ct / 1e9, 3), "unit": "GB/s",
                                   "cores": threads, "kind": "oracle",
                                   "sample": f"the full workload (7 tensors, {total} elements) "
-                                            f"fwd+bwd, binary64 C oracle, one run ({ct:.2f} s)"}
+                                            f"fwd+bwd, binary64 C oracle, median of {runs} runs "
+                                            f"({ct:.2f} s each, {spent:.1f} s in all)"}
     return result
 
 

@@ -4,6 +4,7 @@ Usage (after the rocprofv3 runs listed in each summary's header):
 
     python -m memory_efficient_activation_amd.rocprof_summary trace DIR
     python -m memory_efficient_activation_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR
+    python -m memory_efficient_activation_amd.rocprof_summary timeline DIR [WINDOW]
     python -m memory_efficient_activation_amd.rocprof_summary dense-trace DIR f32|bf16
     python -m memory_efficient_activation_amd.rocprof_summary dense-traffic FETCH_DIR WRITE_DIR f32|bf16
     python -m memory_efficient_activation_amd.rocprof_summary fft-trace DIR
@@ -20,6 +21,9 @@ Usage (after the rocprofv3 runs listed in each summary's header):
             ``bytes`` = 2 b n per launch), and prints the HBM bytes per
             launch of the forward and backward kernels next to their
             algorithmic bytes, with the sha256 of the kernel source.
+``timeline`` the kernel times of a ``trace`` run (or of a ``--pmc
+            GRBM_GUI_ACTIVE`` run, then with the counter's cycles per
+            microsecond) in windows of consecutive launches, in run order.
 ``dense-*`` the same for ``bench.py --dense`` (DenseNet-BC-100 block 1,
             layer 16: 204 channels of 64 x 32 x 32; its newest source has 12):
             forward 2 C M b bytes per launch, backward reduction 2 C M b,
@@ -124,6 +128,72 @@ def trace(d: str) -> str:
             t = statistics.fmean(d_)
             out.append(f"| {k} only, back to back | {len(d_)} | {t / 1e3:.2f} | "
                        f"{ALGO[base] / t:.0f} |")
+    return "\n".join(out)
+
+
+def timeline(d: str, window: int = 10) -> str:
+    """Kernel times through the run, in windows of `window` launches of one
+    kind: whether a kernel keeps its speed over a long stretch of launches.
+    With a directory of a ``--pmc GRBM_GUI_ACTIVE`` run instead of a kernel
+    trace, each window also gives the counter's cycles per microsecond of
+    kernel time."""
+    trace_csv = glob.glob(os.path.join(d, "*_kernel_trace.csv"))
+    cycles = {}
+    if trace_csv:
+        rows = list(csv.DictReader(open(_one(os.path.join(d, "*_kernel_trace.csv")))))
+    else:
+        rows = [r for r in csv.DictReader(open(_one(os.path.join(d, "*_counter_collection.csv"))))
+                if r["Counter_Name"] == "GRBM_GUI_ACTIVE"]
+        cycles = {r["Dispatch_Id"]: float(r["Counter_Value"]) for r in rows}
+    seq = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r.get("Dispatch_Id", ""),
+                  kind(r["Kernel_Name"], act_of(r["Kernel_Name"]) or "swish"),
+                  act_of(r["Kernel_Name"])) for r in rows)
+    seq = [x for x in seq if x[3] in ALGO]
+    if not seq:
+        return "(no activation or copy kernels)"
+    t0 = seq[0][0]
+
+    def region(i):
+        # "fwd/bwd" inside the alternating steps (a neighbour of the other
+        # kind and, one further, one of the same), else the launch's own kind.
+        act, k = seq[i][4], seq[i][3]
+
+        def at(j):
+            return seq[j][3] if 0 <= j < len(seq) and seq[j][4] == act else None
+        for d_ in (-1, 1):
+            if k != "copy" and at(i + d_) not in (None, k) and at(i + 2 * d_) == k:
+                return "fwd/bwd"
+        return k
+    regions = [region(i) for i in range(len(seq))]
+    head = "| window | launches | starts at (ms) | fwd (us) | bwd (us) | copy (us) | GB/s |"
+    if cycles:
+        head += " cycles per us |"
+    out = [head, "|" + "---|" * (head.count("|") - 1)]
+    i = 0
+    while i < len(seq):
+        a, reg = seq[i][4] or "copy", regions[i]
+        j = i
+        # A window: up to `window` consecutive launches (steps, when
+        # alternating) of one activation in one region of the run.
+        limit = 2 * window if reg == "fwd/bwd" else window
+        while (j < len(seq) and (seq[j][4] or "copy") == a and regions[j] == reg
+               and j - i < limit):
+            j += 1
+        w = seq[i:j]
+        mean = {}
+        for k in ("fwd", "bwd", "copy"):
+            d_ = [e - s for s, e, _, kk, _ in w if kk == k]
+            mean[k] = statistics.fmean(d_) / 1e3 if d_ else None
+        tot_b = sum(ALGO[kk] for _, _, _, kk, _ in w)
+        tot_t = sum(e - s for s, e, _, _, _ in w)
+        cells = [f"{a} {reg}" if a != "copy" else a, f"{len(w)}", f"{(w[0][0] - t0) / 1e6:.2f}"]
+        cells += [f"{mean[k]:.1f}" if mean[k] is not None else "" for k in ("fwd", "bwd", "copy")]
+        cells.append(f"{tot_b / tot_t:.0f}")
+        if cycles:
+            cyc = sum(cycles.get(x[2], 0.0) for x in w)
+            cells.append(f"{cyc / (tot_t / 1e3):.0f}")
+        out.append("| " + " | ".join(cells) + " |")
+        i = j
     return "\n".join(out)
 
 
@@ -351,6 +421,8 @@ def main(argv):
         print(dense_trace(argv[1], argv[2]))
     elif len(argv) >= 4 and argv[0] == "dense-traffic":
         print(dense_traffic(argv[1], argv[2], argv[3]))
+    elif len(argv) >= 2 and argv[0] == "timeline":
+        print(timeline(argv[1], int(argv[2]) if len(argv) >= 3 else 10))
     elif len(argv) >= 2 and argv[0] == "fft-trace":
         print(fft_trace(argv[1]))
     elif len(argv) >= 3 and argv[0] == "fft-traffic":
