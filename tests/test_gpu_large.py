@@ -14,8 +14,12 @@ with a few planted values next to 2^31 and in the ragged tail.  The samples
 are the first elements, the neighbourhoods of 2^30 and 2^31, the last
 elements and 200,000 uniform indices; the oracle computes each of them from
 the sampled input.
+
+The DenseNet stage gets the same treatment: a source and a shared map past
+2^31 elements, with sampled channels checked against its binary64 oracle.
 """
 
+import numpy as np
 import pytest
 import torch
 
@@ -124,3 +128,106 @@ def test_f32_past_8_gib(oracle):
     dx = mea.swish_bwd(x, dy, 1.5)
     torch.cuda.synchronize()
     _check(x, dy, y, dx, 1.5, oracle, "f32")
+
+
+def test_dense_stage_past_2_31_elements(oracle):
+    """The DenseNet stage (include/dense_bn.h) on two binary32 sources of 1040
+    and 24 channels, n = 2 rows of hw = 2^20 each: the first source holds
+    2,181,038,080 elements, the shared map z 2,231,369,728 (both past 2^31,
+    8.7 and 8.9 GB).  Per channel there are 2^21 elements, inside the stage's
+    limit.  Seven channels at the ends and middle of both sources are checked
+    against the binary64 oracle: statistics, z, dx, dgamma, dbeta (channels
+    are independent, so the oracle takes them as one small layer)."""
+    from memory_efficient_activation_amd import dense
+    from oracle import dense_oracle as do
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(31)
+    n, hw, chans = 2, 1 << 20, (1040, 24)
+    say(f"[large] dense stage: sources {chans} x n={n} x hw={hw}, binary32")
+    xs = []
+    for c in chans:
+        off = torch.randn(c, device=dev, generator=g)
+        sc = torch.rand(c, device=dev, generator=g) * 1.5 + 0.5
+        x = torch.empty((n, c, hw), device=dev)
+        x.normal_(generator=g)
+        x.mul_(sc[None, :, None]).add_(off[None, :, None])
+        xs.append(x)
+    total = sum(chans)
+    gamma = 1.0 + 0.25 * torch.randn(total, device=dev, generator=g)
+    beta = 0.5 * torch.randn(total, device=dev, generator=g)
+    dz = torch.empty((n, total, hw), device=dev)
+    dz.normal_(generator=g)
+    eps = dense.EPS
+    stats = [dense.bn_stats(x) for x in xs]
+    z = dense.bn_relu_fwd(xs, stats, gamma, beta, eps)
+    dxs, dg, db = dense.bn_relu_bwd(xs, stats, gamma, beta, dz, eps)
+    torch.cuda.synchronize()
+
+    picks = [(0, 0), (0, 1), (0, 517), (0, 1038), (0, 1039), (1, 0), (1, 23)]
+    zc = [sum(chans[:j]) + c for j, c in picks]
+    src = np.stack([to_host(xs[j][:, c, :]).astype(np.float64) for j, c in picks], axis=1)
+    g64 = to_host(gamma)[zc].astype(np.float64)
+    b64 = to_host(beta)[zc].astype(np.float64)
+    dz64 = np.stack([to_host(dz[:, c, :]).astype(np.float64) for c in zc], axis=1)
+    zo, f = do.forward([src], g64, b64, eps)
+    duo, dgo, dbo, aux = do.backward([src], dz64, g64, b64, eps)
+
+    mean = np.array([to_host(stats[j][c, 0]) for j, c in picks])
+    var = np.array([to_host(stats[j][c, 1]) for j, c in picks])
+    mean_err = float((np.abs(mean - f["mean"]) / (np.abs(f["mean"]) + np.sqrt(f["var"]))).max())
+    var_err = float((np.abs(var - f["var"]) / f["var"]).max())
+    say(f"[large] dense stats: mean {mean_err:.2e}, var {var_err:.2e}")
+    assert mean_err <= 1e-12 and var_err <= 1e-10
+
+    zg = np.stack([to_host(z[:, c, :]) for c in zc], axis=1)
+    rz = f32_report(zg, oracle.round_array(zo, "f32"), f["scale"], 1e-5)
+    dxg = np.stack([to_host(dxs[j][:, c, :]) for j, c in picks], axis=1)
+    rdx = f32_report(dxg, oracle.round_array(duo[0], "f32"), aux["du_scale"][0], 1e-5)
+    rdg = f32_report(to_host(dg)[zc], dgo.astype(np.float32), aux["dgamma_scale"], 1e-5)
+    rdb = f32_report(to_host(db)[zc], dbo.astype(np.float32), aux["dbeta_scale"], 1e-5)
+    say(f"[large] dense z {rz['max_rel']:.2e}, dx {rdx['max_rel']:.2e}, "
+        f"dgamma {rdg['max_rel']:.2e}, dbeta {rdb['max_rel']:.2e}")
+    for r in (rz, rdx, rdg, rdb):
+        assert r["ok"], r
+
+
+def test_fft_transforms_near_the_size_limit():
+    """FFT convolution's transforms (include/fft_conv.h) at the size limit:
+    3,900,000 maps of 32 x 32 (15.6 GB) give half spectra of 2,121,600,000
+    complex values (17 GB, bin-major), just under the limit of 2^31 per
+    spectrum array, so offsets run past byte 2^34.  Sampled maps are checked
+    against the oracle's transform (numpy FFT of the map); every map must come
+    back from the inverse (the round trip, a property at any size) to within
+    1e-5 of its norm."""
+    from memory_efficient_activation_amd import fft
+    from oracle import fft_oracle as fo_
+
+    dev = torch.device("cuda:0")
+    B, n = 3_900_000, 32
+    say(f"[large] fft: r2c + c2r of {B} maps of {n} x {n}, {fft.bins(n) * B} bins")
+    g = torch.Generator(device=dev)
+    g.manual_seed(37)
+    x = torch.empty((B, n, n), device=dev)
+    x.normal_(generator=g)
+    spec = fft.r2c(x, n)
+    torch.cuda.synchronize()
+    idx = torch.cat([torch.tensor([0, 1, 2, B // 2, B - 3, B - 2, B - 1]),
+                     torch.randint(0, B, (40,), generator=torch.Generator().manual_seed(3))])
+    xs = to_host(x[idx.to(dev)]).astype(np.float64)
+    got = to_host(spec[:, idx.to(dev)]).astype(np.complex128)           # [P, k]
+    want = fo_.rfft2_half(xs, n).reshape(len(idx), -1).T
+    err = float((np.abs(got - want).max(0) / fo_.spectrum_scale(xs, n)).max())
+    say(f"[large] fft r2c, sampled maps: max err / (n ||x||) = {err:.2e}")
+    assert err <= 1e-5
+
+    y = fft.c2r(spec, n, n, 1.0 / (n * n))
+    del spec
+    worst = 0.0
+    for c0 in range(0, B, 500_000):
+        xc, yc = x[c0:c0 + 500_000], y[c0:c0 + 500_000]
+        d = (yc - xc).abs().amax(dim=(1, 2)) / xc.norm(dim=(1, 2))
+        worst = max(worst, float(d.max()))
+    say(f"[large] fft round trip, all maps: max |y - x| / ||x|| = {worst:.2e}")
+    assert worst <= 1e-5
