@@ -5,6 +5,7 @@ Usage (after the rocprofv3 runs listed in each summary's header):
     python -m memory_efficient_activation_amd.rocprof_summary trace DIR
     python -m memory_efficient_activation_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR
     python -m memory_efficient_activation_amd.rocprof_summary timeline DIR [WINDOW]
+    python -m memory_efficient_activation_amd.rocprof_summary grouped-trace DIR [STEPS]
     python -m memory_efficient_activation_amd.rocprof_summary dense-trace DIR f32|bf16
     python -m memory_efficient_activation_amd.rocprof_summary dense-traffic FETCH_DIR WRITE_DIR f32|bf16
     python -m memory_efficient_activation_amd.rocprof_summary fft-trace DIR
@@ -24,6 +25,9 @@ Usage (after the rocprofv3 runs listed in each summary's header):
 ``timeline`` the kernel times of a ``trace`` run (or of a ``--pmc
             GRBM_GUI_ACTIVE`` run, then with the counter's cycles per
             microsecond) in windows of consecutive launches, in run order.
+``grouped-trace`` the kernel times of ``bench.py --grouped``: the grouped
+            kernels in the timed steps and back to back, and the step as
+            fourteen single launches.
 ``dense-*`` the same for ``bench.py --dense`` (DenseNet-BC-100 block 1,
             layer 16: 204 channels of 64 x 32 x 32; its newest source has 12):
             forward 2 C M b bytes per launch, backward reduction 2 C M b,
@@ -194,6 +198,71 @@ def timeline(d: str, window: int = 10) -> str:
             cells.append(f"{cyc / (tot_t / 1e3):.0f}")
         out.append("| " + " | ".join(cells) + " |")
         i = j
+    return "\n".join(out)
+
+
+GROUPED_ELEMS = 70_045_696   # the seven EfficientNet-shaped tensors of the grouped bench
+
+
+def grouped_trace(d: str, steps: int = 200) -> str:
+    """``bench.py --grouped``: the grouped kernels in the timed alternating
+    steps (the last `steps` of them), back to back, and the same step as
+    fourteen single launches."""
+    stats = list(csv.DictReader(open(_one(os.path.join(d, "*_kernel_stats.csv")))))
+    rows = list(csv.DictReader(open(_one(os.path.join(d, "*_kernel_trace.csv")))))
+    out = ["| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+    for r in stats:
+        out.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+
+    def lab(name):
+        m = re.search(r"act_(group|vec)_kernel<meswish::bf16_t, (true|false), 0>", name)
+        if not m:
+            return None
+        return ("g" if m.group(1) == "group" else "s") + ("b" if m.group(2) == "true" else "f")
+    seq = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), lab(r["Kernel_Name"]))
+                 for r in rows)
+    seq = [x for x in seq if x[2]]
+    kinds = [k for _, _, k in seq]
+    fb = {"f": 4 * GROUPED_ELEMS, "b": 6 * GROUPED_ELEMS}
+    out += ["", "| region | launches | mean kernel time (us) | algorithmic GB/s |",
+            "|---|---|---|---|"]
+    # Alternating grouped steps: the longest run of gf/gb pairs; its last
+    # `steps` steps are the timed ones.
+    best, i = (0, 0), 0
+    while i < len(kinds):
+        j = i
+        while j < len(kinds) and kinds[j] == ("gf" if (j - i) % 2 == 0 else "gb"):
+            j += 1
+        if j - i > best[1] - best[0]:
+            best = (i, j)
+        i = max(j, i + 1)
+    seg = seq[max(best[0], best[1] - 2 * steps):best[1]]
+    for k in ("gf", "gb"):
+        d_ = [e - s_ for s_, e, kk in seg if kk == k]
+        t = statistics.fmean(d_)
+        out.append(f"| grouped {'forward' if k == 'gf' else 'backward'}, timed alternating steps "
+                   f"| {len(d_)} | {t / 1e3:.2f} | {fb[k[1]] / t:.0f} |")
+    for k, name in (("gb", "grouped backward only, back to back"),
+                    ("gf", "grouped forward only, back to back")):
+        runs, cur = [], []
+        for x in seq[best[1]:]:
+            if x[2] == k:
+                cur.append(x)
+            elif cur:
+                runs.append(cur)
+                cur = []
+        if cur:
+            runs.append(cur)
+        r_ = max(runs, key=len)
+        t = statistics.fmean(e - s_ for s_, e, _ in r_)
+        out.append(f"| {name} | {len(r_)} | {t / 1e3:.2f} | {fb[k[1]] / t:.0f} |")
+    single = [x for x in seq if x[2] in ("sf", "sb")]
+    if single:
+        n_steps = len(single) // 14
+        t = sum(e - s_ for s_, e, _ in single) / max(n_steps, 1)
+        out.append(f"| single launches, 14 per step (kernel time per step) | {len(single)} | "
+                   f"{t / 1e3:.2f} | {(fb['f'] + fb['b']) / t:.0f} |")
     return "\n".join(out)
 
 
@@ -421,6 +490,8 @@ def main(argv):
         print(dense_trace(argv[1], argv[2]))
     elif len(argv) >= 4 and argv[0] == "dense-traffic":
         print(dense_traffic(argv[1], argv[2], argv[3]))
+    elif len(argv) >= 2 and argv[0] == "grouped-trace":
+        print(grouped_trace(argv[1], int(argv[2]) if len(argv) >= 3 else 200))
     elif len(argv) >= 2 and argv[0] == "timeline":
         print(timeline(argv[1], int(argv[2]) if len(argv) >= 3 else 10))
     elif len(argv) >= 2 and argv[0] == "fft-trace":
