@@ -251,7 +251,7 @@ struct TanhOp {
     static constexpr bool kHasRare = true;
 
     template <bool P>
-    __device__ static float fwd(float x, const Coef& k, bool& rare)
+    __device__ static float fwd(float x, const Coef& k, bool& /*rare: the forward has none*/)
     {
         float a = fabsf(x);
         float v;

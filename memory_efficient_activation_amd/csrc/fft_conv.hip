@@ -833,7 +833,8 @@ static int launch_cmul(int op, const float2* a, const float2* b, float2* c, int 
     } else {
         M = fo; N = f; K = S; sAp = (int64_t)S * fo; sBp = (int64_t)S * f; lda = fo; ldb = f;
     }
-    const int tiles_n = (N + kBN - 1) / kBN, tiles_m = (M + kBM - 1) / kBM;
+    [[maybe_unused]] const int tiles_n = (N + kBN - 1) / kBN;
+    const int tiles_m = (M + kBM - 1) / kBM;
 #if FFTCONV_MFMA == 2
     // 32-column block tiles where they pad less than 64-column ones.
 #ifndef FFTCONV_PLANAR_WC

@@ -436,9 +436,9 @@ __global__ MESWISH_BOUNDS void act_group_kernel(GroupArgs g, Coef k)
         body_tile<IO, kBwd, ACT>(reinterpret_cast<const uint4*>(x + head),
                             kBwd ? reinterpret_cast<const uint4*>(dy + head) : nullptr,
                             reinterpret_cast<uint4*>(out + head), local * kTileVecs, nvec, k);
-        if (local == 0 && threadIdx.x < head + tail) {
-            int64_t i = threadIdx.x < head ? (int64_t)threadIdx.x
-                                           : head + nvec * E + (threadIdx.x - head);
+        const int64_t t = threadIdx.x;  // head >= 0 here
+        if (local == 0 && t < head + tail) {
+            int64_t i = t < head ? t : head + nvec * E + (t - head);
             one_element<IO, kBwd, ACT>(x, dy, out, i, k);
         }
     }

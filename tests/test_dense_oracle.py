@@ -1,7 +1,6 @@
 """The DenseNet-layer oracle against its pins, and planted mistakes that the
 pins must catch (CPU only)."""
 
-import importlib.util
 import os
 import types
 

@@ -6,7 +6,6 @@ flags into a temporary library.  The pins of ``pins.py`` run against it; at
 least one must fail.  The mistakes are planted in the oracle, on the CPU only.
 """
 
-import os
 
 import pytest
 
