@@ -5,6 +5,7 @@ Usage (after the rocprofv3 runs listed in each summary's header):
     python -m memory_efficient_activation_amd.rocprof_summary trace DIR
     python -m memory_efficient_activation_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR
     python -m memory_efficient_activation_amd.rocprof_summary timeline DIR [WINDOW]
+    python -m memory_efficient_activation_amd.rocprof_summary valu DIR
     python -m memory_efficient_activation_amd.rocprof_summary grouped-trace DIR [STEPS]
     python -m memory_efficient_activation_amd.rocprof_summary dense-trace DIR f32|bf16
     python -m memory_efficient_activation_amd.rocprof_summary dense-traffic FETCH_DIR WRITE_DIR f32|bf16
@@ -25,6 +26,8 @@ Usage (after the rocprofv3 runs listed in each summary's header):
 ``timeline`` the kernel times of a ``trace`` run (or of a ``--pmc
             GRBM_GUI_ACTIVE`` run, then with the counter's cycles per
             microsecond) in windows of consecutive launches, in run order.
+``valu``    vector-ALU counters of ``bench.py --act all`` per kernel: VALUBusy
+            and vector instructions per element.
 ``grouped-trace`` the kernel times of ``bench.py --grouped``: the grouped
             kernels in the timed steps and back to back, and the step as
             fourteen single launches.
@@ -266,6 +269,37 @@ def grouped_trace(d: str, steps: int = 200) -> str:
     return "\n".join(out)
 
 
+def valu(d: str) -> str:
+    """A ``--pmc VALUBusy SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 SQ_WAVES`` run
+    of ``bench.py --act all``: per kernel, the mean kernel time, VALUBusy
+    (rocprofv3's derived metric: percent of GPU time the vector ALUs are
+    issuing) and vector instructions per element (per-lane instructions:
+    SQ_INSTS_VALU counts wavefront instructions of 64 lanes)."""
+    rows = list(csv.DictReader(open(_one(os.path.join(d, "*_counter_collection.csv")))))
+    agg = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        k = kind(name, act_of(name) or "swish")
+        if k not in ALGO:
+            continue
+        key = (act_of(name) or "copy", k)
+        x = agg.setdefault(key, {}).setdefault(r["Dispatch_Id"], {
+            "dur": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+        x[r["Counter_Name"]] = float(r["Counter_Value"])
+    out = ["| kernel | launches | mean time (us) | VALUBusy (%) | vector instructions per "
+           "element | of which transcendental |", "|---|---|---|---|---|---|"]
+    for (a, k), v in agg.items():
+        ds = list(v.values())
+
+        def mean(c):
+            return statistics.fmean(x[c] for x in ds)
+        label = "copy" if a == "copy" else f"{a} {k}"
+        out.append(f"| {label} | {len(ds)} | {mean('dur'):.1f} | {mean('VALUBusy'):.1f} | "
+                   f"{mean('SQ_INSTS_VALU') * 64 / N:.2f} | "
+                   f"{mean('SQ_INSTS_VALU_TRANS_F32') * 64 / N:.2f} |")
+    return "\n".join(out)
+
+
 def _counter(d: str, name: str) -> dict:
     rows = list(csv.DictReader(open(_one(os.path.join(d, "*_counter_collection.csv")))))
     acc: dict = {}
@@ -492,6 +526,8 @@ def main(argv):
         print(dense_traffic(argv[1], argv[2], argv[3]))
     elif len(argv) >= 2 and argv[0] == "grouped-trace":
         print(grouped_trace(argv[1], int(argv[2]) if len(argv) >= 3 else 200))
+    elif len(argv) >= 2 and argv[0] == "valu":
+        print(valu(argv[1]))
     elif len(argv) >= 2 and argv[0] == "timeline":
         print(timeline(argv[1], int(argv[2]) if len(argv) >= 3 else 10))
     elif len(argv) >= 2 and argv[0] == "fft-trace":

@@ -82,3 +82,19 @@ def test_grouped_trace_regions(tmp_path):
 def test_one_file_per_pattern(tmp_path):
     with pytest.raises(SystemExit):
         rs.timeline(str(tmp_path))
+
+
+def test_valu_table(tmp_path):
+    names = {"fwd": FWD, "bwd": BWD}
+    with open(tmp_path / "valu_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
+                    "Start_Timestamp", "End_Timestamp"])
+        n = rs.N
+        for i, (k, busy, per) in enumerate([("fwd", 30.0, 9), ("bwd", 40.0, 15), ("bwd", 50.0, 15)]):
+            for c, v in (("VALUBusy", busy), ("SQ_INSTS_VALU", per * n / 64),
+                         ("SQ_INSTS_VALU_TRANS_F32", 2 * n / 64), ("SQ_WAVES", n / 512)):
+                w.writerow([i + 1, names[k], c, v, 0, 60_000])
+    rows = {r[0]: r for r in _rows(rs.valu(str(tmp_path)))}
+    assert rows["swish fwd"][1:] == ["1", "60.0", "30.0", "9.00", "2.00"]
+    assert rows["swish bwd"][1:] == ["2", "60.0", "45.0", "15.00", "2.00"]
