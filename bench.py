@@ -509,8 +509,8 @@ def measure_dense(args, lib, torch, dev):
 
 
 # Dense binary32 matrix-core (MFMA) throughput of MI355X, AMD's published
-# figure.  (The vector ALUs without packed instructions, which this build
-# disables, give 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz = 78.6.)
+# figure.  (The vector ALUs without packed instructions, which the library's
+# compile flags disable, give 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz = 78.6.)
 PEAK_FP32_MFMA_TFLOPS = 157.3
 
 
@@ -828,9 +828,9 @@ def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the Swish path is element-wise and would shard "
-              "with no communication (each GPU runs its local tensor); multi-GPU runs are not "
-              "part of this build. Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the Swish path is element-wise and shards "
+              "with no communication (each GPU runs on its local tensor), so the one-GPU "
+              "figure times N is the N-GPU figure. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
