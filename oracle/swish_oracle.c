@@ -26,7 +26,7 @@
  *   [P3] "What activations cost, in memory and in arithmetic", Step 1 and
  *        Step 2: element counts and bytes of one activation tensor.
  *
- * Readings where the pages leave a step open (each is listed in the design doc):
+ * Readings where the pages leave a step open:
  *   - alpha in the backward: the memory-efficient code is written for
  *     alpha = 1.  For general alpha the product rule applied to
  *     x * Sigmoid(alpha x) gives s + alpha x s (1 - s) = s (1 + t (1 - s))
