@@ -60,7 +60,7 @@ MUTANTS = {
     "gelu_scale_drops_abs": ("m = fabs(dy) * (cdf + fabs(x) * pdf);", "m = fabs(dy) * (cdf + x * pdf);"),
     "family_nan_passthrough": ("    if (isnan(x))\n        return x;\n    switch (act) {",
                                "    switch (act) {"),
-    # Limits at +-inf (R8).
+    # Limits at +-inf: the value as x -> +-inf with the parameter fixed.
     "swish_limit_wrong_zero_sign": ("return t > 0.0 ? x : copysign(0.0, x);", "return t > 0.0 ? x : 0.0;"),
     "swish_grad_limit_dropped": ("    if (isinf(x)) {\n        double g = swish_grad_limit(x, dy, alpha);",
                                  "    if (0) {\n        double g = swish_grad_limit(x, dy, alpha);"),
