@@ -261,3 +261,28 @@ def test_fft_alias_rejections_without_gpu(lib):
                              None) == _lib.EALIAS
     # Stage calls: spectrum output over the input maps.
     assert lib.fftconv_r2c(g, 4, 8, 8, g + 64, None) == _lib.EALIAS
+
+
+def test_fft_size_limits(lib):
+    """fftconv_*: every spectrum array below 2^31 complex values and every map
+    count below 2^31, else EINVAL before any launch (checked without a GPU)."""
+    from memory_efficient_activation_amd import _lib
+    g = 0x10000000
+    bins32 = 32 * 17
+    at_limit = (1 << 31) // bins32 + 1                  # first batch with batch * bins >= 2^31
+    assert (at_limit - 1) * bins32 < (1 << 31) <= at_limit * bins32
+    assert lib.fftconv_r2c(g, at_limit, 32, 32, g + (1 << 36), None) == _lib.EINVAL
+    assert lib.fftconv_c2r(g, at_limit, 32, 32, 1.0, g + (1 << 36), None) == _lib.EINVAL
+    # Layer sizes whose S f spectra reach 2^31 values: no buffer size, and EINVAL.
+    S, f = 1 << 16, at_limit // (1 << 16) + 1
+    assert lib.fftconv_buffer_bytes(S, f, 1, 32) == 0
+    f_ok = ((1 << 31) - 1) // (S * bins32)              # largest f under the limit
+    assert lib.fftconv_buffer_bytes(S, f_ok, 1, 32) == (S * f_ok + S + f_ok) * bins32 * 8
+    assert lib.fftconv_fprop(g, g + 4096, g + 8192, S, f, 1, 32, 3, g + (1 << 36), 1 << 40,
+                             None) == _lib.EINVAL
+    # Per-bin products: at most 65535 bins per call.
+    assert lib.fftconv_cmul(0, g, g + 4096, g + 8192, 2, 2, 2, 65536, None) == _lib.EINVAL
+    # Misaligned real input (16 bytes required) or spectrum (8 bytes).
+    assert lib.fftconv_r2c(g + 4, 4, 8, 8, g + (1 << 20), None) == _lib.EINVAL
+    assert lib.fftconv_r2c(g, 4, 8, 8, g + (1 << 20) + 4, None) == _lib.EINVAL
+    assert lib.fftconv_c2r(g + 4, 4, 8, 8, 1.0, g + (1 << 20), None) == _lib.EINVAL
