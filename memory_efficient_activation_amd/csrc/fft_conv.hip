@@ -628,9 +628,10 @@ __global__ __launch_bounds__(kThreads) void cgemm_mfma_kernel(const float2* __re
 // as four v_mfma_f32_32x32x2f32 on accumulators acc_re, acc_im; no
 // per-lane selects, a third of the LDS bytes of the interleaved form.  Lane
 // l supplies A[row l%32][k l/32] and B[k l/32][col l%32] of the pair.
-// Block tile: 64 rows x 32 WC columns, 2 WC waves of 32 x 32 each.  WC = 2
+// Block tile: 32 WR rows x 32 WC columns, WR WC waves of 32 x 32 each.  WC = 2
 // in general; WC = 1 where 64-column tiles would pad the product (96
-// columns take 3 tiles of 32 instead of 2 of 64, a quarter of them empty).
+// columns take 3 tiles of 32 instead of 2 of 64, a quarter of them empty),
+// and then WR = 4 where 128-row tiles pad no more than 64-row ones.
 // (Two column subtiles per wave, reusing A, measured slower: 178 VGPRs.)
 // Complex k per K-tile of the planar kernel: 8 measured fastest on the
 // measured layer (16: +2 %, 32: +6 %, registers 174-226).  Two LDS buffers
@@ -650,10 +651,16 @@ constexpr int kPK = FFTCONV_PLANAR_KT;
 #ifndef FFTCONV_PLANAR_WPE2
 #define FFTCONV_PLANAR_WPE2 1
 #endif
+// 128 x 32 tiles (four waves of 32 x 32 in a column) for the 32-column
+// products: 17 % fewer operand bytes per output than 64 x 32 tiles of two
+// waves, 5-8 % faster input- and weight-gradient products.
+#ifndef FFTCONV_PLANAR_WR4
+#define FFTCONV_PLANAR_WR4 1
+#endif
 
 
-template <bool AK, bool BK, bool CA, bool CB, int WC>
-__global__ __launch_bounds__(128 * WC, WC == 1 ? FFTCONV_PLANAR_WPE1 : FFTCONV_PLANAR_WPE2)
+template <bool AK, bool BK, bool CA, bool CB, int WC, int WR = 2>
+__global__ __launch_bounds__(64 * WR * WC, WR * WC == 2 ? FFTCONV_PLANAR_WPE1 : FFTCONV_PLANAR_WPE2)
 void cgemm_planar_kernel(const float2* __restrict__ A,
                                                                const float2* __restrict__ B,
                                                                float2* __restrict__ C, int M,
@@ -661,18 +668,20 @@ void cgemm_planar_kernel(const float2* __restrict__ A,
                                                                int64_t sBp, int lda, int ldb,
                                                                int tiles_n, int tiles, int nbins)
 {
-    constexpr int NT = 128 * WC;        // threads
+    constexpr int NT = 64 * WR * WC;    // threads
+    constexpr int BM = 32 * WR;         // block tile rows
     constexpr int BN = 32 * WC;         // block tile columns
-    constexpr int LA = kBM * kPK / NT;  // A values per thread per K-tile
+    constexpr int LA = BM * kPK / NT;   // A values per thread per K-tile
     constexpr int LB = BN * kPK / NT;   // B values per thread per K-tile
-    __shared__ float Ar[kPK][kBM + 4], Ai[kPK][kBM + 4];
+    static_assert(LA * NT == BM * kPK && LB * NT == BN * kPK, "whole values per thread");
+    __shared__ float Ar[kPK][BM + 4], Ai[kPK][BM + 4];
     __shared__ float Br[kPK][BN + 4], Bi[kPK][BN + 4];
     const int xcd = (int)(blockIdx.x & 7u), q = (int)(blockIdx.x >> 3);
     const int p = (q / tiles) * 8 + xcd;
     if (p >= nbins)
         return;
     const int tile = q % tiles;
-    const int i0 = (tile / tiles_n) * kBM, j0 = (tile % tiles_n) * BN;
+    const int i0 = (tile / tiles_n) * BM, j0 = (tile % tiles_n) * BN;
     const float2* Ap = A + p * sAp;
     const float2* Bp = B + p * sBp;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -685,13 +694,13 @@ void cgemm_planar_kernel(const float2* __restrict__ A,
     // the current tile's products.
     float2 ra[LA], rb[LB];
     // Tiles wholly inside the matrices load without per-element checks.
-    const bool a_inside = i0 + kBM <= M, b_inside = j0 + BN <= N;
+    const bool a_inside = i0 + BM <= M, b_inside = j0 + BN <= N;
     auto fetch = [&](int k0) {
         const bool k_inside = k0 + kPK <= K;
 #pragma unroll
         for (int qq = 0; qq < LA; ++qq) {
             const int idx = threadIdx.x + qq * NT;
-            const int k = AK ? idx % kPK : idx / kBM, i = AK ? idx / kPK : idx % kBM;
+            const int k = AK ? idx % kPK : idx / BM, i = AK ? idx / kPK : idx % BM;
             float2 v = make_float2(0.0f, 0.0f);
             if ((a_inside && k_inside) || (i0 + i < M && k0 + k < K))
                 v = AK ? Ap[(int64_t)(i0 + i) * lda + (k0 + k)] : Ap[(int64_t)(k0 + k) * lda + (i0 + i)];
@@ -711,7 +720,7 @@ void cgemm_planar_kernel(const float2* __restrict__ A,
 #pragma unroll
         for (int qq = 0; qq < LA; ++qq) {
             const int idx = threadIdx.x + qq * NT;
-            const int k = AK ? idx % kPK : idx / kBM, i = AK ? idx / kPK : idx % kBM;
+            const int k = AK ? idx % kPK : idx / BM, i = AK ? idx / kPK : idx % BM;
             Ar[k][i] = ra[qq].x;
             Ai[k][i] = ra[qq].y;
         }
@@ -834,7 +843,7 @@ static int launch_cmul(int op, const float2* a, const float2* b, float2* c, int 
         M = fo; N = f; K = S; sAp = (int64_t)S * fo; sBp = (int64_t)S * f; lda = fo; ldb = f;
     }
     [[maybe_unused]] const int tiles_n = (N + kBN - 1) / kBN;
-    const int tiles_m = (M + kBM - 1) / kBM;
+    [[maybe_unused]] const int tiles_m = (M + kBM - 1) / kBM;
 #if FFTCONV_MFMA == 2
     // 32-column block tiles where they pad less than 64-column ones.
 #ifndef FFTCONV_PLANAR_WC
@@ -842,14 +851,22 @@ static int launch_cmul(int op, const float2* a, const float2* b, float2* c, int 
 #else
     const int wc = FFTCONV_PLANAR_WC;
 #endif
-    const int ptn = (N + 32 * wc - 1) / (32 * wc), ptiles = ptn * tiles_m;
+    // 128-row tiles (four waves) for the 32-column kernel where they pad M
+    // no more than 64-row ones.
+    const int wr = (FFTCONV_PLANAR_WR4 && wc == 1 &&
+                    (M + 127) / 128 * 128 - M <= (M + 63) / 64 * 64 - M) ? 4 : 2;
+    const int ptm = (M + 32 * wr - 1) / (32 * wr);
+    const int ptn = (N + 32 * wc - 1) / (32 * wc), ptiles = ptn * ptm;
     const int64_t pblocks = (int64_t)((nbins + 7) / 8) * 8 * ptiles;
     if (pblocks > 0x7FFFFFFF)
         return MESWISH_EINVAL;
-    const dim3 pgrid((unsigned)pblocks), pthreads(128 * wc);
+    const dim3 pgrid((unsigned)pblocks), pthreads(64 * wr * wc);
 #define FFTCONV_PLANAR(AK, BK, CA, CB)                                                            \
     do {                                                                                          \
-        if (wc == 1)                                                                              \
+        if (wc == 1 && wr == 4)                                                                   \
+            hipLaunchKernelGGL((cgemm_planar_kernel<AK, BK, CA, CB, 1, 4>), pgrid, pthreads, 0, s, \
+                               a, b, c, M, N, K, sAp, sBp, lda, ldb, ptn, ptiles, nbins);         \
+        else if (wc == 1)                                                                         \
             hipLaunchKernelGGL((cgemm_planar_kernel<AK, BK, CA, CB, 1>), pgrid, pthreads, 0, s, a, \
                                b, c, M, N, K, sAp, sBp, lda, ldb, ptn, ptiles, nbins);            \
         else                                                                                      \

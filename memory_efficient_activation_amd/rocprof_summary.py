@@ -452,7 +452,7 @@ def fft_key(r: dict):
                 if key[0] == kind and -(-key[1] // maps_per_block[int(mm.group(1))]) == blocks:
                     return key
             return (kind, B)
-    mm = re.search(r"cgemm(?:_mfma|_planar)?_kernel<(true|false), (true|false), (true|false), (true|false)(?:, \d+)?>", name)
+    mm = re.search(r"cgemm(?:_mfma|_planar)?_kernel<(true|false), (true|false), (true|false), (true|false)(?:, \d+)*>", name)
     if mm:
         flags = tuple(x == "true" for x in mm.groups())
         return ("cmul", {(True, True, False, True): 0, (True, False, False, False): 1,
