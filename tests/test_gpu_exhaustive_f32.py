@@ -1,7 +1,8 @@
-"""Every binary32 input x of Swish, through the C ABI, against the binary64
-oracle rounded to binary32: all 2^32 bit patterns (normal, subnormal, zero,
-infinite and NaN), the forward at alpha = 1 and 1.5 and the backward at
-alpha = 1 with dy = 1 and dy = -0.3.  The rules are the binary32 ones:
+"""Every binary32 input x of Swish and of the activation family, through the
+C ABI, against the binary64 oracle rounded to binary32: all 2^32 bit
+patterns (normal, subnormal, zero, infinite and NaN).  Swish: the forward at
+alpha = 1 and 1.5 and the backward at alpha = 1 with dy = 1 and dy = -0.3;
+the family: forward and backward with dy = 1 (LeakyReLU slope 0.01).  The rules are the binary32 ones:
 forward within 1e-5 of |reference| (floored at 2^-126), backward within 1e-5
 of the oracle's term scale m, NaN exactly where the oracle gives NaN.
 Chunks of 2^28 patterns; outputs bitwise equal to the oracle's are exact, and
@@ -64,3 +65,25 @@ def test_every_binary32_x_backward(dy, oracle):
         return oracle.bwd(xh, np.full_like(xh, np.float32(dy)), 1.0, threads=ORACLE_THREADS)
 
     _sweep(f"backward dy={dy}", gpu, ref)
+
+
+FAMILY = ["relu", "leaky_relu", "sigmoid", "tanh", "gelu", "gelu_tanh"]
+ORACLE_NAME = {"gelu": "gelu_erf"}
+PARAM = {"leaky_relu": 0.01}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("kind", FAMILY)
+def test_every_binary32_x_family(kind, oracle):
+    """The activation family, forward and backward (dy = 1), every binary32 x."""
+    p, oname = PARAM.get(kind, 0.0), ORACLE_NAME.get(kind, kind)
+    _sweep(f"{kind} forward", lambda x: mea.act_fwd(kind, x, p),
+           lambda xh: (oracle.act_fwd(oname, xh, p, threads=ORACLE_THREADS), None))
+
+    def gpu(x):
+        return mea.act_bwd(kind, x, torch.ones_like(x), p)
+
+    def ref(xh):
+        return oracle.act_bwd(oname, xh, np.ones_like(xh), p, threads=ORACLE_THREADS)
+
+    _sweep(f"{kind} backward dy=1", gpu, ref)
