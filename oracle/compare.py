@@ -19,6 +19,12 @@
 The floor 2^-126 (the smallest binary32 normal) reads "relative error" for
 references that are zero or subnormal, where a relative measure is
 undefined.  o is the oracle's value rounded to the output type.
+
+Every report counts the elements that break the rule (n_bad, NaN mismatches
+included) and gives the index of the first one in the input arrays
+(first_bad, -1 if none).  tests/compare_pins.py pins these rules on
+hand-built cases at both sides of each bound, and tests/test_compare_cpu.py
+checks that planted mistakes in this file are caught.
 """
 
 from __future__ import annotations
@@ -34,21 +40,23 @@ def ord_bf16(bits: np.ndarray) -> np.ndarray:
 
 
 def _nan_mask(got: np.ndarray, want: np.ndarray, is_nan):
-    gn, wn = is_nan(got), is_nan(want)
-    return gn, wn, int(np.count_nonzero(gn != wn))
+    return is_nan(got), is_nan(want)
 
 
 def bf16_report(got: np.ndarray, want: np.ndarray) -> dict:
     got = np.asarray(got, dtype=np.uint16).ravel()
     want = np.asarray(want, dtype=np.uint16).ravel()
     isn = lambda b: ((b & 0x7F80) == 0x7F80) & ((b & 0x007F) != 0)
-    gn, wn, nan_mismatch = _nan_mask(got, want, isn)
+    gn, wn = _nan_mask(got, want, isn)
     ok = ~(gn | wn)
     d = np.abs(ord_bf16(got[ok]) - ord_bf16(want[ok]))
-    bad = int(np.count_nonzero(d > 1)) + nan_mismatch
+    bad_mask = np.zeros(got.size, dtype=bool)
+    bad_mask[np.nonzero(ok)[0]] = d > 1
+    bad_mask |= gn != wn
+    bad = int(np.count_nonzero(bad_mask))
     return {"n": int(got.size), "max_ulp": int(d.max()) if d.size else 0,
             "n_off_by_one": int(np.count_nonzero(d == 1)), "n_bad": bad, "ok": bad == 0,
-            "first_bad": int(np.nonzero(np.concatenate([(d > 1), gn != wn]))[0][0]) if bad else -1}
+            "first_bad": int(np.nonzero(bad_mask)[0][0]) if bad else -1}
 
 
 def f32_report(got: np.ndarray, want: np.ndarray, scale: np.ndarray | None = None,
@@ -56,20 +64,20 @@ def f32_report(got: np.ndarray, want: np.ndarray, scale: np.ndarray | None = Non
     """Forward rule if scale is None, else the backward rule with scale m."""
     got = np.asarray(got, dtype=np.float32).ravel().astype(np.float64)
     want = np.asarray(want, dtype=np.float32).ravel().astype(np.float64)
-    gn, wn, nan_mismatch = _nan_mask(got, want, np.isnan)
+    gn, wn = _nan_mask(got, want, np.isnan)
     ok = ~(gn | wn)
     ref = np.abs(want[ok]) if scale is None else np.asarray(scale, np.float64).ravel()[ok]
     den = np.maximum(ref, FLOOR)
     with np.errstate(invalid="ignore"):
         err = np.abs(got[ok] - want[ok]) / den
     err = np.where(got[ok] == want[ok], 0.0, err)  # equal infinities
-    bad_mask = ~(err <= rtol)
-    bad = int(np.count_nonzero(bad_mask)) + nan_mismatch
-    idx = np.nonzero(ok)[0]
+    bad_mask = np.zeros(got.size, dtype=bool)
+    bad_mask[np.nonzero(ok)[0]] = ~(err <= rtol)
+    bad_mask |= gn != wn
+    bad = int(np.count_nonzero(bad_mask))
     return {"n": int(got.size), "max_rel": float(err.max()) if err.size else 0.0,
             "n_bad": bad, "ok": bad == 0,
-            "first_bad": int(idx[np.nonzero(bad_mask)[0][0]]) if np.any(bad_mask) else
-            (int(np.nonzero(gn != wn)[0][0]) if nan_mismatch else -1)}
+            "first_bad": int(np.nonzero(bad_mask)[0][0]) if bad else -1}
 
 
 def bf16_scaled_report(got: np.ndarray, want_bits: np.ndarray, want64: np.ndarray,
@@ -80,16 +88,17 @@ def bf16_scaled_report(got: np.ndarray, want_bits: np.ndarray, want64: np.ndarra
     want64 = np.asarray(want64, np.float64).ravel()
     scale = np.asarray(scale, np.float64).ravel()
     isn = lambda b: ((b & 0x7F80) == 0x7F80) & ((b & 0x007F) != 0)
-    gn, wn, nan_mismatch = _nan_mask(got, want_bits, isn)
+    gn, wn = _nan_mask(got, want_bits, isn)
     ok = ~(gn | wn)
     d = np.abs(ord_bf16(got[ok]) - ord_bf16(want_bits[ok]))
     gv = (got[ok].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     near = np.abs(gv - want64[ok]) <= rtol * np.maximum(scale[ok], FLOOR)
-    bad_mask = (d > 1) & ~near
-    bad = int(np.count_nonzero(bad_mask)) + nan_mismatch
-    idx = np.nonzero(ok)[0]
+    bad_mask = np.zeros(got.size, dtype=bool)
+    bad_mask[np.nonzero(ok)[0]] = (d > 1) & ~near
+    bad_mask |= gn != wn
+    bad = int(np.count_nonzero(bad_mask))
     return {"n": int(got.size), "max_ulp": int(d.max()) if d.size else 0,
             "n_off_by_one": int(np.count_nonzero(d == 1)),
             "n_beyond_one_within_scale": int(np.count_nonzero((d > 1) & near)),
             "n_bad": bad, "ok": bad == 0,
-            "first_bad": int(idx[np.nonzero(bad_mask)[0][0]]) if np.any(bad_mask) else -1}
+            "first_bad": int(np.nonzero(bad_mask)[0][0]) if bad else -1}

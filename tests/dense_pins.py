@@ -61,6 +61,63 @@ def pin_torch_autograd(d):
         assert np.all(np.abs(db - tb.grad.numpy()) <= 1e-12 * aux["dbeta_scale"] + 1e-300)
 
 
+def _torch_layer(srcs, gamma, beta, dz):
+    """binary64 PyTorch CPU: z, and the gradients of the sources, gamma and
+    beta, by autograd of torch.cat + batch_norm (training) + relu."""
+    import torch
+    import torch.nn.functional as F
+    ts = [torch.tensor(s, dtype=torch.float64, requires_grad=True) for s in srcs]
+    tg = torch.tensor(gamma, dtype=torch.float64, requires_grad=True)
+    tb = torch.tensor(beta, dtype=torch.float64, requires_grad=True)
+    z = torch.relu(F.batch_norm(torch.cat(ts, dim=1), None, None, tg, tb, training=True, eps=EPS))
+    z.backward(torch.tensor(dz, dtype=torch.float64))
+    return (z.detach().numpy(), [t.grad.numpy() for t in ts], tg.grad.numpy(), tb.grad.numpy())
+
+
+def pin_scales_attained(d):
+    """Each error scale is the sum of the absolute values of the terms its
+    result sums, so it equals |result| where all terms share a sign: the
+    scales are tight, not merely upper bounds (an inflated scale would
+    loosen the tolerance it sets).  One channel, values by hand, results
+    from PyTorch autograd:
+      forward: gamma > 0, beta > 0, mean < 0, u > 0    -> z = scale;
+      dbeta: every g > 0 (beta large: ReLU passes all) -> dbeta = scale;
+      dgamma: mean exactly 0, g with the sign of u     -> dgamma = scale;
+      du at element e: mean 0, g_e > 0, dbeta < 0 and u_e dgamma < 0, so
+        gamma r g_e, -gamma r dbeta / M and -gamma r xhat_e dgamma / M are
+        all positive                                    -> du_e = scale_e."""
+    # Forward: mean = -1.25 < 0; elements 3..5 have u > 0.
+    u = np.array([-5.0, -4.0, -3.0, 1.0, 2.0, 1.5])[None, None, :]
+    gamma, beta = np.array([0.7]), np.array([0.3])
+    dz = np.ones_like(u)
+    z, aux = d.forward([u], gamma, beta, EPS)
+    zt = _torch_layer([u], gamma, beta, dz)[0]
+    pos = u > 0
+    assert np.allclose(aux["scale"][pos], zt[pos], rtol=1e-13, atol=0), (aux["scale"][pos], zt[pos])
+    # Backward: symmetric values (mean exactly 0), beta large.
+    u = np.array([-3.0, -1.0, 1.0, 3.0])[None, None, :]
+    gamma, beta = np.array([0.5]), np.array([10.0])
+    for dz, what in ((np.array([0.5, 1.5, 2.0, 0.7]), "dbeta"),
+                     (np.array([-0.5, -1.5, 2.0, 0.7]), "dgamma"),
+                     (np.array([1.0, -0.5, 0.2, -1.5]), "du")):
+        dz = dz[None, None, :]
+        _, dut, dgt, dbt = _torch_layer([u], gamma, beta, dz)
+        dus, dg, db, aux = d.backward([u], dz, gamma, beta, EPS)
+        if what == "dbeta":
+            assert np.allclose(aux["dbeta_scale"], np.abs(dbt), rtol=1e-13, atol=0)
+        elif what == "dgamma":
+            assert np.allclose(aux["dgamma_scale"], np.abs(dgt), rtol=1e-13, atol=0)
+        else:
+            assert dbt[0] < 0 and dgt[0] < 0  # the sign conditions of element e = 2
+            e = (0, 0, 2)
+            assert np.isclose(aux["du_scale"][0][e], abs(dut[0][e]), rtol=1e-13, atol=0), \
+                (aux["du_scale"][0][e], dut[0][e])
+        # Everywhere, the scales bound the results.
+        assert np.all(np.abs(dut[0]) <= aux["du_scale"][0] * (1 + 1e-13))
+        assert np.all(np.abs(dgt) <= aux["dgamma_scale"] * (1 + 1e-13))
+        assert np.all(np.abs(dbt) <= aux["dbeta_scale"] * (1 + 1e-13))
+
+
 def pin_constant_channel(d):
     """Variance 0: xhat = 0, z = ReLU(beta); du = gamma / sqrt(eps) (g - mean g)."""
     srcs, gamma, beta, dz = _case(5, (3,), 4, 5)
@@ -179,6 +236,6 @@ def pin_batch_permutation(d):
         assert np.allclose(b, a[perm], rtol=1e-12, atol=1e-14)
 
 
-ALL_PINS = [pin_torch_autograd, pin_constant_channel, pin_two_values, pin_backward_invariants,
+ALL_PINS = [pin_torch_autograd, pin_scales_attained, pin_constant_channel, pin_two_values, pin_backward_invariants,
             pin_output_moments, pin_finite_differences, pin_channel_independence,
             pin_batch_permutation]

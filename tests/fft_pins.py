@@ -122,5 +122,52 @@ def pin_special_kernels(o):
     assert np.all(np.abs(o.fprop_direct(x, w)) <= o.fprop_scale(x, w)[:, :, None, None] + 1e-12)
 
 
+def pin_scales_attained(o):
+    """Each error scale is the Cauchy-Schwarz bound of its output elements
+    and is attained where that bound is sharp, so it is tight and not merely
+    an upper bound (an inflated scale would loosen every tolerance built on
+    it).  The cases have kernels as large as the maps, so each operation
+    reduces to dot products written out here with einsum:
+      forward: x[s, f] a positive multiple of w[g0, f]   -> y = sum ||x|| ||w||;
+      input gradient: every w[g, f] one spike at the same place, with the
+        sign of g[s0, g]                                 -> the spike's gradient;
+      weight gradient: every x[s, f] one spike, with the sign of g[s, g0];
+      spectrum: a constant map, all of whose energy is in the zero bin
+        (Parseval: the bin's magnitude is n ||x||)."""
+    r = _rng(71)
+    S, F, G, n = 3, 4, 5, 6
+    # Forward.
+    w = r.standard_normal((G, F, n, n))
+    g0 = 2
+    x = r.uniform(0.5, 2.0, (S, F))[:, :, None, None] * w[g0][None]
+    y = np.einsum("sfij,gfij->sg", x, w)
+    sc = o.fprop_scale(x, w)
+    assert np.allclose(sc[:, g0], np.abs(y[:, g0]), rtol=1e-12, atol=0), (sc[:, g0], y[:, g0])
+    assert np.all(np.abs(y) <= sc * (1 + 1e-12))
+    # Input gradient: the output gradient is 1 x 1 (m = 1).
+    g = r.standard_normal((S, G, 1, 1))
+    s0, i0, j0 = 1, 4, 2
+    w = np.zeros((G, F, n, n))
+    w[:, :, i0, j0] = np.sign(g[s0, :, 0, 0])[:, None] * r.uniform(0.5, 2.0, (G, F))
+    gx = np.einsum("sg,gfij->sfij", g[:, :, 0, 0], w)
+    sc = o.bprop_scale(g, w)
+    assert np.allclose(sc[s0], np.abs(gx[s0, :, i0, j0]), rtol=1e-12, atol=0)
+    assert np.all(np.abs(gx) <= sc[:, :, None, None] * (1 + 1e-12))
+    # Weight gradient.
+    x = np.zeros((S, F, n, n))
+    x[:, :, i0, j0] = np.sign(g[:, g0, 0, 0])[:, None] * r.uniform(0.5, 2.0, (S, F))
+    gw = np.einsum("sfij,sg->gfij", x, g[:, :, 0, 0])
+    sc = o.accgrad_scale(x, g)
+    assert np.allclose(sc[g0], np.abs(gw[g0, :, i0, j0]), rtol=1e-12, atol=0)
+    assert np.all(np.abs(gw) <= sc[:, :, None, None] * (1 + 1e-12))
+    # Spectrum of a constant map.
+    c = np.full((2, n, n), -1.75)
+    X = np.fft.fft2(c)
+    sc = o.spectrum_scale(c, n)
+    assert np.allclose(sc, np.abs(X[:, 0, 0]), rtol=1e-12, atol=0), (sc, X[:, 0, 0])
+    assert np.all(np.abs(X) <= sc[:, None, None] * (1 + 1e-12))
+
+
 ALL_PINS = [pin_dft_by_definition, pin_parseval_and_symmetry, pin_shift_theorem_and_round_trip,
-            pin_torch_conv2d, pin_convolution_theorem, pin_special_kernels]
+            pin_torch_conv2d, pin_convolution_theorem, pin_special_kernels,
+            pin_scales_attained]

@@ -570,4 +570,32 @@ def pin_infinite_inputs(o):
     assert y[0] == inf and y[1] == 0.0 and math.copysign(1, y[1]) < 0
 
 
+def pin_family_error_scale(o):
+    """The error scale m of each backward is tight, not just an upper bound:
+    it is the sum of the absolute values of the terms of dy f'(x), so it
+    equals |dy f'(x)| wherever those terms share a sign -- every x for ReLU,
+    LeakyReLU, sigmoid and tanh (one term each), x >= 0 for both GELUs -- and
+    it bounds |dy f'(x)|, staying within 1.3 times it, where the GELU terms
+    Phi and x phi differ in sign but x phi dominates (x <= -3: the ratio is
+    (|x| + 1/|x|) / (|x| - 1/|x|) at leading order for erf, and likewise
+    for the tanh form).  An inflated or loosened scale fails here."""
+    for act in FAMILY:
+        p = _param(act)
+        for x in _grid(-30.0, 30.0, 300, 67):
+            for dy in (1.0, -0.37):
+                g, m = o.act_grad_f64(act, x, dy, p)
+                assert m >= abs(g) * (1 - 1e-15), (act, x, g, m)
+                if act in ("gelu_erf", "gelu_tanh"):
+                    if x >= 0:
+                        assert abs(m - abs(g)) <= 1e-15 * m, (act, x, g, m)
+                    elif x <= -3.0 and g != 0.0:
+                        assert m <= 1.3 * abs(g), (act, x, g, m)
+                else:
+                    assert m == abs(g), (act, x, g, m)
+    # A case where the two GELU terms cancel exactly is where m is needed:
+    # near the zero of GELU' (x = -0.7518 for erf) m stays of order Phi.
+    g, m = o.act_grad_f64("gelu_erf", -0.7517915241, 1.0)
+    assert abs(g) < 1e-9 and 0.4 < m < 0.5, (g, m)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -38,6 +38,13 @@ MUTANTS = {
     "concat_reversed": ("for s in sources], axis=1)", "for s in sources[::-1]], axis=1)"),
     "split_shifted": ("out.append(u[:, c0:c0 + c, :])", "out.append(np.roll(u, 1, axis=1)[:, c0:c0 + c, :])"),
     "leaky_output": ("z = np.maximum(h, 0.0)", "z = np.maximum(h, 0.0) + 0.01 * np.minimum(h, 0.0)"),
+    # Inflated error scales (each would loosen the tolerance it sets).
+    "fwd_scale_doubled": ("scale = np.where(h > 0, terms, 0.0)", "scale = np.where(h > 0, 2 * terms, 0.0)"),
+    "du_scale_doubled": ("du_scale = np.abs(k) * (", "du_scale = 2 * np.abs(k) * ("),
+    "du_scale_drops_mean_term": ("np.abs(g) + np.abs(dbeta)[None, :, None] / m\n",
+                                 "np.abs(g)\n"),
+    "dgamma_scale_doubled": ('"dgamma_scale": (np.abs(g) * xsize)', '"dgamma_scale": 2 * (np.abs(g) * xsize)'),
+    "dbeta_scale_doubled": ('"dbeta_scale": np.abs(g).sum(axis=(0, 2))', '"dbeta_scale": 2 * np.abs(g).sum(axis=(0, 2))'),
     "beta_outside_relu": ("z = np.maximum(h, 0.0)", "z = np.maximum(gamma * xhat, 0.0) + beta"),
 }
 

@@ -39,6 +39,11 @@ MUTANTS = {
                                  'y += np.einsum("sfij,gf->sgij", x[:, :1, a:a + m, b:b + m], w[:, :1, a, b])'),
     "half_spectrum_too_narrow": ("return np.fft.rfft2(pad(x, n), axes=(-2, -1))",
                                  "return np.fft.rfft2(pad(x, n), axes=(-2, -1))[..., :n // 2]"),
+    # Inflated error scales (each would loosen the tolerance it sets).
+    "fprop_scale_doubled": ("return _norms(x) @ _norms(w).T", "return 2 * _norms(x) @ _norms(w).T"),
+    "bprop_scale_doubled": ("return _norms(g) @ _norms(w)\n", "return 2 * _norms(g) @ _norms(w)\n"),
+    "accgrad_scale_doubled": ("return _norms(g).T @ _norms(x)", "return 2 * _norms(g).T @ _norms(x)"),
+    "spectrum_scale_doubled": ("return n * _norms(x)", "return 2 * n * _norms(x)"),
     "scale_without_root": ("return np.sqrt((np.asarray(a, np.float64) ** 2).sum(axis=(-2, -1)))",
                            "return (np.asarray(a, np.float64) ** 2).sum(axis=(-2, -1)) / 1e3"),
 }

@@ -58,6 +58,15 @@ MUTANTS = {
     "leaky_fwd_drops_x": ("return x > 0.0 ? x : p * x;", "return x > 0.0 ? x : p;"),
     "leaky_grad_at_zero": ("g = dy * (x > 0.0 ? 1.0 : p);", "g = dy * (x >= 0.0 ? 1.0 : p);"),
     "gelu_scale_drops_abs": ("m = fabs(dy) * (cdf + fabs(x) * pdf);", "m = fabs(dy) * (cdf + x * pdf);"),
+    # Error scales inflated: the tolerance they set would loosen.
+    "swish_scale_doubled": ("*scale = fabs(dy) * s * (1.0 + fabs(t) * one_minus_s);",
+                            "*scale = 2.0 * fabs(dy) * s * (1.0 + fabs(t) * one_minus_s);"),
+    "gelu_scale_doubled": ("m = fabs(dy) * (cdf + fabs(x) * pdf);",
+                           "m = 2.0 * fabs(dy) * (cdf + fabs(x) * pdf);"),
+    "gelu_tanh_scale_doubled": ("m = fabs(dy) * (s + fabs(x) * s * c * 2.0 * du);",
+                                "m = 2.0 * fabs(dy) * (s + fabs(x) * s * c * 2.0 * du);"),
+    "tanh_scale_inflated": ("g = dy / (c * c);\n        m = fabs(g);",
+                            "g = dy / (c * c);\n        m = 1.5 * fabs(g);"),
     "family_nan_passthrough": ("    if (isnan(x))\n        return x;\n    switch (act) {",
                                "    switch (act) {"),
     # Limits at +-inf: the value as x -> +-inf with the parameter fixed.
