@@ -30,7 +30,10 @@
  * - dtype is MESWISH_F32 (binary32) or MESWISH_BF16 (bfloat16).  Input and
  *   output share the dtype.  Arithmetic is binary32 in every case; outputs
  *   are rounded to nearest even, subnormals kept.
- * - alpha is a finite binary32 value (any sign).
+ * - alpha is a finite binary32 value (any sign) whose product with log2 e
+ *   is finite in binary32: |alpha| <= about 2.3586e38 (larger values return
+ *   MESWISH_EINVAL; the sigmoid is evaluated as 1 / (1 + 2^(x C)) with
+ *   C = -alpha log2 e).
  * - Calls are asynchronous: they enqueue kernels on `stream` (a hipStream_t;
  *   NULL means the default stream) and return once the work is enqueued.
  *   Faults inside a kernel surface at the caller's next synchronisation.
@@ -62,7 +65,8 @@ typedef enum { MESWISH_F32 = 0, MESWISH_BF16 = 1 } meswish_dtype;
 typedef enum {
     MESWISH_OK = 0,
     MESWISH_EINVAL = 1,   /* NULL pointer with n > 0, unknown dtype,
-                             non-finite alpha, misaligned element pointer,
+                             non-finite alpha (or, for Swish, |alpha| log2 e
+                             beyond binary32), misaligned element pointer,
                              negative count, n too large */
     MESWISH_EALIAS = 2,   /* an output overlaps an input or another output
                              other than by exact, same-tensor coincidence */
@@ -177,10 +181,11 @@ typedef struct {
     long long nvec;             /* 16-byte vectors of the body */
     long long tail;             /* elements after the body (all n on the element path) */
     long long tiles;            /* work tiles (one block each) */
-    long long grid;             /* blocks launched */
+    long long grid;             /* blocks per launch (grid x block < 2^32) */
     long long block;            /* threads per block */
     long long elems_per_vector; /* 4 (binary32) or 8 (bfloat16) */
     long long vectors_per_tile; /* 16-byte vectors per tile */
+    long long launches;         /* kernel launches (vector path: one per 2^30 tiles) */
 } meswish_plan_t;
 
 /*

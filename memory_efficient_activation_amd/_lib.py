@@ -48,7 +48,8 @@ class Plan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int), ("head", ctypes.c_longlong), ("nvec", ctypes.c_longlong),
                 ("tail", ctypes.c_longlong), ("tiles", ctypes.c_longlong),
                 ("grid", ctypes.c_longlong), ("block", ctypes.c_longlong),
-                ("elems_per_vector", ctypes.c_longlong), ("vectors_per_tile", ctypes.c_longlong)]
+                ("elems_per_vector", ctypes.c_longlong), ("vectors_per_tile", ctypes.c_longlong),
+                ("launches", ctypes.c_longlong)]
 
 
 class DenseSource(ctypes.Structure):

@@ -2,9 +2,10 @@
 //
 // Every activation is written as a struct with the same device interface:
 //
-//   fwd<P>(x, k, rare)       value at x                       (fast path)
-//   bwd<P>(x, dy, k, rare)   dy times the derivative at x     (fast path)
-//   is_rare<BWD, P>(x, k)    true exactly where the fast path sets `rare`
+//   fwd<P>(x, k, rk)         value at x                       (fast path)
+//   bwd<P>(x, dy, k, rk)     dy times the derivative at x     (fast path)
+//   rare_thr<P>()            an element is rare where its key exceeds this
+//   is_rare<BWD, P>(x, k)    true exactly where the element's key > rare_thr
 //   fwd_rare(x, k), bwd_rare(x, dy, k)   the rare branch, taken per wave
 //
 // x = +-inf gives the limits as x -> +-inf with the parameter fixed (a zero
@@ -12,8 +13,13 @@
 //
 // P (precise) is true for binary32 I/O, where results must agree with the
 // exact value to 1e-5 relative; bfloat16 I/O needs only 2^-9, so its fast
-// paths skip the extra-precision terms.  The fast paths set `rare` exactly
-// where is_rare is true; the caller then recomputes those elements.
+// paths skip the extra-precision terms.  Each fast path folds the element's
+// rare key into the running maximum rk (rk = fmaxf(rk, key); a NaN key is
+// never rare, as the comparison it stands for is false).  A vector whose
+// maximum exceeds rare_thr<P>() holds at least one rare element, and the
+// caller recomputes exactly those where is_rare is true.  One max3 per
+// three elements and one comparison per vector replace a comparison per
+// element.  Keys must be quiet: a signaling NaN makes the maximum NaN.
 //
 // Sources, by page title and section:
 //   Swish: blog post "Memory efficient Swish" (adeeplearner.github.io),
@@ -51,7 +57,10 @@ enum ActKind {
     kTanh = 4,
     kGeluErf = 5,
     kGeluTanh = 6,
-    kActCount = 7
+    kActCount = 7,
+    // Swish with alpha exactly 1: the same results by a shorter backward
+    // (internal to the library; callers name kSwish).
+    kSwishUnit = 8
 };
 
 // Coefficients prepared on the host (make_coef in meswish.hip).
@@ -119,29 +128,35 @@ __device__ __forceinline__ float scale_pow2(float m, float g, float ef, int kf)
 
 // ---------------------------------------------------------------------------
 // Swish: x Sigmoid(t), t = alpha x.  C = -alpha log2 e, so E = 2^(x C) = e^-t.
+// kUnit: alpha is exactly 1 (t = x, one multiply less per element in the
+// backward); the host selects it from the value of alpha.
 // ---------------------------------------------------------------------------
-struct SwishOp {
+template <bool kUnit>
+struct SwishOpT {
     static constexpr bool kHasRare = true;
 
     template <bool P>
-    __device__ static float fwd(float x, const Coef& k, bool& rare)
+    __device__ static constexpr float rare_thr() { return kMaxExp; }
+
+    template <bool P>
+    __device__ static float fwd(float x, const Coef& k, float& rk)
     {
         float v;
         float e = exp2_lin<P>(x, k, v);
         float s = rcp_hw(1.0f + e);
-        rare |= fabsf(v) > kMaxExp;
+        rk = fmaxf(rk, fabsf(v));
         return x * s;
     }
 
     template <bool P>
-    __device__ static float bwd(float x, float dy, const Coef& k, bool& rare)
+    __device__ static float bwd(float x, float dy, const Coef& k, float& rk)
     {
         float v;
         float e = exp2_lin<P>(x, k, v);
         float s = rcp_hw(1.0f + e);
         float c = e * s;  // 1 - s without cancellation
-        float g = fmaf(k.p * x, c, 1.0f);
-        rare |= fabsf(v) > kMaxExp;
+        float g = fmaf(kUnit ? x : k.p * x, c, 1.0f);
+        rk = fmaxf(rk, fabsf(v));
         return dy * (s * g);
     }
 
@@ -180,6 +195,7 @@ struct SwishOp {
         return scale_pow2(dy, 1.0f + t, ef, kf);
     }
 };
+typedef SwishOpT<false> SwishOp;
 
 // ---------------------------------------------------------------------------
 // Sigmoid: C = -log2 e, E = e^-x, s = 1 / (1 + E), s' = s (E s).
@@ -188,23 +204,26 @@ struct SigmoidOp {
     static constexpr bool kHasRare = true;
 
     template <bool P>
-    __device__ static float fwd(float x, const Coef& k, bool& rare)
+    __device__ static constexpr float rare_thr() { return kMaxExp; }
+
+    template <bool P>
+    __device__ static float fwd(float x, const Coef& k, float& rk)
     {
         float v;
         float e = exp2_lin<P>(x, k, v);
         // x < -86.6: s is e^x, possibly subnormal.  x > 86.6: s rounds to 1
         // (and the exponent may have overflowed, which the P terms dislike).
-        rare |= fabsf(v) > kMaxExp;
+        rk = fmaxf(rk, fabsf(v));
         return rcp_hw(1.0f + e);
     }
 
     template <bool P>
-    __device__ static float bwd(float x, float dy, const Coef& k, bool& rare)
+    __device__ static float bwd(float x, float dy, const Coef& k, float& rk)
     {
         float v;
         float e = exp2_lin<P>(x, k, v);
         float s = rcp_hw(1.0f + e);
-        rare |= fabsf(v) > kMaxExp;
+        rk = fmaxf(rk, fabsf(v));
         return dy * (s * (e * s));
     }
 
@@ -251,7 +270,10 @@ struct TanhOp {
     static constexpr bool kHasRare = true;
 
     template <bool P>
-    __device__ static float fwd(float x, const Coef& k, bool& /*rare: the forward has none*/)
+    __device__ static constexpr float rare_thr() { return kMaxExp; }
+
+    template <bool P>
+    __device__ static float fwd(float x, const Coef& k, float& /*rk: the forward has no rare case*/)
     {
         float a = fabsf(x);
         float v;
@@ -268,12 +290,12 @@ struct TanhOp {
     }
 
     template <bool P>
-    __device__ static float bwd(float x, float dy, const Coef& k, bool& rare)
+    __device__ static float bwd(float x, float dy, const Coef& k, float& rk)
     {
         float v;
         float e = exp2_lin<P>(fabsf(x), k, v);
         float r = rcp_hw(1.0f + e);
-        rare |= v < -kMaxExp;  // |x| > 43.3: 4E below the normal range
+        rk = fmaxf(rk, -v);  // v < -125, |x| > 43.3: 4E below the normal range
         return dy * (4.0f * e * r * r);
     }
 
@@ -305,13 +327,16 @@ struct ReluOp {
     static constexpr bool kHasRare = false;
 
     template <bool P>
-    __device__ static float fwd(float x, const Coef&, bool&)
+    __device__ static constexpr float rare_thr() { return INFINITY; }
+
+    template <bool P>
+    __device__ static float fwd(float x, const Coef&, float&)
     {
         return x > 0.0f ? x : (x <= 0.0f ? 0.0f : x);
     }
 
     template <bool P>
-    __device__ static float bwd(float x, float dy, const Coef&, bool&)
+    __device__ static float bwd(float x, float dy, const Coef&, float&)
     {
         return dy * (x > 0.0f ? 1.0f : (x <= 0.0f ? 0.0f : x));
     }
@@ -326,13 +351,16 @@ struct LeakyReluOp {
     static constexpr bool kHasRare = false;
 
     template <bool P>
-    __device__ static float fwd(float x, const Coef& k, bool&)
+    __device__ static constexpr float rare_thr() { return INFINITY; }
+
+    template <bool P>
+    __device__ static float fwd(float x, const Coef& k, float&)
     {
         return x > 0.0f ? x : k.p * x;
     }
 
     template <bool P>
-    __device__ static float bwd(float x, float dy, const Coef& k, bool&)
+    __device__ static float bwd(float x, float dy, const Coef& k, float&)
     {
         return dy * (x > 0.0f ? 1.0f : (x <= 0.0f ? k.p : x));
     }
@@ -429,16 +457,25 @@ struct GeluErfOp {
     }
 
     template <bool P>
-    __device__ static float fwd(float x, const Coef& k, bool& rare)
+    __device__ static constexpr float rare_thr() { return -kRareBelow; }
+
+    // Key of the rare test x < -6: -x, canonicalised.  A plain negation
+    // keeps a signaling NaN signaling, and a maximum that meets one returns
+    // NaN, which would hide the rare elements of the same vector (the
+    // keys of the other activations come out of arithmetic, which quiets).
+    __device__ static float rare_key(float x) { return __builtin_canonicalizef(-x); }
+
+    template <bool P>
+    __device__ static float fwd(float x, const Coef& k, float& rk)
     {
         float h = P ? half_erfc_abs(x, k, nullptr) : tail_short<false>(x);
         float cdf = x < 0.0f ? h : 1.0f - h;
-        rare |= x < kRareBelow;
+        rk = fmaxf(rk, rare_key(x));
         return x * cdf;
     }
 
     template <bool P>
-    __device__ static float bwd(float x, float dy, const Coef& k, bool& rare)
+    __device__ static float bwd(float x, float dy, const Coef& k, float& rk)
     {
         float e2, h;
         if (P) {
@@ -449,7 +486,7 @@ struct GeluErfOp {
             e2 = exp2_hw(a * a * k.c_hi);
         }
         float cdf = x < 0.0f ? h : 1.0f - h;
-        rare |= x < kRareBelow;
+        rk = fmaxf(rk, rare_key(x));
         // x = +inf: the limit 1 (the product x phi would be inf * 0).
         return x == INFINITY ? dy : dy * fmaf(x, e2 * kInvSqrt2Pif, cdf);
     }
@@ -517,17 +554,20 @@ struct GeluTanhOp {
     }
 
     template <bool P>
-    __device__ static float fwd(float x, const Coef& k, bool& rare)
+    __device__ static constexpr float rare_thr() { return P ? kPreciseMaxExp : kMaxExp; }
+
+    template <bool P>
+    __device__ static float fwd(float x, const Coef& k, float& rk)
     {
         float a = x * fmaf(k.aux_hi * x, x, 1.0f);
         float v;
         float e = exp2_lin<false>(a, k, v);
-        rare |= flag<P>(v);
+        rk = fmaxf(rk, fabsf(v));
         return x * rcp_hw(1.0f + e);
     }
 
     template <bool P>
-    __device__ static float bwd(float x, float dy, const Coef& k, bool& rare)
+    __device__ static float bwd(float x, float dy, const Coef& k, float& rk)
     {
         float a = x * fmaf(k.aux_hi * x, x, 1.0f);
         float v;
@@ -536,7 +576,7 @@ struct GeluTanhOp {
         float c = e * s;                                               // 1 - s
         float du2 = kGeluTanhK * fmaf(3.0f * k.aux_hi * x, x, 1.0f);  // 2 u'
         float g = fmaf(x * c, du2, 1.0f);
-        rare |= flag<P>(v);
+        rk = fmaxf(rk, fabsf(v));
         return dy * (s * g);
     }
 
@@ -613,5 +653,6 @@ template <> struct ActOp<kSigmoid> : SigmoidOp {};
 template <> struct ActOp<kTanh> : TanhOp {};
 template <> struct ActOp<kGeluErf> : GeluErfOp {};
 template <> struct ActOp<kGeluTanh> : GeluTanhOp {};
+template <> struct ActOp<kSwishUnit> : SwishOpT<true> {};
 
 }  // namespace meswish

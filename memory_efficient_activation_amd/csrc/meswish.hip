@@ -76,11 +76,6 @@
 #ifndef MESWISH_BLOCKS_PER_CU
 #define MESWISH_BLOCKS_PER_CU 100000
 #endif
-// Remap block ids so that the blocks one XCD receives (the dispatcher deals
-// blocks to the 8 XCDs round-robin) work on adjacent tiles.
-#ifndef MESWISH_XCD_SWIZZLE
-#define MESWISH_XCD_SWIZZLE 0
-#endif
 // Minimum waves per SIMD the compiler must allow (caps VGPRs); 0 = no cap.
 #ifndef MESWISH_MIN_WAVES
 #define MESWISH_MIN_WAVES 0
@@ -241,11 +236,11 @@ __device__ __forceinline__ uint4 fwd_vec(const uint4& xv, const Coef& k)
     constexpr bool P = Io<IO>::kPrecise;
     float xf[E], yf[E];
     Io<IO>::unpack(xv, xf);
-    bool rare = false;
+    float rk = 0.0f;
 #pragma unroll
     for (int j = 0; j < E; ++j)
-        yf[j] = Op::template fwd<P>(xf[j], k, rare);
-    if (Op::kHasRare && __builtin_expect(rare, 0)) {
+        yf[j] = Op::template fwd<P>(xf[j], k, rk);
+    if (Op::kHasRare && __builtin_expect(rk > Op::template rare_thr<P>(), 0)) {
 #pragma unroll
         for (int j = 0; j < E; ++j)
             if (Op::template is_rare<false, P>(xf[j], k))
@@ -263,11 +258,11 @@ __device__ __forceinline__ uint4 bwd_vec(const uint4& xv, const uint4& dv, const
     float xf[E], df[E], gf[E];
     Io<IO>::unpack(xv, xf);
     Io<IO>::unpack(dv, df);
-    bool rare = false;
+    float rk = 0.0f;
 #pragma unroll
     for (int j = 0; j < E; ++j)
-        gf[j] = Op::template bwd<P>(xf[j], df[j], k, rare);
-    if (Op::kHasRare && __builtin_expect(rare, 0)) {
+        gf[j] = Op::template bwd<P>(xf[j], df[j], k, rk);
+    if (Op::kHasRare && __builtin_expect(rk > Op::template rare_thr<P>(), 0)) {
 #pragma unroll
         for (int j = 0; j < E; ++j)
             if (Op::template is_rare<true, P>(xf[j], k))
@@ -284,60 +279,61 @@ __device__ __forceinline__ void one_element(const IO* x, const IO* dy, IO* out, 
     using Op = ActOp<ACT>;
     constexpr bool P = Io<IO>::kPrecise;
     float xv = Io<IO>::load1(x, i);
-    bool rare = false;
+    float rk = 0.0f;
     float r;
     if (kBwd) {
         float dv = Io<IO>::load1(dy, i);
-        r = Op::template bwd<P>(xv, dv, k, rare);
-        if (Op::kHasRare && rare)
+        r = Op::template bwd<P>(xv, dv, k, rk);
+        if (Op::kHasRare && rk > Op::template rare_thr<P>())
             r = Op::bwd_rare(xv, dv, k);
     } else {
-        r = Op::template fwd<P>(xv, k, rare);
-        if (Op::kHasRare && rare)
+        r = Op::template fwd<P>(xv, k, rk);
+        if (Op::kHasRare && rk > Op::template rare_thr<P>())
             r = Op::fwd_rare(xv, k);
     }
     Io<IO>::store1(out, i, r);
 }
 
-// Vectors [v_begin, v_end) of the 16-byte-aligned body starting at x, dy, out
-// (already offset past the head), processed by this block as tiles of
-// tile_vecs<IO>() vectors.
+// One tile: the nv <= tile_vecs<IO>() 16-byte vectors that start at xb, db,
+// ob.  The base pointers and nv are uniform over the block and lane offsets
+// are 32-bit, so every load and store addresses as a scalar base plus a
+// vector offset, with no 64-bit address arithmetic per lane.
 template <typename IO, bool kBwd, int ACT, int kNt = NtPolicy<IO, kBwd>::kMask>
-__device__ __forceinline__ void body_tile(const uint4* xv, const uint4* dv, uint4* ov,
-                                          int64_t tile_first, int64_t nvec, const Coef& k)
+__device__ __forceinline__ void body_tile(const uint4* xb, const uint4* db, uint4* ob,
+                                          uint32_t nv, const Coef& k)
 {
     constexpr int kUnroll = Io<IO>::kUnroll;
     constexpr int kBlock = Io<IO>::kBlock;
-    int64_t i = tile_first + threadIdx.x;
-    if (tile_first + tile_vecs<IO>() <= nvec) {
+    const uint32_t i = threadIdx.x;
+    if (nv == (uint32_t)tile_vecs<IO>()) {
         uint4 a[kUnroll], b[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            a[u] = ld16<(kNt & 1) != 0>(xv + i + u * kBlock);
+            a[u] = ld16<(kNt & 1) != 0>(xb + (i + u * kBlock));
         if (kBwd) {
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u)
-                b[u] = ld16<(kNt & 2) != 0>(dv + i + u * kBlock);
+                b[u] = ld16<(kNt & 2) != 0>(db + (i + u * kBlock));
         }
         // Keep every load of the tile ahead of the first use of its data, so
         // that a thread has all of them in flight at once.
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            st16<(kNt & 4) != 0>(ov + i + u * kBlock,
+            st16<(kNt & 4) != 0>(ob + (i + u * kBlock),
                                   kBwd ? bwd_vec<IO, ACT>(a[u], b[u], k) : fwd_vec<IO, ACT>(a[u], k));
     } else {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            int64_t j = i + u * kBlock;
-            if (j < nvec) {
-                uint4 a = ld16<(kNt & 1) != 0>(xv + j);
+            const uint32_t j = i + u * kBlock;
+            if (j < nv) {
+                uint4 a = ld16<(kNt & 1) != 0>(xb + j);
                 uint4 r;
                 if (kBwd)
-                    r = bwd_vec<IO, ACT>(a, ld16<(kNt & 2) != 0>(dv + j), k);
+                    r = bwd_vec<IO, ACT>(a, ld16<(kNt & 2) != 0>(db + j), k);
                 else
                     r = fwd_vec<IO, ACT>(a, k);
-                st16<(kNt & 4) != 0>(ov + j, r);
+                st16<(kNt & 4) != 0>(ob + j, r);
             }
         }
     }
@@ -348,29 +344,31 @@ __device__ __forceinline__ void body_tile(const uint4* xv, const uint4* dv, uint
 // ---------------------------------------------------------------------------
 
 // Single tensor, all pointers congruent modulo 16 bytes: `head` scalar
-// elements, then nvec 16-byte vectors, then `tail` scalar elements.
+// elements, then a body of 16-byte vectors in `tiles` tiles (all full but
+// the last, which holds last_vecs vectors), then `tail` scalar elements.
+// Tile indices are 32-bit (the host splits larger tensors into several
+// launches); the loop over tiles only runs more than once when the grid is
+// capped.
 template <typename IO, bool kBwd, int ACT>
 __global__ MESWISH_BOUNDS void act_vec_kernel(const IO* x, const IO* dy, IO* out,
-                                                           int64_t head, int64_t nvec,
-                                                           int64_t tail, Coef k)
+                                              uint32_t head, uint32_t tiles,
+                                              uint32_t last_vecs, uint32_t tail, Coef k)
 {
     constexpr int E = Io<IO>::kPerVec;
+    constexpr uint32_t kTileVecs = tile_vecs<IO>();
     const uint4* xv = reinterpret_cast<const uint4*>(x + head);
     const uint4* dv = kBwd ? reinterpret_cast<const uint4*>(dy + head) : nullptr;
     uint4* ov = reinterpret_cast<uint4*>(out + head);
-    constexpr int64_t kTileVecs = tile_vecs<IO>();
-    const int64_t stride = (int64_t)gridDim.x * kTileVecs;
-    int64_t b = blockIdx.x;
-#if MESWISH_XCD_SWIZZLE
-    if ((gridDim.x & 7u) == 0)
-        b = (b & 7) * (gridDim.x >> 3) + (b >> 3);
-#endif
-    for (int64_t t0 = b * kTileVecs; t0 < nvec; t0 += stride)
-        body_tile<IO, kBwd, ACT>(xv, dv, ov, t0, nvec, k);
+    for (uint32_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+        const size_t v0 = (size_t)t * kTileVecs;
+        body_tile<IO, kBwd, ACT>(xv + v0, kBwd ? dv + v0 : nullptr, ov + v0,
+                                 t + 1 < tiles ? kTileVecs : last_vecs, k);
+    }
     if (blockIdx.x == 0 && threadIdx.x < head + tail) {
-        int64_t i = threadIdx.x < head ? (int64_t)threadIdx.x
-                                       : head + nvec * E + (threadIdx.x - head);
-        one_element<IO, kBwd, ACT>(x, dy, out, i, k);
+        const size_t nvec = tiles ? (size_t)(tiles - 1) * kTileVecs + last_vecs : 0;
+        const size_t i = threadIdx.x < head ? (size_t)threadIdx.x
+                                            : head + nvec * E + (threadIdx.x - head);
+        one_element<IO, kBwd, ACT>(x, dy, out, (int64_t)i, k);
     }
 }
 
@@ -433,9 +431,12 @@ __global__ MESWISH_BOUNDS void act_group_kernel(GroupArgs g, Coef k)
         }
         const int64_t nvec = (n - head) / E;
         const int64_t tail = n - head - nvec * E;
-        body_tile<IO, kBwd, ACT>(reinterpret_cast<const uint4*>(x + head),
-                            kBwd ? reinterpret_cast<const uint4*>(dy + head) : nullptr,
-                            reinterpret_cast<uint4*>(out + head), local * kTileVecs, nvec, k);
+        const int64_t v0 = local * kTileVecs;
+        const int64_t left = nvec - v0;
+        const uint32_t nv = left >= kTileVecs ? (uint32_t)kTileVecs : (uint32_t)(left > 0 ? left : 0);
+        body_tile<IO, kBwd, ACT>(reinterpret_cast<const uint4*>(x + head) + v0,
+                                 kBwd ? reinterpret_cast<const uint4*>(dy + head) + v0 : nullptr,
+                                 reinterpret_cast<uint4*>(out + head) + v0, nv, k);
         const int64_t t = threadIdx.x;  // head >= 0 here
         if (local == 0 && t < head + tail) {
             int64_t i = t < head ? t : head + nvec * E + (t - head);
@@ -496,13 +497,25 @@ static int cu_count()
     return c;
 }
 
-static int64_t grid_for_tiles(int64_t tiles)
+// Blocks for `tiles` tiles of `block` threads: one block per tile, capped
+// at MESWISH_BLOCKS_PER_CU per compute unit and so that grid x block stays
+// below 2^32 threads, the launch limit (the kernels loop over the tiles a
+// capped grid leaves).
+static int64_t grid_for_tiles(int64_t tiles, int block)
 {
     int64_t cap = (int64_t)cu_count() * MESWISH_BLOCKS_PER_CU;
+    const int64_t thread_cap = (int64_t)(UINT32_MAX / (uint32_t)block);
+    if (cap > thread_cap)
+        cap = thread_cap;
     if (tiles < 1)
         tiles = 1;
     return tiles < cap ? tiles : cap;
 }
+
+// Tiles per launch of the vector kernel: tile indices stay 32-bit, and a
+// tile index plus the grid never wraps.  Longer tensors take several
+// launches of this many tiles each.
+constexpr int64_t kMaxLaunchTiles = (int64_t)1 << 30;
 
 static size_t elem_size(int dtype) { return dtype == MESWISH_F32 ? 4 : 2; }
 
@@ -595,8 +608,14 @@ static meswish_plan_t make_plan(const void* x, const void* dy, const void* out, 
         p.tail = nn;
         p.tiles = (nn + kTileVecs - 1) / kTileVecs;
     }
-    p.grid = grid_for_tiles(p.tiles);
     p.block = Io<IO>::kBlock;
+    if (p.path == MESWISH_PATH_VECTOR) {
+        p.launches = p.tiles > kMaxLaunchTiles ? (p.tiles + kMaxLaunchTiles - 1) / kMaxLaunchTiles : 1;
+        p.grid = grid_for_tiles(p.tiles < kMaxLaunchTiles ? p.tiles : kMaxLaunchTiles, (int)p.block);
+    } else {
+        p.launches = 1;
+        p.grid = grid_for_tiles(p.tiles, (int)p.block);
+    }
     p.elems_per_vector = E;
     p.vectors_per_tile = kTileVecs;
     return p;
@@ -606,15 +625,37 @@ template <typename IO, bool kBwd, int ACT>
 static int run_single(const void* x, const void* dy, void* out, size_t n, Coef k,
                       hipStream_t stream)
 {
+    constexpr int E = Io<IO>::kPerVec;
+    constexpr int64_t kTileVecs = tile_vecs<IO>();
     const meswish_plan_t p = make_plan<IO, kBwd>(x, dy, out, n);
     const IO* xp = static_cast<const IO*>(x);
     const IO* dp = static_cast<const IO*>(dy);
     IO* op = static_cast<IO*>(out);
-    int64_t head = p.head, nvec = p.nvec, tail = p.tail;
     if (p.path == MESWISH_PATH_VECTOR) {
-        void* args[] = {&xp, &dp, &op, &head, &nvec, &tail, &k};
-        return launch(reinterpret_cast<const void*>(&act_vec_kernel<IO, kBwd, ACT>), p.grid, args,
-                      stream, (int)p.block);
+        // Launch c covers tiles [c L, min((c + 1) L, tiles)) of the body, L =
+        // kMaxLaunchTiles; the first also does the head, the last the tail.
+        int64_t done = 0;  // elements of the body before launch c
+        for (int64_t c = 0; c < p.launches; ++c) {
+            const int64_t t0 = c * kMaxLaunchTiles;
+            const int64_t nt = p.tiles - t0 < kMaxLaunchTiles ? p.tiles - t0 : kMaxLaunchTiles;
+            const int64_t vecs = (t0 + nt) * kTileVecs <= p.nvec ? nt * kTileVecs : p.nvec - t0 * kTileVecs;
+            const bool first = c == 0, last = c + 1 == p.launches;
+            uint32_t head = first ? (uint32_t)p.head : 0;
+            uint32_t tail = last ? (uint32_t)p.tail : 0;
+            uint32_t tiles = (uint32_t)nt;
+            uint32_t last_vecs = nt ? (uint32_t)(vecs - (nt - 1) * kTileVecs) : 0;
+            const int64_t off = first ? 0 : p.head + done;
+            const IO* xc = xp + off;
+            const IO* dc = kBwd ? dp + off : dp;
+            IO* oc = op + off;
+            void* args[] = {&xc, &dc, &oc, &head, &tiles, &last_vecs, &tail, &k};
+            int rc = launch(reinterpret_cast<const void*>(&act_vec_kernel<IO, kBwd, ACT>), p.grid,
+                            args, stream, (int)p.block);
+            if (rc != MESWISH_OK)
+                return rc;
+            done += vecs * E;
+        }
+        return MESWISH_OK;
     }
     int64_t nn = (int64_t)n;
     void* args[] = {&xp, &dp, &op, &nn, &k};
@@ -638,6 +679,10 @@ static int run_act(int act, int dtype, const void* x, const void* dy, void* out,
     const Coef k = make_coef(act, p);
     switch (act) {
     case kSwish:
+        // alpha == 1: the backward without the multiply by alpha (the same
+        // results bit for bit, as alpha x = x exactly).
+        if (kBwd && p == 1.0f)
+            return run_dtype<kBwd, kSwishUnit>(dtype, x, dy, out, n, k, s);
         return run_dtype<kBwd, kSwish>(dtype, x, dy, out, n, k, s);
     case kRelu:
         return run_dtype<kBwd, kRelu>(dtype, x, dy, out, n, k, s);
@@ -681,10 +726,12 @@ static int run_group(GroupArgs& g, Coef k, hipStream_t stream)
     if (tiles == 0)
         return MESWISH_OK;
     constexpr int G = kBwd ? MESWISH_GROUP_TILES_BWD : MESWISH_GROUP_TILES_FWD;
-    int64_t grid = grid_for_tiles((tiles + G - 1) / G);
+    int64_t grid = grid_for_tiles((tiles + G - 1) / G, Io<IO>::kBlock);
     void* args[] = {&g, &k};
-    return launch(reinterpret_cast<const void*>(&act_group_kernel<IO, kBwd, kSwish>), grid, args,
-                  stream, Io<IO>::kBlock);
+    const void* fn = kBwd && k.p == 1.0f
+                         ? reinterpret_cast<const void*>(&act_group_kernel<IO, kBwd, kSwishUnit>)
+                         : reinterpret_cast<const void*>(&act_group_kernel<IO, kBwd, kSwish>);
+    return launch(fn, grid, args, stream, Io<IO>::kBlock);
 }
 
 // Common argument checks.  Returns MESWISH_OK or an error code.
@@ -695,6 +742,15 @@ static int check_common(float alpha, int dtype)
     if (!isfinite(alpha))
         return MESWISH_EINVAL;
     return MESWISH_OK;
+}
+
+// Swish's exponent coefficient -alpha log2 e must be a finite binary32
+// value (|alpha| <= about 2.36e38); beyond that the kernels' e^-t = 2^(x C)
+// would take C = -inf.
+static int check_swish_alpha(float alpha)
+{
+    const double c = -(double)alpha * 1.44269504088896340735992468100189214;
+    return isfinite((float)c) ? MESWISH_OK : MESWISH_EINVAL;
 }
 
 static int check_tensor(const void* p, size_t n, size_t esize)
@@ -715,10 +771,12 @@ using namespace meswish;
 namespace meswish {
 
 // Argument checks of one single-tensor call (dy is NULL for the forward).
-static int check_single(const void* x, const void* dy, const void* out, size_t n, float alpha,
-                        int dtype, bool bwd)
+static int check_single(int act, const void* x, const void* dy, const void* out, size_t n,
+                        float alpha, int dtype, bool bwd)
 {
     int rc = check_common(alpha, dtype);
+    if (rc == MESWISH_OK && act == kSwish)
+        rc = check_swish_alpha(alpha);
     if (rc != MESWISH_OK || n == 0)
         return rc;
     size_t es = elem_size(dtype);
@@ -738,7 +796,7 @@ extern "C" int meswish_act_fwd(int act, const void* x, void* y, size_t n, float 
 {
     if (act < 0 || act >= kActCount)
         return MESWISH_EINVAL;
-    int rc = check_single(x, nullptr, y, n, param, dtype, false);
+    int rc = check_single(act, x, nullptr, y, n, param, dtype, false);
     if (rc != MESWISH_OK || n == 0)
         return rc;
     return run_act<false>(act, dtype, x, nullptr, y, n, param, static_cast<hipStream_t>(stream));
@@ -749,7 +807,7 @@ extern "C" int meswish_act_bwd(int act, const void* x, const void* dy, void* dx,
 {
     if (act < 0 || act >= kActCount)
         return MESWISH_EINVAL;
-    int rc = check_single(x, dy, dx, n, param, dtype, true);
+    int rc = check_single(act, x, dy, dx, n, param, dtype, true);
     if (rc != MESWISH_OK || n == 0)
         return rc;
     return run_act<true>(act, dtype, x, dy, dx, n, param, static_cast<hipStream_t>(stream));
@@ -773,7 +831,7 @@ extern "C" int meswish_plan(const void* x, const void* dy, const void* out, size
         return MESWISH_EINVAL;
     memset(plan, 0, sizeof *plan);
     plan->path = MESWISH_PATH_NONE;
-    int rc = check_single(x, dy, out, n, alpha, dtype, bwd != 0);
+    int rc = check_single(kSwish, x, dy, out, n, alpha, dtype, bwd != 0);
     if (rc != MESWISH_OK || n == 0)
         return rc;
     if (dtype == MESWISH_F32)
@@ -836,6 +894,8 @@ extern "C" int swish_fwd_grouped(const meswish_fwd_desc* desc, int count, float 
                                  void* stream)
 {
     int rc = check_common(alpha, dtype);
+    if (rc == MESWISH_OK)
+        rc = check_swish_alpha(alpha);
     if (rc != MESWISH_OK)
         return rc;
     if (count < 0 || (count > 0 && desc == nullptr))
@@ -867,6 +927,8 @@ extern "C" int swish_bwd_grouped(const meswish_bwd_desc* desc, int count, float 
                                  void* stream)
 {
     int rc = check_common(alpha, dtype);
+    if (rc == MESWISH_OK)
+        rc = check_swish_alpha(alpha);
     if (rc != MESWISH_OK)
         return rc;
     if (count < 0 || (count > 0 && desc == nullptr))
@@ -907,7 +969,7 @@ extern "C" int meswish_copy(const void* src, void* dst, size_t bytes, void* stre
     const uint4* s = static_cast<const uint4*>(src);
     uint4* d = static_cast<uint4*>(dst);
     int64_t nvec = (int64_t)(bytes / 16);
-    int64_t grid = grid_for_tiles((nvec + kCopyTileVecs - 1) / kCopyTileVecs);
+    int64_t grid = grid_for_tiles((nvec + kCopyTileVecs - 1) / kCopyTileVecs, kCopyBlock);
     void* args[] = {&s, &d, &nvec};
     return launch(reinterpret_cast<const void*>(&copy16_kernel), grid, args,
                   static_cast<hipStream_t>(stream), kCopyBlock);
@@ -919,8 +981,8 @@ extern "C" const char* meswish_strerror(int status)
     case MESWISH_OK:
         return "success";
     case MESWISH_EINVAL:
-        return "invalid argument (null or misaligned pointer, unknown dtype, non-finite alpha, "
-               "bad count or size)";
+        return "invalid argument (null or misaligned pointer, unknown dtype, non-finite alpha "
+               "or Swish alpha beyond 2.3586e38, bad count or size)";
     case MESWISH_EALIAS:
         return "an output partially overlaps an input or another output";
     case MESWISH_EHIP:

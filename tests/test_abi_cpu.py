@@ -124,6 +124,19 @@ def test_rejections_before_launch(lib):
     assert lib.meswish_act_bwd(-1, None, None, None, 16, 1.0, _lib.F32, None) == _lib.EINVAL
     assert lib.meswish_act_fwd(2, None, None, 16, nan, _lib.F32, None) == _lib.EINVAL
     assert lib.meswish_act_fwd(4, None, None, 0, 1.0, _lib.BF16, None) == _lib.OK
+    # Swish alpha whose exponent coefficient -alpha log2 e is not a finite
+    # binary32 value (|alpha| > FLT_MAX / log2 e = 2.3586e38); a slope that
+    # large is fine for LeakyReLU, which has no exponent.
+    for a in (3e38, -3e38, 2.36e38):
+        assert lib.swish_fwd(None, None, 0, a, _lib.F32, None) == _lib.EINVAL, a
+        assert lib.swish_bwd(None, None, None, 0, a, _lib.BF16, None) == _lib.EINVAL, a
+        assert lib.meswish_act_bwd(0, None, None, None, 0, a, _lib.F32, None) == _lib.EINVAL, a
+        assert lib.swish_fwd_grouped(None, 0, a, _lib.F32, None) == _lib.EINVAL, a
+        assert lib.swish_bwd_grouped(None, 0, a, _lib.BF16, None) == _lib.EINVAL, a
+        assert lib.meswish_act_fwd(2, None, None, 0, a, _lib.F32, None) == _lib.OK, a
+    for a in (2.358e38, -2.358e38, 40.0):
+        assert lib.swish_fwd(None, None, 0, a, _lib.F32, None) == _lib.OK, a
+        assert lib.swish_bwd_grouped(None, 0, a, _lib.BF16, None) == _lib.OK, a
     # Copy helper: misaligned or odd sizes.
     assert lib.meswish_copy(None, None, 0, None) == _lib.OK
     assert lib.meswish_copy(None, None, 16, None) == _lib.EINVAL

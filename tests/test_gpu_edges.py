@@ -83,6 +83,32 @@ def test_scaled_exponent_branch(alpha, oracle):
     assert rb["ok"], rb
 
 
+@pytest.mark.parametrize("alpha", [2.358e38, -2.358e38])
+def test_largest_alpha(alpha, oracle):
+    """alpha just inside the accepted range (|alpha log2 e| finite in
+    binary32): zero, tiny and subnormal x (where alpha x is still moderate),
+    and everything out to +-FLT_MAX; beyond it the call is rejected."""
+    tiny = np.array([0.0, -0.0, 1e-38, -1e-38, 3e-39, -3e-39, 1e-45, -1e-45, 5e-40, -7e-41],
+                    dtype=np.float32)
+    rng = np.random.default_rng(29)
+    x = np.concatenate([tiny, rng.uniform(-1e-37, 1e-37, 4000),
+                        rng.standard_normal(4000) * 10.0 ** rng.integers(-45, 38, 4000)]).astype(np.float32)
+    x = x[np.isfinite(x)]
+    dy = rng.standard_normal(x.size).astype(np.float32)
+    rf, rb = _check(x, dy, alpha, oracle)
+    say(f"[edges] alpha={alpha:g}: fwd {rf} bwd {rb}")
+    assert rf["ok"], rf
+    assert rb["ok"], rb
+    rf, rb = _check(inputs.encode(x, "bf16"), inputs.encode(dy, "bf16"), alpha, oracle)
+    assert rf["ok"], rf
+    assert rb["ok"], rb
+    xd = to_dev(x)
+    with pytest.raises(mea.MeswishError):
+        mea.swish_fwd(xd, 3e38)
+    with pytest.raises(mea.MeswishError):
+        mea.swish_bwd(xd, xd, -2.4e38)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_lengths_and_misalignment(dtype, oracle):
     rng = np.random.default_rng(5)

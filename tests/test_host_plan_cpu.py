@@ -28,23 +28,42 @@ def plan(lib, x, dy, out, n, dtype, bwd, alpha=1.0):
     return st, p
 
 
+# Tiles per launch of the vector kernel (the library's kMaxLaunchTiles).
+LAUNCH_TILES = 1 << 30
+
+
 def covered(p, n, esize):
-    """Element indices the vector kernel touches, by the kernel's arithmetic."""
+    """Element indices the kernels touch, by the kernels' own arithmetic:
+    launch c of the vector path covers tiles [c L, (c + 1) L) of the body
+    (L = LAUNCH_TILES) from a pointer at the start of its part; block b takes
+    tiles b, b + grid, ... of its launch; the first launch also does the
+    head and the last the tail."""
     E, TV = p.elems_per_vector, p.vectors_per_tile
     seen = np.zeros(n, dtype=np.int32)
     if p.path == _lib.PATH_VECTOR:
-        for b in range(p.grid):
-            t0 = b * TV
-            while t0 < p.nvec:
-                for thread in range(p.block):
-                    for u in range(TV // p.block):
-                        v = t0 + thread + u * p.block
-                        if v < p.nvec:
-                            seen[p.head + v * E: p.head + (v + 1) * E] += 1
-                t0 += p.grid * TV
-        for thread in range(p.head + p.tail):
-            i = thread if thread < p.head else p.head + p.nvec * E + (thread - p.head)
-            seen[i] += 1
+        done = 0
+        for c in range(p.launches):
+            nt = min(p.tiles - c * LAUNCH_TILES, LAUNCH_TILES)
+            vecs = min(nt * TV, p.nvec - c * LAUNCH_TILES * TV)
+            last_vecs = vecs - (nt - 1) * TV if nt else 0
+            head = p.head if c == 0 else 0
+            tail = p.tail if c + 1 == p.launches else 0
+            base = 0 if c == 0 else p.head + done   # element offset of the launch's pointer
+            for b in range(p.grid):
+                t = b
+                while t < nt:
+                    nv = TV if t + 1 < nt else last_vecs
+                    for thread in range(p.block):
+                        for u in range(TV // p.block):
+                            v = thread + u * p.block
+                            if v < nv:
+                                e0 = base + head + (t * TV + v) * E
+                                seen[e0:e0 + E] += 1
+                    t += p.grid
+            for thread in range(head + tail):
+                i = thread if thread < head else head + vecs * E + (thread - head)
+                seen[base + i] += 1
+            done += vecs * E
     else:
         for b in range(p.grid):
             i = b * p.block
@@ -88,6 +107,7 @@ def test_plan_splits_and_covers(lib, dtype, esize, bwd):
                 assert p.path == _lib.PATH_ELEMENT and p.tail == n
                 assert p.tiles == -(-n // p.vectors_per_tile)
             assert 1 <= p.grid <= max(p.tiles, 1)
+            assert p.launches == 1
             if n <= 4096 * 3 + 5:
                 seen = covered(p, n, esize)
                 assert (seen == 1).all(), (n, ox, od, oo, p.path)
@@ -119,3 +139,26 @@ def test_plan_rejections_match_the_calls(lib):
     st, p = plan(lib, x, None, y, 0, _lib.F32, 0)
     assert st == _lib.OK and p.path == _lib.PATH_NONE
     assert lib.meswish_plan(x, None, y, 16, 1.0, _lib.F32, 0, None) == _lib.EINVAL
+
+
+@pytest.mark.parametrize("bwd", [0, 1])
+def test_plan_grid_stays_below_the_thread_limit(lib, bwd):
+    """grid x block must stay below 2^32 threads (the launch limit) for any
+    n the header accepts: bfloat16 of 2^32 elements on the element path,
+    2^35 + 2^20 on the vector path, and past 2^30 tiles (several launches)."""
+    es = 2
+    span = 1 << 46   # fake buffers far apart: no overlap for these sizes
+    x, dy, out = BASE, BASE + span, BASE + 2 * span
+    cases = [(x + 2, dy + 2 if bwd else None, out, 1 << 32, _lib.PATH_ELEMENT),
+             (x, dy if bwd else None, out, (1 << 35) + (1 << 20), _lib.PATH_VECTOR),
+             (x, dy if bwd else None, out, 1 << 42, _lib.PATH_VECTOR)]
+    for xp, dp, op, n, path in cases:
+        st, p = plan(lib, xp, dp, op, n, _lib.BF16, bwd)
+        assert st == _lib.OK and p.path == path, (n, st, p.path)
+        assert p.grid * p.block < (1 << 32), (n, p.grid, p.block)
+        if path == _lib.PATH_VECTOR:
+            assert p.head + p.nvec * p.elems_per_vector + p.tail == n
+            assert p.launches == -(-p.tiles // LAUNCH_TILES)
+            assert p.grid <= min(p.tiles, LAUNCH_TILES)
+    # Past 2^30 tiles: 2^42 bfloat16 elements are 2^31 tiles of 2048, two launches.
+    assert plan(lib, x, dy if bwd else None, out, 1 << 42, _lib.BF16, bwd)[1].launches == 2
