@@ -411,219 +411,11 @@ __global__ __launch_bounds__(InvTile<N>::kThreads) void c2r_kernel(const float2*
 // with optional conjugation of A or B.
 // ---------------------------------------------------------------------------
 
-constexpr int kBM = 64, kBN = 64, kBK = 16;
-
-template <bool AK, bool BK, bool CA, bool CB>
-__global__ __launch_bounds__(kThreads) void cgemm_kernel(const float2* __restrict__ A,
-                                                         const float2* __restrict__ B,
-                                                         float2* __restrict__ C, int M, int N,
-                                                         int K, int64_t sAp, int64_t sBp,
-                                                         int lda, int ldb)
-{
-    __shared__ float2 As[kBK][kBM + 1];
-    __shared__ float2 Bs[kBK][kBN + 1];
-    const int p = blockIdx.z;
-    const int i0 = blockIdx.y * kBM, j0 = blockIdx.x * kBN;
-    const float2* Ap = A + p * sAp;
-    const float2* Bp = B + p * sBp;
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    float2 acc[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-            acc[a][b] = make_float2(0.0f, 0.0f);
-
-    for (int k0 = 0; k0 < K; k0 += kBK) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int idx = threadIdx.x + r * kThreads;
-            int i, k;
-            if (AK) {
-                i = idx / kBK;
-                k = idx % kBK;
-            } else {
-                k = idx / kBM;
-                i = idx % kBM;
-            }
-            float2 v = make_float2(0.0f, 0.0f);
-            if (i0 + i < M && k0 + k < K)
-                v = AK ? Ap[(int64_t)(i0 + i) * lda + (k0 + k)] : Ap[(int64_t)(k0 + k) * lda + (i0 + i)];
-            As[k][i] = CA ? conjf2(v) : v;
-            int j;
-            if (BK) {
-                j = idx / kBK;
-                k = idx % kBK;
-            } else {
-                k = idx / kBN;
-                j = idx % kBN;
-            }
-            float2 w = make_float2(0.0f, 0.0f);
-            if (j0 + j < N && k0 + k < K)
-                w = BK ? Bp[(int64_t)(j0 + j) * ldb + (k0 + k)] : Bp[(int64_t)(k0 + k) * ldb + (j0 + j)];
-            Bs[k][j] = CB ? conjf2(w) : w;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < kBK; ++k) {
-            float2 a[4], b[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                a[r] = As[k][ty * 4 + r];
-                b[r] = Bs[k][tx * 4 + r];
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    acc[r][c].x = fmaf(a[r].x, b[c].x, acc[r][c].x);
-                    acc[r][c].x = fmaf(-a[r].y, b[c].y, acc[r][c].x);
-                    acc[r][c].y = fmaf(a[r].x, b[c].y, acc[r][c].y);
-                    acc[r][c].y = fmaf(a[r].y, b[c].x, acc[r][c].y);
-                }
-        }
-        __syncthreads();
-    }
-    float2* Cp = C + (int64_t)p * M * N;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int i = i0 + ty * 4 + r;
-        if (i >= M)
-            continue;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int j = j0 + tx * 4 + c;
-            if (j < N)
-                Cp[(int64_t)i * N + j] = acc[r][c];
-        }
-    }
-}
-
-// The same product on the matrix cores.  A complex K-sum is a real sum over
-// 2K terms: with A' = [Re A, Im A] interleaved along k and, for every
-// complex B[k][n], the real 2 x 2 block [[Re B, Im B], [-Im B, Re B]] at
-// rows (2k, 2k+1) and columns (2n, 2n+1) of B', the real product A' B'
-// holds Re C at even and Im C at odd columns.  Each wave owns 32 rows and
-// 32 complex columns (two 32 x 32 real tiles of v_mfma_f32_32x32x2f32);
-// lane l feeds A'[l%32][l/32] and B'[l/32][l%32] and receives, in
-// accumulator v, C'[8 (v/4) + 4 (l/32) + v%4][l%32].
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-//
-// Grid: one dimension, XCD-aware.  The dispatcher deals consecutive blocks to
-// the 8 XCDs in turn, and each XCD has its own L2.  The tiles of one bin
-// share their A and B operands, so all of them go to one XCD: block L has
-// XCD x = L % 8 and q = L / 8; it computes tile q % tiles of bin
-// (q / tiles) * 8 + x.  Bins past the last (padding to a multiple of 8)
-// exit at once.
-template <bool AK, bool BK, bool CA, bool CB>
-__global__ __launch_bounds__(kThreads) void cgemm_mfma_kernel(const float2* __restrict__ A,
-                                                              const float2* __restrict__ B,
-                                                              float2* __restrict__ C, int M,
-                                                              int N, int K, int64_t sAp,
-                                                              int64_t sBp, int lda, int ldb,
-                                                              int tiles_n, int tiles, int nbins)
-{
-    __shared__ float2 As[kBK][kBM + 1];
-    __shared__ float2 Bs[kBK][kBN + 1];
-    const int xcd = (int)(blockIdx.x & 7u), q = (int)(blockIdx.x >> 3);
-    const int p = (q / tiles) * 8 + xcd;
-    if (p >= nbins)
-        return;
-    const int tile = q % tiles;
-    const int i0 = (tile / tiles_n) * kBM, j0 = (tile % tiles_n) * kBN;
-    const float2* Ap = A + p * sAp;
-    const float2* Bp = B + p * sBp;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int r = lane & 31, h = lane >> 5;
-    f32x16 acc0 = {0}, acc1 = {0};
-
-    // Global -> register staging of one K-tile (4 A and 4 B values per
-    // thread); the next tile's loads are issued before the current tile's
-    // products, so their latency overlaps the matrix-core work.
-    float2 ra[4], rb[4];
-    auto fetch = [&](int k0) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int idx = threadIdx.x + q * kThreads;
-            int i, k;
-            if (AK) {
-                i = idx / kBK;
-                k = idx % kBK;
-            } else {
-                k = idx / kBM;
-                i = idx % kBM;
-            }
-            float2 v = make_float2(0.0f, 0.0f);
-            if (i0 + i < M && k0 + k < K)
-                v = AK ? Ap[(int64_t)(i0 + i) * lda + (k0 + k)] : Ap[(int64_t)(k0 + k) * lda + (i0 + i)];
-            ra[q] = CA ? conjf2(v) : v;
-            int j;
-            if (BK) {
-                j = idx / kBK;
-                k = idx % kBK;
-            } else {
-                k = idx / kBN;
-                j = idx % kBN;
-            }
-            float2 w = make_float2(0.0f, 0.0f);
-            if (j0 + j < N && k0 + k < K)
-                w = BK ? Bp[(int64_t)(j0 + j) * ldb + (k0 + k)] : Bp[(int64_t)(k0 + k) * ldb + (j0 + j)];
-            rb[q] = CB ? conjf2(w) : w;
-        }
-    };
-    auto stash = [&]() {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int idx = threadIdx.x + q * kThreads;
-            if (AK)
-                As[idx % kBK][idx / kBK] = ra[q];
-            else
-                As[idx / kBM][idx % kBM] = ra[q];
-            if (BK)
-                Bs[idx % kBK][idx / kBK] = rb[q];
-            else
-                Bs[idx / kBN][idx % kBN] = rb[q];
-        }
-    };
-
-    fetch(0);
-    for (int k0 = 0; k0 < K; k0 += kBK) {
-        stash();
-        __syncthreads();
-        if (k0 + kBK < K)
-            fetch(k0 + kBK);
-#pragma unroll
-        for (int kk = 0; kk < kBK; ++kk) {
-            const float2 a = As[kk][wm * 32 + r];
-            const float av = h ? a.y : a.x;
-            const float2 b0 = Bs[kk][wn * 32 + (r >> 1)];
-            const float2 b1 = Bs[kk][wn * 32 + 16 + (r >> 1)];
-            const float bv0 = h ? ((r & 1) ? b0.x : -b0.y) : ((r & 1) ? b0.y : b0.x);
-            const float bv1 = h ? ((r & 1) ? b1.x : -b1.y) : ((r & 1) ? b1.y : b1.x);
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv0, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv1, acc1, 0, 0, 0);
-        }
-        __syncthreads();
-    }
-    float* Cf = reinterpret_cast<float*>(C + (int64_t)p * M * N);
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int i = i0 + wm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (i >= M)
-            continue;
-        const int n0 = j0 + wn * 32 + (r >> 1);
-        const int n1 = n0 + 16;
-        if (n0 < N)
-            Cf[2 * ((int64_t)i * N + n0) + (r & 1)] = acc0[v];
-        if (n1 < N)
-            Cf[2 * ((int64_t)i * N + n1) + (r & 1)] = acc1[v];
-    }
-}
-
-// The planar form of the same product: real and imaginary parts in separate
-// LDS planes, and one MFMA k-step takes two complex k.  Per pair of k:
+// The products run on the matrix cores with planar operands: real and
+// imaginary parts in separate LDS planes, and one MFMA k-step takes two
+// complex k.  Per pair of k:
 //   Re C += Re A Re B - Im A Im B,   Im C += Re A Im B + Im A Re B
 // as four v_mfma_f32_32x32x2f32 on accumulators acc_re, acc_im; no
 // per-lane selects, a third of the LDS bytes of the interleaved form.  Lane
@@ -764,11 +556,6 @@ void cgemm_planar_kernel(const float2* __restrict__ A,
 // Host side.
 // ---------------------------------------------------------------------------
 
-// Per-bin products: 2 = matrix cores, planar operands; 1 = matrix cores,
-// interleaved 2 x 2 blocks; 0 = vector ALUs.
-#ifndef FFTCONV_MFMA
-#define FFTCONV_MFMA 2
-#endif
 
 static bool n_ok(int n) { return n == 8 || n == 16 || n == 32 || n == 64; }
 
@@ -842,9 +629,6 @@ static int launch_cmul(int op, const float2* a, const float2* b, float2* c, int 
     } else {
         M = fo; N = f; K = S; sAp = (int64_t)S * fo; sBp = (int64_t)S * f; lda = fo; ldb = f;
     }
-    [[maybe_unused]] const int tiles_n = (N + kBN - 1) / kBN;
-    [[maybe_unused]] const int tiles_m = (M + kBM - 1) / kBM;
-#if FFTCONV_MFMA == 2
     // 32-column block tiles where they pad less than 64-column ones.
 #ifndef FFTCONV_PLANAR_WC
     const int wc = ((N + 63) / 64 * 64 - N > (N + 31) / 32 * 32 - N) ? 1 : 2;
@@ -880,33 +664,6 @@ static int launch_cmul(int op, const float2* a, const float2* b, float2* c, int 
     else
         FFTCONV_PLANAR(false, false, true, false);
 #undef FFTCONV_PLANAR
-#elif FFTCONV_MFMA == 1
-    const int tiles = tiles_n * tiles_m;
-    const int64_t blocks = (int64_t)((nbins + 7) / 8) * 8 * tiles;
-    if (blocks > 0x7FFFFFFF)
-        return MESWISH_EINVAL;
-    dim3 grid((unsigned)blocks);
-    if (op == 0)
-        hipLaunchKernelGGL((cgemm_mfma_kernel<true, true, false, true>), grid, dim3(kThreads), 0, s,
-                           a, b, c, M, N, K, sAp, sBp, lda, ldb, tiles_n, tiles, nbins);
-    else if (op == 1)
-        hipLaunchKernelGGL((cgemm_mfma_kernel<true, false, false, false>), grid, dim3(kThreads), 0,
-                           s, a, b, c, M, N, K, sAp, sBp, lda, ldb, tiles_n, tiles, nbins);
-    else
-        hipLaunchKernelGGL((cgemm_mfma_kernel<false, false, true, false>), grid, dim3(kThreads), 0,
-                           s, a, b, c, M, N, K, sAp, sBp, lda, ldb, tiles_n, tiles, nbins);
-#else
-    dim3 grid((unsigned)tiles_n, (unsigned)tiles_m, (unsigned)nbins);
-    if (op == 0)
-        hipLaunchKernelGGL((cgemm_kernel<true, true, false, true>), grid, dim3(kThreads), 0, s, a, b,
-                           c, M, N, K, sAp, sBp, lda, ldb);
-    else if (op == 1)
-        hipLaunchKernelGGL((cgemm_kernel<true, false, false, false>), grid, dim3(kThreads), 0, s, a,
-                           b, c, M, N, K, sAp, sBp, lda, ldb);
-    else
-        hipLaunchKernelGGL((cgemm_kernel<false, false, true, false>), grid, dim3(kThreads), 0, s, a,
-                           b, c, M, N, K, sAp, sBp, lda, ldb);
-#endif
     return status_of(hipGetLastError());
 }
 
