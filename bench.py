@@ -75,7 +75,18 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD public specification
 KERNEL_SOURCES = [os.path.join(ROOT, "memory_efficient_activation_amd", "csrc", f)
                   for f in ("meswish.hip", "act_math.h")]
 SETS = 4
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "swish_bwd_bf16_8x2048x4096_traffic.md")
+# rocprofv3 counter summaries of the Swish backward, per workload.
+TRAFFIC_PROFILES = {
+    3: os.path.join(ROOT, "profiles", "swish_bwd_bf16_8x2048x4096_traffic.md"),
+    4: os.path.join(ROOT, "profiles", "swish_bwd_f32_8x2048x4096_alpha1.5_traffic.md"),
+}
+# How each single-tensor workload draws its values (memory_efficient_activation_amd/inputs.py).
+RECIPES = {
+    1: ("3*N(0,1) seed 0", "N(0,1) seed 1"),
+    2: ("N(0,1) seed 0", "N(0,1) seed 1"),
+    3: ("N(0,1) seed 0", "0.01*N(0,1) seed 1"),
+    4: ("99% N(0,1), 1% +-U(20,90), seed 0", "N(0,1) seed 1"),
+}
 FAMILY = ["swish", "relu", "leaky_relu", "sigmoid", "tanh", "gelu", "gelu_tanh"]
 ORACLE_NAME = {"gelu": "gelu_erf"}
 # Flops per element of each activation as "What activations cost, in memory
@@ -108,6 +119,15 @@ def parse_args():
                         "transient that follows the start of a sustained load)")
     p.add_argument("--act", default="swish", choices=FAMILY + ["all"],
                    help="activation to measure (default swish, the headline)")
+    p.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5],
+                   help="Swish workload (default 3, the headline bf16 [8,2048,4096]); "
+                        "1, 2 and 4 are the binary32 workloads, 5 the grouped launch")
+    p.add_argument("--report", action="store_true",
+                   help="per-launch protocol instead: one JSON line per workload and "
+                        "direction (median and p10/p90 of scrubbed launches, hot launches, "
+                        "copy ceiling, errors against the oracle, band counts, CPU times)")
+    p.add_argument("--report-reps", type=int, default=100,
+                   help="timed launches per direction in --report (1000 for workload 1)")
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the CPU oracle timing (profiling runs)")
     p.add_argument("--no-extras", action="store_true",
@@ -134,12 +154,14 @@ def source_sha256() -> str:
     return h.hexdigest()
 
 
-def traffic_from_profile():
+def traffic_from_profile(cfg: int):
     """HBM bytes per backward launch measured by rocprofv3 counters, if the
-    committed summary was taken on the current kernel sources."""
-    if not os.path.exists(TRAFFIC_PROFILE):
-        return None, "no counter summary"
-    text = open(TRAFFIC_PROFILE).read()
+    committed summary for workload cfg was taken on the current kernel
+    sources."""
+    path = TRAFFIC_PROFILES.get(cfg)
+    if path is None or not os.path.exists(path):
+        return None, "no counter summary for this workload"
+    text = open(path).read()
     m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
     m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not (m_sha and m_b):
@@ -157,7 +179,10 @@ class Rig:
         self.n = w.numel
 
         def to_dev(a):
-            return torch.from_numpy(a).view(torch.int16).view(torch.bfloat16).to(dev)
+            t = torch.from_numpy(a)
+            if a.dtype.name == "uint16":
+                t = t.view(torch.int16).view(torch.bfloat16)
+            return t.to(dev)
 
         # Kernel number k (forward and backward alternate) uses set k % SETS,
         # so no kernel reads memory that any of the previous SETS - 1 kernels
@@ -191,9 +216,11 @@ class Rig:
 def measure(args, act, rig, w, lib, torch):
     from memory_efficient_activation_amd import _lib, accounting
 
-    n, dtype = w.numel, w.dtype
+    n, dtype, cfg = w.numel, w.dtype, w.index
     param = w.alpha if act == "swish" else _lib.DEFAULT_PARAM.get(act, 0.0)
-    code, dt = _lib.ACTS[act], _lib.BF16
+    code, dt = _lib.ACTS[act], (_lib.BF16 if dtype == "bf16" else _lib.F32)
+    esize = 2 if dtype == "bf16" else 4
+    shape = "[" + ",".join(str(d) for d in w.shapes[0]) + "]"
     ptrs, sh = rig.ptrs, rig.sh
 
     def fwd(j):
@@ -226,12 +253,25 @@ def measure(args, act, rig, w, lib, torch):
     bwd_gbps = bwd_b / (bwd_us * 1e-6) / 1e9
     fwd_gbps = fwd_b / (fwd_us * 1e-6) / 1e9
     value = step_b * K / wall / 1e9
-    headline = act == "swish"
-    traffic, traffic_note = traffic_from_profile() if headline else (None, "counters taken for Swish")
+    headline = act == "swish" and cfg == 3
+    traffic, traffic_note = (traffic_from_profile(cfg) if act == "swish"
+                             else (None, "counters taken for Swish"))
+    if headline:
+        metric = METRIC
+    elif cfg == 3:
+        metric = f"HBM GB/s + fraction of peak, {act} fwd+bwd, 67M-elem bf16, 1 MI355X"
+    else:
+        metric = (f"HBM GB/s + fraction of peak, Swish fwd+bwd, {n}-elem {dtype} "
+                  f"{shape} alpha={param:g}, 1 MI355X")
+    xr, dr = RECIPES[cfg]
+    notes = {1: "256 KiB per tensor: the launches are latency-bound and the tensors stay in "
+                "the caches (a parity-size workload, not a bandwidth figure)",
+             2: "stands in for an EfficientNet stem activation (the blog post's measured "
+                "networks are not available)",
+             4: "about 0.46 % of the elements take the rare branch (|alpha x| > 86.6)"}
 
     result = {
-        "metric": METRIC if headline else
-        f"HBM GB/s + fraction of peak, {act} fwd+bwd, 67M-elem bf16, 1 MI355X",
+        "metric": metric,
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -242,18 +282,18 @@ def measure(args, act, rig, w, lib, torch):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "io_dtype": "bf16",
+        "io_dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": f"{act} fwd+bwd, bf16 [8,2048,4096] (67,108,864 elements)"
-                               + (", alpha=1.0" if headline else ""),
-                   "n": n, "param": param, "bytes_per_step": step_b,
-                   "x": "N(0,1) seed 0", "dy": "0.01*N(0,1) seed 1", "buffer_sets": SETS},
+        "config": {"workload": f"{act} fwd+bwd, {dtype} {shape} ({n:,} elements)"
+                               + (f", alpha={param:g}" if act == "swish" else ""),
+                   "config_index": cfg, "n": n, "param": param, "bytes_per_step": step_b,
+                   "x": xr, "dy": dr, "buffer_sets": SETS},
         "frac_peak": round(value / PEAK_HBM_GBPS, 4),
         "elements_per_s": round(n * K / wall, 1),
         "gpu_ms_per_step_events": round(gpu_ms / K, 5),
         "fwd": {"bytes": fwd_b, "mean_us": round(fwd_us, 2), "GBps": round(fwd_gbps, 1)},
         "bwd": {"bytes": bwd_b, "mean_us": round(bwd_us, 2), "GBps": round(bwd_gbps, 1)},
-        "roofline": {"kernel": f"act_vec_kernel<bf16, bwd, {act}>", "bound": "hbm",
+        "roofline": {"kernel": f"act_vec_kernel<{dtype}, bwd, {act}>", "bound": "hbm",
                      "achieved": round(bwd_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(bwd_gbps / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "traffic_note": traffic_note,
@@ -263,16 +303,18 @@ def measure(args, act, rig, w, lib, torch):
                            "naive_3_maps": accounting.retained_bytes(n, dtype, naive=True)},
     }
 
+    if cfg in notes:
+        result["config"]["note"] = notes[cfg]
     if not args.no_extras:
         def copy(j):
             xp, _, yp, _ = ptrs[j % SETS]
-            _lib.check(lib.meswish_copy(xp, yp, 2 * n, sh), "meswish_copy")
+            _lib.check(lib.meswish_copy(xp, yp, esize * n, sh), "meswish_copy")
         for i in range(5):
             copy(i)
         _, cms = rig.region(copy, K)
         copy_us = cms * 1e3 / K
-        copy_gbps = 2 * (2 * n) / (copy_us * 1e-6) / 1e9
-        result["copy_ceiling"] = {"bytes": 4 * n, "mean_us": round(copy_us, 2),
+        copy_gbps = 2 * (esize * n) / (copy_us * 1e-6) / 1e9
+        result["copy_ceiling"] = {"bytes": 2 * esize * n, "mean_us": round(copy_us, 2),
                                   "GBps": round(copy_gbps, 1),
                                   "bwd_frac_of_copy": round(bwd_gbps / copy_gbps, 4),
                                   "value_frac_of_copy": round(value / copy_gbps, 4)}
@@ -824,6 +866,187 @@ def measure_grouped(args, lib, torch, dev):
     return result
 
 
+# Stationary point of Swish' in t = alpha x: 1 + t (1 - sigma(t)) = 0 at
+# t0 = -(1 + W(1/e)); results near it cancel (their error is judged against
+# the size of the terms).
+T0_SWISH_GRAD = -1.2784645427610738
+SCRUB_BYTES = 1 << 30   # 4x the 256 MB Infinity Cache
+
+
+def _pct(v, q):
+    v = sorted(v)
+    return v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+
+
+def measure_report(args, lib, torch, dev, cfgs):
+    """The per-launch protocol, one JSON line per workload and direction.
+
+    For each direction: W warm launches, then R launches timed one by one
+    with a HIP event pair each on the launch stream, every one preceded
+    (outside its pair) by a read of a 1 GiB buffer that evicts the caches;
+    the median and p10/p90 of those times give GB/s.  Also: the same R
+    launches back to back without the fill ("hot"), the 16-byte copy kernel
+    over one tensor under the same protocol (the practical ceiling), the
+    GPU results against the oracle (largest error under the parity rule,
+    elements beyond it), the counts of the two hazard bands (subnormal
+    outputs; |alpha x - t0| < 0.05 in the backward), and the oracle's time
+    on the host: all threads (median of 3) and one thread (on the first
+    2^22 elements, scaled)."""
+    import numpy as np
+    from memory_efficient_activation_amd import _lib, accounting, inputs
+    import oracle
+    from oracle.compare import bf16_report, f32_report
+
+    orc = oracle.Oracle()
+    threads = len(os.sched_getaffinity(0))
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    scrub = torch.zeros(SCRUB_BYTES // 4, dtype=torch.float32, device=dev)
+
+    def to_dev(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if a.dtype == np.uint16:
+            t = t.view(torch.int16).view(torch.bfloat16)
+        return t.to(dev)
+
+    def to_host(t):
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+
+    def timed(fn, reps, scrubbed):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            if scrubbed:
+                # Read, not write: a read pass leaves the caches holding
+                # clean lines, so the timed kernel pays no write-back of
+                # the scrub's own data (a fill of the buffer left up to
+                # 256 MB of dirty lines, written back inside the timed pair).
+                scrub.sum()
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) * 1e3 for a, b in evs]   # microseconds
+
+    out = []
+    for c in cfgs:
+        w = inputs.make(c)
+        dt = _lib.BF16 if w.dtype == "bf16" else _lib.F32
+        esize = 2 if w.dtype == "bf16" else 4
+        n, alpha = w.numel, float(w.alpha)
+        reps = args.report_reps * (10 if c == 1 else 1)
+        xs = [to_dev(a) for a in w.xs]
+        dys = [to_dev(a) for a in w.dys]
+        ys = [torch.empty_like(x) for x in xs]
+        dxs = [torch.empty_like(x) for x in xs]
+        if c == 5:
+            fd = (_lib.FwdDesc * len(xs))(*[_lib.FwdDesc(x.data_ptr(), y.data_ptr(), x.numel())
+                                            for x, y in zip(xs, ys)])
+            bd = (_lib.BwdDesc * len(xs))(*[_lib.BwdDesc(x.data_ptr(), d.data_ptr(), g.data_ptr(),
+                                                         x.numel()) for x, d, g in zip(xs, dys, dxs)])
+
+            def fwd():
+                _lib.check(lib.swish_fwd_grouped(fd, len(xs), alpha, dt, sh), "swish_fwd_grouped")
+
+            def bwd():
+                _lib.check(lib.swish_bwd_grouped(bd, len(xs), alpha, dt, sh), "swish_bwd_grouped")
+        else:
+            x, dy, y, dx = xs[0], dys[0], ys[0], dxs[0]
+
+            def fwd():
+                _lib.check(lib.swish_fwd(x.data_ptr(), y.data_ptr(), n, alpha, dt, sh), "swish_fwd")
+
+            def bwd():
+                _lib.check(lib.swish_bwd(x.data_ptr(), dy.data_ptr(), dx.data_ptr(), n, alpha, dt, sh),
+                           "swish_bwd")
+        csrc = torch.empty(n * esize, dtype=torch.uint8, device=dev)
+        cdst = torch.empty_like(csrc)
+
+        def copy():
+            _lib.check(lib.meswish_copy(csrc.data_ptr(), cdst.data_ptr(), n * esize, sh), "meswish_copy")
+
+        for _ in range(5):
+            fwd()
+            bwd()
+            copy()
+        t_copy = timed(copy, reps, True)
+        copy_med = statistics.median(t_copy)
+        copy_gbps = 2 * n * esize / (copy_med * 1e-6) / 1e9
+        # The oracle on the same inputs: values for the errors, and times.
+        x64 = np.concatenate([inputs.decode(a).astype(np.float64) for a in w.xs])
+        for direction, fn in (("fwd", fwd), ("bwd", bwd)):
+            t_s = timed(fn, reps, True)
+            t_h = timed(fn, reps, False)
+            nbytes = (accounting.fwd_bytes(n, w.dtype) if direction == "fwd"
+                      else accounting.bwd_bytes(n, w.dtype))
+            med = statistics.median(t_s)
+            got = np.concatenate([to_host(t).ravel() for t in (ys if direction == "fwd" else dxs)])
+
+            def run_oracle(th, k=None):
+                if direction == "fwd":
+                    return [orc.fwd(a[:k], alpha, threads=th) for a in w.xs]
+                return [orc.bwd(a[:k], d[:k], alpha, threads=th, want_scale=k is None)
+                        for a, d in zip(w.xs, w.dys)]
+
+            cpu_t = []
+            for _ in range(3):
+                c0 = time.perf_counter()
+                res = run_oracle(threads)
+                cpu_t.append(time.perf_counter() - c0)
+            k1 = 1 << 22
+            done = sum(min(a.size, k1) for a in w.xs)
+            c0 = time.perf_counter()
+            run_oracle(1, k1)
+            t1 = (time.perf_counter() - c0) * n / done
+            if direction == "fwd":
+                want = np.concatenate([r.ravel() for r in res])
+                scale = None
+            else:
+                want = np.concatenate([r[0].ravel() for r in res])
+                scale = np.concatenate([r[1].ravel() for r in res])
+            rep = (bf16_report(got, want) if w.dtype == "bf16" else f32_report(got, want, scale))
+            wv = inputs.decode(want).astype(np.float64)
+            bands = {"subnormal_outputs": int(np.count_nonzero((wv != 0) & (np.abs(wv) < 2.0 ** -126)))}
+            if direction == "bwd":
+                bands["near_t0"] = int(np.count_nonzero(np.abs(alpha * x64 - T0_SWISH_GRAD) < 0.05))
+            cpu_med = statistics.median(cpu_t)
+            line = {
+                "report": "per-launch protocol", "config_index": c, "direction": direction,
+                "workload": w.name, "io_dtype": w.dtype, "n": n, "bytes": nbytes, "reps": reps,
+                "t_median_us": round(med, 2), "t_p10_us": round(_pct(t_s, 0.1), 2),
+                "t_p90_us": round(_pct(t_s, 0.9), 2),
+                "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
+                "frac_peak": round(nbytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                "hot": {"t_median_us": round(statistics.median(t_h), 2),
+                        "GBps": round(nbytes / (statistics.median(t_h) * 1e-6) / 1e9, 1),
+                        "note": "back to back, no cache scrub"},
+                "copy": {"bytes": 2 * n * esize, "t_median_us": round(copy_med, 2),
+                         "GBps": round(copy_gbps, 1)},
+                "frac_copy": round(nbytes / (med * 1e-6) / 1e9 / copy_gbps, 4),
+                "elems_per_s": round(n / (med * 1e-6), 1),
+                "retained_bytes": {"memory_efficient": accounting.retained_bytes(n, w.dtype),
+                                   "naive_3_maps": accounting.retained_bytes(n, w.dtype, naive=True)},
+                "max_err": ({"max_ulp": rep["max_ulp"], "n_off_by_one": rep["n_off_by_one"]}
+                            if w.dtype == "bf16" else {"max_rel": rep["max_rel"]}),
+                "n_bad": rep["n_bad"], "parity_ok": rep["ok"],
+                "bands": bands,
+                "cpu": {"cores": threads, "t_s": round(cpu_med, 4),
+                        "GBps": round(nbytes / cpu_med / 1e9, 3),
+                        "t_1thread_s": round(t1, 3), "GBps_1thread": round(nbytes / t1 / 1e9, 3),
+                        "kind": "oracle"},
+                "gpu_over_cpu": round(cpu_med / (med * 1e-6), 1),
+            }
+            log(f"[report] config {c} {direction}: {line['t_median_us']} us, {line['GBps']} GB/s, "
+                f"parity {rep['ok']}")
+            out.append(line)
+        del xs, dys, ys, dxs, csrc, cdst
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -849,12 +1072,20 @@ def main():
     if args.fft:
         print(json.dumps(measure_fft(args, lib, torch, dev)), flush=True)
         return
-    if args.grouped:
+    if args.report:
+        cfgs = [args.config] if "--config" in sys.argv else [1, 2, 3, 4, 5]
+        for line in measure_report(args, lib, torch, dev, cfgs):
+            print(json.dumps(line), flush=True)
+        return
+    if args.grouped or args.config == 5:
         print(json.dumps(measure_grouped(args, lib, torch, dev)), flush=True)
         return
+    if args.act != "swish" and args.config != 3:
+        print("--act measures the bf16 [8,2048,4096] workload (--config 3)", file=sys.stderr)
+        sys.exit(2)
 
     t_gen = time.perf_counter()
-    w = inputs.make(3)
+    w = inputs.make(args.config)
     log(f"[bench] inputs generated in {time.perf_counter() - t_gen:.1f} s: {w.name}, n={w.numel}")
     rig = Rig(torch, w, dev)
     acts = FAMILY if args.act == "all" else [args.act]

@@ -2,10 +2,11 @@
 
 Usage (after the rocprofv3 runs listed in each summary's header):
 
-    python -m memory_efficient_activation_amd.rocprof_summary trace DIR
-    python -m memory_efficient_activation_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR
-    python -m memory_efficient_activation_amd.rocprof_summary timeline DIR [WINDOW]
-    python -m memory_efficient_activation_amd.rocprof_summary valu DIR
+    python -m memory_efficient_activation_amd.rocprof_summary trace DIR [--io f32]
+    python -m memory_efficient_activation_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR [--io f32]
+    python -m memory_efficient_activation_amd.rocprof_summary timeline DIR [WINDOW] [--io f32]
+    python -m memory_efficient_activation_amd.rocprof_summary valu DIR [--io f32]
+    python -m memory_efficient_activation_amd.rocprof_summary rare [WORKLOAD]
     python -m memory_efficient_activation_amd.rocprof_summary grouped-trace DIR [STEPS]
     python -m memory_efficient_activation_amd.rocprof_summary dense-trace DIR f32|bf16
     python -m memory_efficient_activation_amd.rocprof_summary dense-traffic FETCH_DIR WRITE_DIR f32|bf16
@@ -55,20 +56,41 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCES = [os.path.join(HERE, "csrc", f) for f in ("meswish.hip", "act_math.h")]
 
 N = 8 * 2048 * 4096          # elements of the benchmark tensor
-BF16 = 2                     # bytes per element
-COPY_BYTES = BF16 * N        # bytes the copy kernel reads (and writes) per launch
-ALGO = {"fwd": 2 * BF16 * N, "bwd": 3 * BF16 * N, "copy": 2 * BF16 * N}
+# I/O type of the summarised run (the element type of act_vec_kernel's
+# first template argument): "bf16" (the headline workload) or "f32" (the
+# binary32 workload of the same shape); set_io() switches.
+IO = "bf16"
+IO_TYPE = {"bf16": "meswish::bf16_t", "f32": "float"}
+ESIZE = {"bf16": 2, "f32": 4}
+COPY_BYTES = ESIZE[IO] * N   # bytes the copy kernel reads (and writes) per launch
+ALGO = {"fwd": 2 * COPY_BYTES, "bwd": 3 * COPY_BYTES, "copy": 2 * COPY_BYTES}
 
 
-ACT_NAMES = ["swish", "relu", "leaky_relu", "sigmoid", "tanh", "gelu", "gelu_tanh"]
+def set_io(io: str) -> None:
+    global IO, COPY_BYTES, ALGO
+    if io not in ESIZE:
+        raise SystemExit(f"unknown I/O type {io!r} (bf16 or f32)")
+    IO = io
+    COPY_BYTES = ESIZE[io] * N
+    ALGO = {"fwd": 2 * COPY_BYTES, "bwd": 3 * COPY_BYTES, "copy": 2 * COPY_BYTES}
+
+
+# Activation codes of act_vec_kernel's third template argument; 8 is Swish
+# with alpha exactly 1 (the library's shorter backward).
+ACT_NAMES = {0: "swish", 1: "relu", 2: "leaky_relu", 3: "sigmoid", 4: "tanh", 5: "gelu",
+             6: "gelu_tanh", 8: "swish"}
+
+
+def _vec_re() -> str:
+    return r"act_vec_kernel<" + re.escape(IO_TYPE[IO]) + r", (true|false), (\d+)>"
 
 
 def kind(name: str, act: str = "swish") -> str:
-    """'fwd' / 'bwd' for the bf16 vector kernel of activation `act`, 'copy'
-    for the copy kernel, 'other' otherwise."""
-    m = re.search(r"act_vec_kernel<meswish::bf16_t, (true|false), (\d+)>", name)
+    """'fwd' / 'bwd' for the vector kernel (of the current I/O type) of
+    activation `act`, 'copy' for the copy kernel, 'other' otherwise."""
+    m = re.search(_vec_re(), name)
     if m:
-        if ACT_NAMES[int(m.group(2))] != act:
+        if ACT_NAMES.get(int(m.group(2))) != act:
             return "other"
         return "bwd" if m.group(1) == "true" else "fwd"
     if "copy16_kernel" in name:
@@ -77,8 +99,8 @@ def kind(name: str, act: str = "swish") -> str:
 
 
 def act_of(name: str) -> str:
-    m = re.search(r"act_vec_kernel<meswish::bf16_t, (?:true|false), (\d+)>", name)
-    return ACT_NAMES[int(m.group(1))] if m else ""
+    m = re.search(_vec_re(), name)
+    return ACT_NAMES.get(int(m.group(2)), "") if m else ""
 
 
 def _one(pattern: str) -> str:
@@ -219,7 +241,7 @@ def grouped_trace(d: str, steps: int = 200) -> str:
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
 
     def lab(name):
-        m = re.search(r"act_(group|vec)_kernel<meswish::bf16_t, (true|false), 0>", name)
+        m = re.search(r"act_(group|vec)_kernel<meswish::bf16_t, (true|false), [08]>", name)
         if not m:
             return None
         return ("g" if m.group(1) == "group" else "s") + ("b" if m.group(2) == "true" else "f")
@@ -297,6 +319,37 @@ def valu(d: str) -> str:
         out.append(f"| {label} | {len(ds)} | {mean('dur'):.1f} | {mean('VALUBusy'):.1f} | "
                    f"{mean('SQ_INSTS_VALU') * 64 / N:.2f} | "
                    f"{mean('SQ_INSTS_VALU_TRANS_F32') * 64 / N:.2f} |")
+    return "\n".join(out)
+
+
+def rare_rate(index: int = 4) -> str:
+    """How often the binary32 Swish kernels enter their rare branch on
+    workload `index` (default 4: alpha 1.5, 1 % of x in +-[20, 90]): an
+    element is rare where |fl(x c_hi)| > 125 (c_hi = fl(-alpha log2 e)); a
+    wave of the binary32 kernels covers 64 lanes x 4 consecutive elements
+    and takes the branch if any of them is rare, then runs one masked
+    region per element slot j = 0..3 that some lane needs.  Computed from
+    the workload's own inputs, exactly."""
+    import numpy as np
+
+    from . import inputs
+    w = inputs.make(index)
+    x = inputs.decode(w.xs[0]).astype(np.float32)
+    c_hi = np.float32(-float(np.float32(w.alpha)) * 1.4426950408889634)
+    v = (x * c_hi).astype(np.float32)
+    rare = np.abs(v) > np.float32(125.0)
+    per = 256  # elements per wave: 64 lanes x one 16-byte vector of 4
+    n = x.size - x.size % per
+    waves = rare[:n].reshape(-1, 64, 4)
+    any_wave = waves.any(axis=(1, 2))
+    slots = waves.any(axis=1)          # [wave, j]: some lane's element j is rare
+    out = [f"workload {index}: {w.name}, {x.size} elements, alpha {w.alpha}",
+           f"rare elements: {int(rare.sum())} ({rare.mean() * 100:.3f} %)",
+           f"waves (256 elements) entering the rare branch: {int(any_wave.sum())} of "
+           f"{any_wave.size} ({any_wave.mean() * 100:.1f} %)",
+           f"masked regions run per wave (element slots needed, mean over all waves): "
+           f"{slots.sum(axis=1).mean():.3f}",
+           f"rare elements per entering wave (mean): {waves.sum(axis=(1, 2))[any_wave].mean():.2f}"]
     return "\n".join(out)
 
 
@@ -516,6 +569,10 @@ def fft_traffic(fetch_dir: str, write_dir: str) -> str:
 
 
 def main(argv):
+    if "--io" in argv:
+        i = argv.index("--io")
+        set_io(argv[i + 1])
+        argv = argv[:i] + argv[i + 2:]
     if len(argv) >= 2 and argv[0] == "trace":
         print(trace(argv[1]))
     elif len(argv) >= 3 and argv[0] == "traffic":
@@ -534,6 +591,8 @@ def main(argv):
         print(fft_trace(argv[1]))
     elif len(argv) >= 3 and argv[0] == "fft-traffic":
         print(fft_traffic(argv[1], argv[2]))
+    elif len(argv) >= 1 and argv[0] == "rare":
+        print(rare_rate(int(argv[1]) if len(argv) >= 2 else 4))
     else:
         raise SystemExit(__doc__)
 
