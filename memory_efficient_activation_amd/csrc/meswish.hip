@@ -49,12 +49,26 @@
 #include "meswish.h"
 #include "act_math.h"
 
-// Threads per block, per element type.
+// Threads per block, per element type and direction (one wave: measured
+// against 128, 256 and 512, and against other sizes per direction, on the
+// bf16 [8, 2048, 4096] Swish: the fastest step and the fastest kernels
+// alone).
 #ifndef MESWISH_BLOCK_BF16
-#define MESWISH_BLOCK_BF16 256
+#define MESWISH_BLOCK_BF16 64
+#endif
+#ifndef MESWISH_BLOCK_BF16_FWD
+#define MESWISH_BLOCK_BF16_FWD MESWISH_BLOCK_BF16
+#endif
+#ifndef MESWISH_BLOCK_BF16_BWD
+#define MESWISH_BLOCK_BF16_BWD MESWISH_BLOCK_BF16
 #endif
 #ifndef MESWISH_BLOCK_F32
 #define MESWISH_BLOCK_F32 64
+#endif
+// Threads per block of the grouped kernel (bf16): a grouped block finds its
+// tensor by dependent scalar loads, so it keeps larger tiles.
+#ifndef MESWISH_GROUP_BLOCK_BF16
+#define MESWISH_GROUP_BLOCK_BF16 256
 #endif
 // 16-byte vectors per thread and stream, per element type.
 #ifndef MESWISH_UNROLL_BF16
@@ -81,9 +95,11 @@
 #define MESWISH_MIN_WAVES 0
 #endif
 #if MESWISH_MIN_WAVES > 0
-#define MESWISH_BOUNDS __launch_bounds__(Io<IO>::kBlock, MESWISH_MIN_WAVES)
+#define MESWISH_BOUNDS __launch_bounds__((Shape<IO, kBwd>::kBlock), MESWISH_MIN_WAVES)
+#define MESWISH_GROUP_BOUNDS __launch_bounds__((GroupShape<IO, kBwd>::kBlock), MESWISH_MIN_WAVES)
 #else
-#define MESWISH_BOUNDS __launch_bounds__(Io<IO>::kBlock)
+#define MESWISH_BOUNDS __launch_bounds__((Shape<IO, kBwd>::kBlock))
+#define MESWISH_GROUP_BOUNDS __launch_bounds__((GroupShape<IO, kBwd>::kBlock))
 #endif
 #define MESWISH_COPY_BOUNDS __launch_bounds__(MESWISH_COPY_BLOCK)
 // Non-temporal (streaming) cache policy per stream, as bit masks:
@@ -144,8 +160,6 @@ template <typename IO> struct Io;
 
 template <> struct Io<float> {
     static constexpr int kPerVec = 4;
-    static constexpr int kUnroll = MESWISH_UNROLL_F32;
-    static constexpr int kBlock = MESWISH_BLOCK_F32;
     static constexpr bool kPrecise = true;
     __device__ static void unpack(const uint4& v, float (&f)[4])
     {
@@ -165,8 +179,6 @@ template <> struct Io<float> {
 
 template <> struct Io<bf16_t> {
     static constexpr int kPerVec = 8;
-    static constexpr int kUnroll = MESWISH_UNROLL_BF16;
-    static constexpr int kBlock = MESWISH_BLOCK_BF16;
     static constexpr bool kPrecise = false;
     __device__ static void unpack(const uint4& v, float (&f)[8])
     {
@@ -196,9 +208,27 @@ template <> struct NtPolicy<float, true> { static constexpr int kMask = MESWISH_
 template <> struct NtPolicy<bf16_t, false> { static constexpr int kMask = MESWISH_NT_FWD_BF16; };
 template <> struct NtPolicy<bf16_t, true> { static constexpr int kMask = MESWISH_NT_BWD_BF16; };
 
+// Launch shape per element type and direction: threads per block and
+// 16-byte vectors per thread and stream.
+template <typename IO, bool kBwd> struct Shape;
+template <bool kBwd> struct Shape<float, kBwd> {
+    static constexpr int kBlock = MESWISH_BLOCK_F32;
+    static constexpr int kUnroll = MESWISH_UNROLL_F32;
+};
+template <bool kBwd> struct Shape<bf16_t, kBwd> {
+    static constexpr int kBlock = kBwd ? MESWISH_BLOCK_BF16_BWD : MESWISH_BLOCK_BF16_FWD;
+    static constexpr int kUnroll = MESWISH_UNROLL_BF16;
+};
+
+// The grouped kernel's shape.
+template <typename IO, bool kBwd> struct GroupShape : Shape<IO, kBwd> {};
+template <bool kBwd> struct GroupShape<bf16_t, kBwd> : Shape<bf16_t, kBwd> {
+    static constexpr int kBlock = MESWISH_GROUP_BLOCK_BF16;
+};
+
 // 16-byte vectors per tile (one block's share of work).
-template <typename IO>
-constexpr int tile_vecs() { return Io<IO>::kBlock * Io<IO>::kUnroll; }
+template <typename IO, bool kBwd, typename SH = Shape<IO, kBwd>>
+constexpr int tile_vecs() { return SH::kBlock * SH::kUnroll; }
 
 typedef uint32_t u32x4_v __attribute__((ext_vector_type(4)));
 
@@ -294,18 +324,19 @@ __device__ __forceinline__ void one_element(const IO* x, const IO* dy, IO* out, 
     Io<IO>::store1(out, i, r);
 }
 
-// One tile: the nv <= tile_vecs<IO>() 16-byte vectors that start at xb, db,
+// One tile: the nv <= tile_vecs<IO, kBwd>() 16-byte vectors that start at xb, db,
 // ob.  The base pointers and nv are uniform over the block and lane offsets
 // are 32-bit, so every load and store addresses as a scalar base plus a
 // vector offset, with no 64-bit address arithmetic per lane.
-template <typename IO, bool kBwd, int ACT, int kNt = NtPolicy<IO, kBwd>::kMask>
+template <typename IO, bool kBwd, int ACT, typename SH = Shape<IO, kBwd>,
+          int kNt = NtPolicy<IO, kBwd>::kMask>
 __device__ __forceinline__ void body_tile(const uint4* xb, const uint4* db, uint4* ob,
                                           uint32_t nv, const Coef& k)
 {
-    constexpr int kUnroll = Io<IO>::kUnroll;
-    constexpr int kBlock = Io<IO>::kBlock;
+    constexpr int kUnroll = SH::kUnroll;
+    constexpr int kBlock = SH::kBlock;
     const uint32_t i = threadIdx.x;
-    if (nv == (uint32_t)tile_vecs<IO>()) {
+    if (nv == (uint32_t)tile_vecs<IO, kBwd, SH>()) {
         uint4 a[kUnroll], b[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
@@ -355,7 +386,7 @@ __global__ MESWISH_BOUNDS void act_vec_kernel(const IO* x, const IO* dy, IO* out
                                               uint32_t last_vecs, uint32_t tail, Coef k)
 {
     constexpr int E = Io<IO>::kPerVec;
-    constexpr uint32_t kTileVecs = tile_vecs<IO>();
+    constexpr uint32_t kTileVecs = tile_vecs<IO, kBwd>();
     const uint4* xv = reinterpret_cast<const uint4*>(x + head);
     const uint4* dv = kBwd ? reinterpret_cast<const uint4*>(dy + head) : nullptr;
     uint4* ov = reinterpret_cast<uint4*>(out + head);
@@ -377,7 +408,7 @@ template <typename IO, bool kBwd, int ACT>
 __global__ MESWISH_BOUNDS void act_elem_kernel(const IO* x, const IO* dy, IO* out,
                                                             int64_t n, Coef k)
 {
-    constexpr int kBlock = Io<IO>::kBlock;
+    constexpr int kBlock = Shape<IO, kBwd>::kBlock;
     const int64_t stride = (int64_t)gridDim.x * kBlock;
     for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride)
         one_element<IO, kBwd, ACT>(x, dy, out, i, k);
@@ -389,7 +420,7 @@ __global__ MESWISH_BOUNDS void act_elem_kernel(const IO* x, const IO* dy, IO* ou
 // (b + gridDim) ..) and finds each tile's tensor by a forward scan (tiles of
 // one block are increasing, so the scan is amortised O(1)).  The first tile of a tensor also does its scalar head and
 // tail.  A tensor whose pointers are not congruent modulo 16 bytes (flag 0)
-// is processed element by element, tile_vecs<IO>() elements per tile.
+// is processed element by element, tile_vecs<IO, kBwd>() elements per tile.
 struct GroupArgs {
     const void* x[MESWISH_MAX_GROUP];
     const void* dy[MESWISH_MAX_GROUP];
@@ -401,11 +432,12 @@ struct GroupArgs {
 };
 
 template <typename IO, bool kBwd, int ACT>
-__global__ MESWISH_BOUNDS void act_group_kernel(GroupArgs g, Coef k)
+__global__ MESWISH_GROUP_BOUNDS void act_group_kernel(GroupArgs g, Coef k)
 {
     constexpr int E = Io<IO>::kPerVec;
-    constexpr int kUnroll = Io<IO>::kUnroll;
-    constexpr int64_t kTileVecs = tile_vecs<IO>();
+    using SH = GroupShape<IO, kBwd>;
+    constexpr int kUnroll = SH::kUnroll;
+    constexpr int64_t kTileVecs = tile_vecs<IO, kBwd, SH>();
     constexpr int G = kBwd ? MESWISH_GROUP_TILES_BWD : MESWISH_GROUP_TILES_FWD;
     const int64_t total = g.tile_begin[g.count];
     int j = 0;
@@ -423,7 +455,7 @@ __global__ MESWISH_BOUNDS void act_group_kernel(GroupArgs g, Coef k)
             int64_t e0 = local * kTileVecs;
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                int64_t i = e0 + u * Io<IO>::kBlock + threadIdx.x;
+                int64_t i = e0 + u * SH::kBlock + threadIdx.x;
                 if (i < n)
                     one_element<IO, kBwd, ACT>(x, dy, out, i, k);
             }
@@ -434,7 +466,7 @@ __global__ MESWISH_BOUNDS void act_group_kernel(GroupArgs g, Coef k)
         const int64_t v0 = local * kTileVecs;
         const int64_t left = nvec - v0;
         const uint32_t nv = left >= kTileVecs ? (uint32_t)kTileVecs : (uint32_t)(left > 0 ? left : 0);
-        body_tile<IO, kBwd, ACT>(reinterpret_cast<const uint4*>(x + head) + v0,
+        body_tile<IO, kBwd, ACT, SH>(reinterpret_cast<const uint4*>(x + head) + v0,
                                  kBwd ? reinterpret_cast<const uint4*>(dy + head) + v0 : nullptr,
                                  reinterpret_cast<uint4*>(out + head) + v0, nv, k);
         const int64_t t = threadIdx.x;  // head >= 0 here
@@ -584,11 +616,11 @@ static Coef make_coef(int act, float p)
 }
 
 // How one tensor is split between the kernels' paths (see meswish_plan_t).
-template <typename IO, bool kBwd>
+template <typename IO, bool kBwd, typename SH = Shape<IO, kBwd>>
 static meswish_plan_t make_plan(const void* x, const void* dy, const void* out, size_t n)
 {
     constexpr int E = Io<IO>::kPerVec;
-    constexpr int64_t kTileVecs = tile_vecs<IO>();
+    constexpr int64_t kTileVecs = tile_vecs<IO, kBwd, SH>();
     meswish_plan_t p;
     memset(&p, 0, sizeof p);
     uintptr_t mx = (uintptr_t)x & 15u, mo = (uintptr_t)out & 15u;
@@ -608,7 +640,7 @@ static meswish_plan_t make_plan(const void* x, const void* dy, const void* out, 
         p.tail = nn;
         p.tiles = (nn + kTileVecs - 1) / kTileVecs;
     }
-    p.block = Io<IO>::kBlock;
+    p.block = SH::kBlock;
     if (p.path == MESWISH_PATH_VECTOR) {
         p.launches = p.tiles > kMaxLaunchTiles ? (p.tiles + kMaxLaunchTiles - 1) / kMaxLaunchTiles : 1;
         p.grid = grid_for_tiles(p.tiles < kMaxLaunchTiles ? p.tiles : kMaxLaunchTiles, (int)p.block);
@@ -626,7 +658,7 @@ static int run_single(const void* x, const void* dy, void* out, size_t n, Coef k
                       hipStream_t stream)
 {
     constexpr int E = Io<IO>::kPerVec;
-    constexpr int64_t kTileVecs = tile_vecs<IO>();
+    constexpr int64_t kTileVecs = tile_vecs<IO, kBwd>();
     const meswish_plan_t p = make_plan<IO, kBwd>(x, dy, out, n);
     const IO* xp = static_cast<const IO*>(x);
     const IO* dp = static_cast<const IO*>(dy);
@@ -710,7 +742,8 @@ static int run_group(GroupArgs& g, Coef k, hipStream_t stream)
         int64_t t = 0;
         g.head[j] = 0;
         if (g.n[j] > 0) {
-            const meswish_plan_t p = make_plan<IO, kBwd>(g.x[j], g.dy[j], g.out[j], (size_t)g.n[j]);
+            const meswish_plan_t p =
+                make_plan<IO, kBwd, GroupShape<IO, kBwd>>(g.x[j], g.dy[j], g.out[j], (size_t)g.n[j]);
             if (p.path == MESWISH_PATH_VECTOR) {
                 g.head[j] = (int32_t)p.head;
                 // A tensor shorter than one vector still needs its scalar tile.
@@ -726,12 +759,12 @@ static int run_group(GroupArgs& g, Coef k, hipStream_t stream)
     if (tiles == 0)
         return MESWISH_OK;
     constexpr int G = kBwd ? MESWISH_GROUP_TILES_BWD : MESWISH_GROUP_TILES_FWD;
-    int64_t grid = grid_for_tiles((tiles + G - 1) / G, Io<IO>::kBlock);
+    int64_t grid = grid_for_tiles((tiles + G - 1) / G, GroupShape<IO, kBwd>::kBlock);
     void* args[] = {&g, &k};
     const void* fn = kBwd && k.p == 1.0f
                          ? reinterpret_cast<const void*>(&act_group_kernel<IO, kBwd, kSwishUnit>)
                          : reinterpret_cast<const void*>(&act_group_kernel<IO, kBwd, kSwish>);
-    return launch(fn, grid, args, stream, Io<IO>::kBlock);
+    return launch(fn, grid, args, stream, GroupShape<IO, kBwd>::kBlock);
 }
 
 // Common argument checks.  Returns MESWISH_OK or an error code.
