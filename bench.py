@@ -139,6 +139,9 @@ def parse_args():
     p.add_argument("--dense", action="store_true",
                    help="measure the shared-buffer DenseNet layer stage instead")
     p.add_argument("--dense-dtype", default="f32", choices=["f32", "bf16"])
+    p.add_argument("--dense-sets", type=int, default=DENSE_SETS,
+                   help="rotating buffer sets of the DenseNet layer bench (default 8; fewer "
+                        "sets hold less memory but let the caches serve part of the traffic)")
     p.add_argument("--grouped", action="store_true",
                    help="grouped Swish over the 7 EfficientNet-shaped bf16 tensors (config 5)")
     p.add_argument("--fft", action="store_true",
@@ -338,7 +341,7 @@ def measure(args, act, rig, w, lib, torch):
     return result
 
 
-DENSE_SETS = 8
+DENSE_SETS = 8  # default of --dense-sets
 DENSE_SOURCES = [os.path.join(ROOT, "memory_efficient_activation_amd", "csrc", "dense_bn.hip")]
 
 
@@ -383,7 +386,8 @@ def measure_dense(args, lib, torch, dev):
     sets = []
     xs0 = [to_dev(s_) for s_ in w.sources]
     dz0 = to_dev(w.dz)
-    for _ in range(DENSE_SETS):
+    nsets = max(1, args.dense_sets)
+    for _ in range(nsets):
         xs = [x.clone() for x in xs0]
         st = [dense.bn_stats(x) for x in xs]
         dxs = [torch.empty_like(x) for x in xs]
@@ -408,19 +412,19 @@ def measure_dense(args, lib, torch, dev):
     nsrc = len(w.sources)
 
     def k_stats(j):
-        s_ = sets[j % DENSE_SETS]
+        s_ = sets[j % nsets]
         _lib.check(lib.dense_bn_stats(s_["xs"][-1].data_ptr(), n, new_c, hw, code,
                                       s_["stat_new"].data_ptr(), s_["ws_new"].data_ptr(),
                                       s_["ws_new"].numel(), sh), "dense_bn_stats")
 
     def k_fwd(j):
-        s_ = sets[j % DENSE_SETS]
+        s_ = sets[j % nsets]
         _lib.check(lib.dense_bn_relu_fwd(s_["descs"], nsrc, n, hw, C, gamma.data_ptr(),
                                          beta.data_ptr(), eps, s_["z"].data_ptr(), code, sh),
                    "dense_bn_relu_fwd")
 
     def k_bwd(j):
-        s_ = sets[j % DENSE_SETS]
+        s_ = sets[j % nsets]
         _lib.check(lib.dense_bn_relu_bwd(s_["descs"], nsrc, n, hw, C, gamma.data_ptr(),
                                          beta.data_ptr(), eps, s_["dz"].data_ptr(),
                                          s_["dg"].data_ptr(), s_["db"].data_ptr(),
@@ -463,7 +467,7 @@ def measure_dense(args, lib, torch, dev):
     # Copy ceiling on one concatenated map's bytes (read + write), same
     # rotation depth; it also calibrates the HBM counters.
     cbufs = [(torch.empty(cmb, dtype=torch.uint8, device=dev),
-              torch.empty(cmb, dtype=torch.uint8, device=dev)) for _ in range(DENSE_SETS // 2)]
+              torch.empty(cmb, dtype=torch.uint8, device=dev)) for _ in range(max(1, nsets // 2))]
 
     def k_copy(j):
         a_, b_ = cbufs[j % len(cbufs)]
@@ -513,7 +517,7 @@ def measure_dense(args, lib, torch, dev):
         "config": {"workload": f"DenseNet-BC-100 (growth 12) block 1 layer 16 at batch 64: "
                                f"{nsrc} sources, {C} channels of 64x32x32, {w.dtype}",
                    "channels": w.channels, "n": n, "hw": hw, "eps": eps,
-                   "bytes_per_step": step_b, "buffer_sets": DENSE_SETS,
+                   "bytes_per_step": step_b, "buffer_sets": nsets,
                    "step": "stats(newest source) + fwd + fwd (recompute) + bwd (reduce+apply)"},
         "frac_peak": round(value / PEAK_HBM_GBPS, 4),
         "kernels": per,

@@ -5,7 +5,7 @@ Usage (after the rocprofv3 runs listed in each summary's header):
     python -m memory_efficient_activation_amd.rocprof_summary trace DIR [--io f32]
     python -m memory_efficient_activation_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR [--io f32]
     python -m memory_efficient_activation_amd.rocprof_summary timeline DIR [WINDOW] [--io f32]
-    python -m memory_efficient_activation_amd.rocprof_summary valu DIR [--io f32]
+    python -m memory_efficient_activation_amd.rocprof_summary valu DIR [--io f32] [--elements N]
     python -m memory_efficient_activation_amd.rocprof_summary rare [WORKLOAD]
     python -m memory_efficient_activation_amd.rocprof_summary grouped-trace DIR [STEPS]
     python -m memory_efficient_activation_amd.rocprof_summary dense-trace DIR f32|bf16
@@ -66,11 +66,15 @@ COPY_BYTES = ESIZE[IO] * N   # bytes the copy kernel reads (and writes) per laun
 ALGO = {"fwd": 2 * COPY_BYTES, "bwd": 3 * COPY_BYTES, "copy": 2 * COPY_BYTES}
 
 
-def set_io(io: str) -> None:
-    global IO, COPY_BYTES, ALGO
+def set_io(io: str, elements: int | None = None) -> None:
+    """Summarise runs of I/O type `io` over tensors of `elements` elements
+    (default the [8, 2048, 4096] tensor)."""
+    global IO, N, COPY_BYTES, ALGO
     if io not in ESIZE:
         raise SystemExit(f"unknown I/O type {io!r} (bf16 or f32)")
     IO = io
+    if elements is not None:
+        N = int(elements)
     COPY_BYTES = ESIZE[io] * N
     ALGO = {"fwd": 2 * COPY_BYTES, "bwd": 3 * COPY_BYTES, "copy": 2 * COPY_BYTES}
 
@@ -569,10 +573,16 @@ def fft_traffic(fetch_dir: str, write_dir: str) -> str:
 
 
 def main(argv):
-    if "--io" in argv:
-        i = argv.index("--io")
-        set_io(argv[i + 1])
-        argv = argv[:i] + argv[i + 2:]
+    io, elements = IO, None
+    for flag in ("--io", "--elements"):
+        if flag in argv:
+            i = argv.index(flag)
+            if flag == "--io":
+                io = argv[i + 1]
+            else:
+                elements = int(argv[i + 1])
+            argv = argv[:i] + argv[i + 2:]
+    set_io(io, elements)
     if len(argv) >= 2 and argv[0] == "trace":
         print(trace(argv[1]))
     elif len(argv) >= 3 and argv[0] == "traffic":
