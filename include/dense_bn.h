@@ -124,6 +124,29 @@ int dense_bn_relu_bwd(const dense_bn_source *src, int count, size_t n, size_t hw
                       const void *dz, float *dgamma, float *dbeta,
                       void *workspace, size_t workspace_bytes, int dtype, void *stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * backward of dense_bn_relu_bwd without a workspace argument.  Its
+ * per-block partial sums go to a static device array of
+ * DENSE_BN_STATIC_WORKSPACE_BYTES bytes that the library holds on each GPU
+ * it runs on, until the process ends; the call itself allocates, frees and
+ * synchronises nothing.  Same arguments, checks and results (bit for bit)
+ * as dense_bn_relu_bwd otherwise.  A call that needs more than the array
+ * holds -- dense_bn_workspace_bytes(n, sum of the sources' channels, hw) >
+ * DENSE_BN_STATIC_WORKSPACE_BYTES, e.g. more than 262,144 channel-chunks of
+ * 4096 elements -- returns MESWISH_ESCRATCH and launches nothing.  Every
+ * call on one GPU shares that GPU's array: calls that may run at the same
+ * time on one GPU (on different streams) race and must be ordered by the
+ * caller.  MESWISH_EHIP if the array's address cannot be looked up.
+ */
+#define DENSE_BN_STATIC_WORKSPACE_BYTES ((size_t)4 << 20)
+
+int dense_bn_relu_bwd_noalloc(const dense_bn_source *src, int count, size_t n, size_t hw,
+                              int z_channels, const float *gamma, const float *beta, float eps,
+                              const void *dz, float *dgamma, float *dbeta, int dtype,
+                              void *stream);
+
 #ifdef __cplusplus
 }
 #endif

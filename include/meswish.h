@@ -71,7 +71,9 @@ typedef enum {
     MESWISH_EALIAS = 2,   /* an output overlaps an input or another output
                              other than by exact, same-tensor coincidence */
     MESWISH_EHIP = 3,     /* the HIP runtime reported an error at launch */
-    MESWISH_ETOOMANY = 4  /* grouped call with count > MESWISH_MAX_GROUP */
+    MESWISH_ETOOMANY = 4, /* grouped call with count > MESWISH_MAX_GROUP */
+    MESWISH_ESCRATCH = 5  /* a call without a workspace needs more than the
+                             library's static device array holds */
 } meswish_status;
 
 /* Largest number of tensors one grouped call accepts (one launch). */

@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(_HERE, "libmeswish.so")
 
 # Status codes and dtypes (mirror include/meswish.h).
-OK, EINVAL, EALIAS, EHIP, ETOOMANY = 0, 1, 2, 3, 4
+OK, EINVAL, EALIAS, EHIP, ETOOMANY, ESCRATCH = 0, 1, 2, 3, 4, 5
 F32, BF16 = 0, 1
 MAX_GROUP = 64
 
@@ -24,9 +24,11 @@ EXPORTED = ("swish_fwd", "swish_bwd", "swish_fwd_grouped", "swish_bwd_grouped",
             "meswish_act_fwd", "meswish_act_bwd",
             "meswish_strerror", "meswish_version", "meswish_copy", "meswish_plan",
             "dense_bn_workspace_bytes", "dense_bn_stats", "dense_bn_relu_fwd", "dense_bn_relu_bwd",
+            "dense_bn_relu_bwd_noalloc",
             "fftconv_buffer_bytes", "fftconv_fprop", "fftconv_bprop", "fftconv_accgrad",
             "fftconv_r2c", "fftconv_c2r", "fftconv_cmul")
 DENSE_MAX_SOURCES = 64
+DENSE_STATIC_WORKSPACE_BYTES = 4 << 20
 
 # Activation codes (mirror meswish_act) and their default parameters.
 ACTS = {"swish": 0, "relu": 1, "leaky_relu": 2, "sigmoid": 3, "tanh": 4, "gelu": 5,
@@ -98,6 +100,9 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.dense_bn_relu_bwd.argtypes = [ctypes.POINTER(DenseSource), i, sz, sz, i, vp, vp, f, vp, vp,
                                       vp, vp, sz, i, vp]
     lib.dense_bn_relu_bwd.restype = i
+    lib.dense_bn_relu_bwd_noalloc.argtypes = [ctypes.POINTER(DenseSource), i, sz, sz, i, vp, vp, f,
+                                              vp, vp, vp, i, vp]
+    lib.dense_bn_relu_bwd_noalloc.restype = i
     lib.fftconv_buffer_bytes.argtypes = [i, i, i, i]
     lib.fftconv_buffer_bytes.restype = sz
     for name in ("fftconv_fprop", "fftconv_bprop", "fftconv_accgrad"):

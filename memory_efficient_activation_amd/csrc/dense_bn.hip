@@ -38,6 +38,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "dense_bn.h"
 
 namespace dense_bn {
@@ -858,10 +860,15 @@ extern "C" int dense_bn_relu_fwd(const dense_bn_source* src, int count, size_t n
                : run_fwd<bf16_t, 1>(t, total, n, hw, z_channels, gamma, beta, eps, z, s);
 }
 
-extern "C" int dense_bn_relu_bwd(const dense_bn_source* src, int count, size_t n, size_t hw,
-                                 int z_channels, const float* gamma, const float* beta, float eps,
-                                 const void* dz, float* dgamma, float* dbeta, void* workspace,
-                                 size_t workspace_bytes, int dtype, void* stream)
+namespace dense_bn {
+
+// The backward of both entry points; `workspace` is the caller's memory or
+// the library's static scratch.  too_big: status when the workspace is
+// smaller than the call needs.
+static int relu_bwd(const dense_bn_source* src, int count, size_t n, size_t hw, int z_channels,
+                    const float* gamma, const float* beta, float eps, const void* dz,
+                    float* dgamma, float* dbeta, void* workspace, size_t workspace_bytes,
+                    int dtype, hipStream_t s, int too_big)
 {
     if (!dtype_ok(dtype) || !params_ok(z_channels, gamma, beta, eps) || !dz || !dgamma ||
         !dbeta || !workspace || channel_elems(n, hw) == 0)
@@ -879,8 +886,10 @@ extern "C" int dense_bn_relu_bwd(const dense_bn_source* src, int count, size_t n
     if (count == 0)
         return MESWISH_OK;
     const size_t need = dense_bn_workspace_bytes(n, (size_t)total, hw);
-    if (need == 0 || workspace_bytes < need)
+    if (need == 0)
         return MESWISH_EINVAL;
+    if (workspace_bytes < need)
+        return too_big;
     reg.add(dz, n * (size_t)z_channels * hw * esize(dtype), false);
     reg.add(gamma, (size_t)z_channels * 4, false);
     reg.add(beta, (size_t)z_channels * 4, false);
@@ -891,7 +900,6 @@ extern "C" int dense_bn_relu_bwd(const dense_bn_source* src, int count, size_t n
         return MESWISH_EALIAS;
     vec = vec && aligned(dz, 16);
     double* ws = static_cast<double*>(workspace);
-    hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == MESWISH_F32)
         return vec ? run_bwd<float, 4>(t, total, n, hw, z_channels, gamma, beta, eps, dz, dgamma,
                                        dbeta, ws, s)
@@ -901,4 +909,65 @@ extern "C" int dense_bn_relu_bwd(const dense_bn_source* src, int count, size_t n
                                     dbeta, ws, s)
                : run_bwd<bf16_t, 1>(t, total, n, hw, z_channels, gamma, beta, eps, dz, dgamma,
                                     dbeta, ws, s);
+}
+
+}  // namespace dense_bn
+
+extern "C" int dense_bn_relu_bwd(const dense_bn_source* src, int count, size_t n, size_t hw,
+                                 int z_channels, const float* gamma, const float* beta, float eps,
+                                 const void* dz, float* dgamma, float* dbeta, void* workspace,
+                                 size_t workspace_bytes, int dtype, void* stream)
+{
+    return relu_bwd(src, count, n, hw, z_channels, gamma, beta, eps, dz, dgamma, dbeta, workspace,
+                    workspace_bytes, dtype, static_cast<hipStream_t>(stream), MESWISH_EINVAL);
+}
+
+// ---------------------------------------------------------------------------
+// The backward without a caller workspace: its per-block partial sums go to
+// `scratch`, a fixed array in device memory that every GPU the library runs
+// on holds until the process ends.  Host code never passes the array's name
+// to a kernel (on the host it is a stand-in symbol, not a device address):
+// its address on each device is looked up once, with that device current,
+// and kept per device.  Every partial slot a call reads is written by the
+// same call first, so the array needs no clearing; calls that overlap on
+// one GPU share the array and race.
+// ---------------------------------------------------------------------------
+
+static __device__ __align__(256) double scratch[DENSE_BN_STATIC_WORKSPACE_BYTES / sizeof(double)];
+
+namespace dense_bn {
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mutex;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device, or nullptr.
+static void* scratch_on_current_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess)
+            return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace dense_bn
+
+extern "C" int dense_bn_relu_bwd_noalloc(const dense_bn_source* src, int count, size_t n,
+                                         size_t hw, int z_channels, const float* gamma,
+                                         const float* beta, float eps, const void* dz,
+                                         float* dgamma, float* dbeta, int dtype, void* stream)
+{
+    void* ws = scratch_on_current_device();
+    if (!ws)
+        return MESWISH_EHIP;
+    return relu_bwd(src, count, n, hw, z_channels, gamma, beta, eps, dz, dgamma, dbeta, ws,
+                    DENSE_BN_STATIC_WORKSPACE_BYTES, dtype, static_cast<hipStream_t>(stream),
+                    MESWISH_ESCRATCH);
 }

@@ -1022,6 +1022,9 @@ extern "C" const char* meswish_strerror(int status)
         return "the HIP runtime reported an error at kernel launch";
     case MESWISH_ETOOMANY:
         return "grouped call with more tensors than MESWISH_MAX_GROUP";
+    case MESWISH_ESCRATCH:
+        return "the call needs more scratch than the library's static device array holds "
+               "(use the entry point that takes a workspace)";
     default:
         return "unknown status";
     }

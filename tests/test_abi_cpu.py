@@ -49,6 +49,7 @@ def test_header_declares_the_boundary():
         "meswish_copy", "meswish_plan", "meswish_strerror", "meswish_version", "swish_bwd",
         "swish_bwd_grouped", "swish_fwd", "swish_fwd_grouped",
         "dense_bn_workspace_bytes", "dense_bn_stats", "dense_bn_relu_fwd", "dense_bn_relu_bwd",
+        "dense_bn_relu_bwd_noalloc",
         "fftconv_buffer_bytes", "fftconv_fprop", "fftconv_bprop", "fftconv_accgrad",
         "fftconv_r2c", "fftconv_c2r", "fftconv_cmul"])
 
@@ -67,7 +68,7 @@ def test_binding_constants_match_header(lib):
     st = declared_enum("meswish_status")
     assert st == {"MESWISH_OK": _lib.OK, "MESWISH_EINVAL": _lib.EINVAL,
                   "MESWISH_EALIAS": _lib.EALIAS, "MESWISH_EHIP": _lib.EHIP,
-                  "MESWISH_ETOOMANY": _lib.ETOOMANY}
+                  "MESWISH_ETOOMANY": _lib.ETOOMANY, "MESWISH_ESCRATCH": _lib.ESCRATCH}
     assert declared_enum("meswish_dtype") == {"MESWISH_F32": _lib.F32, "MESWISH_BF16": _lib.BF16}
     acts = declared_enum("meswish_act")
     assert {k[len("MESWISH_ACT_"):].lower(): v for k, v in acts.items()} == {
@@ -85,6 +86,9 @@ def test_binding_constants_match_header(lib):
     assert ctypes.sizeof(_lib.FwdDesc) == 24 and ctypes.sizeof(_lib.BwdDesc) == 32
     m = re.search(r"#define DENSE_BN_MAX_SOURCES (\d+)", _header_text())
     assert int(m.group(1)) == _lib.DENSE_MAX_SOURCES
+    m = re.search(r"#define DENSE_BN_STATIC_WORKSPACE_BYTES \(\(size_t\)(\d+) << (\d+)\)",
+                  _header_text())
+    assert int(m.group(1)) << int(m.group(2)) == _lib.DENSE_STATIC_WORKSPACE_BYTES
     fields = re.search(r"typedef struct \{([^{}]*)\}\s*dense_bn_source;", _header_text()).group(1)
     assert re.findall(r"(\w+);", fields) == [f[0] for f in _lib.DenseSource._fields_]
     assert ctypes.sizeof(_lib.DenseSource) == 32
