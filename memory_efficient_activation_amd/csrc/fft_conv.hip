@@ -28,8 +28,7 @@
 //     pair of complex k.  Tiles of 64 x 64 (or 64 x 32 where that pads
 //     less) complex outputs, K in steps of 8 through LDS with the next step
 //     prefetched into registers; all tiles of one bin run on one XCD
-//     (shared operands stay in that XCD's L2).  An interleaved matrix-core
-//     version and a vector-ALU version are kept for comparison.
+//     (shared operands stay in that XCD's L2).
 //   * Inverse.  Column transforms first, keeping only the rows that survive
 //     the crop, then row transforms of the Hermitian half rows; only the
 //     kept m x m corner is written, scaled by 1/n^2, through LDS as whole
