@@ -68,52 +68,43 @@ class MeswishError(RuntimeError):
         self.status = status
 
 
-def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
+def _signatures() -> dict:
+    """Argument and result types of every exported function."""
     vp, sz, f, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float, ctypes.c_int
-    lib.swish_fwd.argtypes = [vp, vp, sz, f, i, vp]
-    lib.swish_fwd.restype = i
-    lib.swish_bwd.argtypes = [vp, vp, vp, sz, f, i, vp]
-    lib.swish_bwd.restype = i
-    lib.swish_fwd_grouped.argtypes = [ctypes.POINTER(FwdDesc), i, f, i, vp]
-    lib.swish_fwd_grouped.restype = i
-    lib.swish_bwd_grouped.argtypes = [ctypes.POINTER(BwdDesc), i, f, i, vp]
-    lib.swish_bwd_grouped.restype = i
-    lib.meswish_strerror.argtypes = [i]
-    lib.meswish_strerror.restype = ctypes.c_char_p
-    lib.meswish_version.argtypes = []
-    lib.meswish_version.restype = i
-    lib.meswish_copy.argtypes = [vp, vp, sz, vp]
-    lib.meswish_copy.restype = i
-    lib.meswish_act_fwd.argtypes = [i, vp, vp, sz, f, i, vp]
-    lib.meswish_act_fwd.restype = i
-    lib.meswish_act_bwd.argtypes = [i, vp, vp, vp, sz, f, i, vp]
-    lib.meswish_act_bwd.restype = i
-    lib.meswish_plan.argtypes = [vp, vp, vp, sz, f, i, i, ctypes.POINTER(Plan)]
-    lib.meswish_plan.restype = i
-    lib.dense_bn_workspace_bytes.argtypes = [sz, sz, sz]
-    lib.dense_bn_workspace_bytes.restype = sz
-    lib.dense_bn_stats.argtypes = [vp, sz, i, sz, i, vp, vp, sz, vp]
-    lib.dense_bn_stats.restype = i
-    lib.dense_bn_relu_fwd.argtypes = [ctypes.POINTER(DenseSource), i, sz, sz, i, vp, vp, f, vp, i,
-                                      vp]
-    lib.dense_bn_relu_fwd.restype = i
-    lib.dense_bn_relu_bwd.argtypes = [ctypes.POINTER(DenseSource), i, sz, sz, i, vp, vp, f, vp, vp,
-                                      vp, vp, sz, i, vp]
-    lib.dense_bn_relu_bwd.restype = i
-    lib.dense_bn_relu_bwd_noalloc.argtypes = [ctypes.POINTER(DenseSource), i, sz, sz, i, vp, vp, f,
-                                              vp, vp, vp, i, vp]
-    lib.dense_bn_relu_bwd_noalloc.restype = i
-    lib.fftconv_buffer_bytes.argtypes = [i, i, i, i]
-    lib.fftconv_buffer_bytes.restype = sz
+    src = ctypes.POINTER(DenseSource)
+    sig = {
+        "swish_fwd": ([vp, vp, sz, f, i, vp], i),
+        "swish_bwd": ([vp, vp, vp, sz, f, i, vp], i),
+        "swish_fwd_grouped": ([ctypes.POINTER(FwdDesc), i, f, i, vp], i),
+        "swish_bwd_grouped": ([ctypes.POINTER(BwdDesc), i, f, i, vp], i),
+        "meswish_strerror": ([i], ctypes.c_char_p),
+        "meswish_version": ([], i),
+        "meswish_copy": ([vp, vp, sz, vp], i),
+        "meswish_act_fwd": ([i, vp, vp, sz, f, i, vp], i),
+        "meswish_act_bwd": ([i, vp, vp, vp, sz, f, i, vp], i),
+        "meswish_plan": ([vp, vp, vp, sz, f, i, i, ctypes.POINTER(Plan)], i),
+        "dense_bn_workspace_bytes": ([sz, sz, sz], sz),
+        "dense_bn_stats": ([vp, sz, i, sz, i, vp, vp, sz, vp], i),
+        "dense_bn_relu_fwd": ([src, i, sz, sz, i, vp, vp, f, vp, i, vp], i),
+        "dense_bn_relu_bwd": ([src, i, sz, sz, i, vp, vp, f, vp, vp, vp, vp, sz, i, vp], i),
+        "dense_bn_relu_bwd_noalloc": ([src, i, sz, sz, i, vp, vp, f, vp, vp, vp, i, vp], i),
+        "fftconv_buffer_bytes": ([i, i, i, i], sz),
+        "fftconv_r2c": ([vp, i, i, i, vp, vp], i),
+        "fftconv_c2r": ([vp, i, i, i, f, vp, vp], i),
+        "fftconv_cmul": ([i, vp, vp, vp, i, i, i, i, vp], i),
+    }
     for name in ("fftconv_fprop", "fftconv_bprop", "fftconv_accgrad"):
-        getattr(lib, name).argtypes = [vp, vp, vp, i, i, i, i, i, vp, sz, vp]
-        getattr(lib, name).restype = i
-    lib.fftconv_r2c.argtypes = [vp, i, i, i, vp, vp]
-    lib.fftconv_r2c.restype = i
-    lib.fftconv_c2r.argtypes = [vp, i, i, i, f, vp, vp]
-    lib.fftconv_c2r.restype = i
-    lib.fftconv_cmul.argtypes = [i, vp, vp, vp, i, i, i, i, vp]
-    lib.fftconv_cmul.restype = i
+        sig[name] = ([vp, vp, vp, i, i, i, i, i, vp, sz, vp], i)
+    return sig
+
+
+def _declare(lib: ctypes.CDLL, names=None) -> ctypes.CDLL:
+    """Set argtypes/restype of ``names`` (every exported function by default);
+    a missing symbol raises AttributeError."""
+    sig = _signatures()
+    for name in (sig if names is None else names):
+        fn = getattr(lib, name)
+        fn.argtypes, fn.restype = sig[name]
     return lib
 
 
@@ -121,12 +112,14 @@ _LIB = None
 _LOCK = threading.Lock()
 
 
-def library(path: str | None = None) -> ctypes.CDLL:
-    """Load libmeswish.so once (after torch, so that both share one HIP runtime)."""
+def library(path: str | None = None, names=None) -> ctypes.CDLL:
+    """Load libmeswish.so once (after torch, so that both share one HIP runtime).
+    With ``path``, load that build instead (not cached), declaring ``names``
+    (every exported function by default)."""
     global _LIB
     if path is not None:
         import torch  # noqa: F401  (the HIP runtime torch loads is the one the library binds to)
-        return _declare(ctypes.CDLL(path))
+        return _declare(ctypes.CDLL(path), names)
     with _LOCK:
         if _LIB is None:
             if not os.path.exists(LIBRARY):

@@ -28,13 +28,33 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
-def build(output: str = LIBRARY, extra_flags: list[str] | None = None) -> str:
+# A test build of the activation kernels alone with three tiles per launch,
+# so that the split of long tensors into several launches runs on tensors
+# small enough for a GPU test (the library's own limit is 2^30 tiles).
+SPLIT_TEST_LIBRARY = os.path.join(HERE, "libmeswish_split3.so")
+SPLIT_TEST_TILES = 3
+# What that build exports: the activation entry points and their helpers.
+SPLIT_TEST_NAMES = ("swish_fwd", "swish_bwd", "swish_fwd_grouped", "swish_bwd_grouped",
+                    "meswish_act_fwd", "meswish_act_bwd", "meswish_strerror",
+                    "meswish_version", "meswish_copy", "meswish_plan")
+
+
+def build(output: str = LIBRARY, extra_flags: list[str] | None = None,
+          sources: list[str] | None = None) -> str:
     """Compile libmeswish.so (always recompiles) and return its path."""
     tmp = output + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", *SOURCES, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", *(sources or SOURCES),
+           "-o", tmp]
     subprocess.run(cmd, check=True)
     os.replace(tmp, output)
     return output
+
+
+def build_split_test() -> str:
+    """The test build of the activation kernels with SPLIT_TEST_TILES tiles
+    per launch (used by the GPU tests of the multi-launch split only)."""
+    return build(SPLIT_TEST_LIBRARY, [f"-DMESWISH_MAX_LAUNCH_TILES={SPLIT_TEST_TILES}"],
+                 [os.path.join(HERE, "csrc", "meswish.hip")])
 
 
 if __name__ == "__main__":

@@ -546,8 +546,14 @@ static int64_t grid_for_tiles(int64_t tiles, int block)
 
 // Tiles per launch of the vector kernel: tile indices stay 32-bit, and a
 // tile index plus the grid never wraps.  Longer tensors take several
-// launches of this many tiles each.
-constexpr int64_t kMaxLaunchTiles = (int64_t)1 << 30;
+// launches of this many tiles each.  (A test build sets a small value so
+// that the multi-launch split runs on tensors that fit a GPU.)
+#ifndef MESWISH_MAX_LAUNCH_TILES
+#define MESWISH_MAX_LAUNCH_TILES (1 << 30)
+#endif
+constexpr int64_t kMaxLaunchTiles = (int64_t)(MESWISH_MAX_LAUNCH_TILES);
+static_assert(kMaxLaunchTiles >= 1 && kMaxLaunchTiles <= ((int64_t)1 << 30),
+              "tile indices and tile + grid must stay below 2^32");
 
 static size_t elem_size(int dtype) { return dtype == MESWISH_F32 ? 4 : 2; }
 

@@ -32,19 +32,20 @@ def plan(lib, x, dy, out, n, dtype, bwd, alpha=1.0):
 LAUNCH_TILES = 1 << 30
 
 
-def covered(p, n, esize):
+def covered(p, n, esize, launch_tiles=None):
     """Element indices the kernels touch, by the kernels' own arithmetic:
     launch c of the vector path covers tiles [c L, (c + 1) L) of the body
     (L = LAUNCH_TILES) from a pointer at the start of its part; block b takes
     tiles b, b + grid, ... of its launch; the first launch also does the
     head and the last the tail."""
     E, TV = p.elems_per_vector, p.vectors_per_tile
+    L = launch_tiles or LAUNCH_TILES
     seen = np.zeros(n, dtype=np.int32)
     if p.path == _lib.PATH_VECTOR:
         done = 0
         for c in range(p.launches):
-            nt = min(p.tiles - c * LAUNCH_TILES, LAUNCH_TILES)
-            vecs = min(nt * TV, p.nvec - c * LAUNCH_TILES * TV)
+            nt = min(p.tiles - c * L, L)
+            vecs = min(nt * TV, p.nvec - c * L * TV)
             last_vecs = vecs - (nt - 1) * TV if nt else 0
             head = p.head if c == 0 else 0
             tail = p.tail if c + 1 == p.launches else 0
@@ -163,3 +164,27 @@ def test_plan_grid_stays_below_the_thread_limit(lib, bwd):
     # Past 2^30 tiles: 2^42 bfloat16 elements are 2^39 vectors.
     p = plan(lib, x, dy if bwd else None, out, 1 << 42, _lib.BF16, bwd)[1]
     assert p.launches == (1 << 39) // p.vectors_per_tile // LAUNCH_TILES >= 2
+
+
+def test_split_into_several_launches():
+    """The test build with 3 tiles per launch (built by __graft_entry__.build())
+    splits moderate tensors into several launches; the kernels' arithmetic,
+    launch by launch, covers every element exactly once, with the head in
+    the first launch and the tail in the last."""
+    from memory_efficient_activation_amd import build as lib_build
+    if not __import__("os").path.exists(lib_build.SPLIT_TEST_LIBRARY):
+        pytest.fail("the split test build is missing (run __graft_entry__.build())")
+    lib3 = _lib.library(lib_build.SPLIT_TEST_LIBRARY, lib_build.SPLIT_TEST_NAMES)
+    L = lib_build.SPLIT_TEST_TILES
+    rng = np.random.default_rng(5)
+    for dtype, esize in ((_lib.F32, 4), (_lib.BF16, 2)):
+        for bwd in (0, 1):
+            for n in (1, 100, 511, 2048, 2049, 5000, 9 * 512 + 7, 40000):
+                off = int(rng.integers(0, 16 // esize)) * esize
+                x, dy, out = BASE + off, BASE + (1 << 30) + off, BASE + (2 << 30) + off
+                st, p = plan(lib3, x, dy if bwd else None, out, n, dtype, bwd)
+                assert st == _lib.OK and p.path == _lib.PATH_VECTOR
+                assert p.launches == max(1, -(-p.tiles // L)), (n, p.tiles, p.launches)
+                assert p.grid <= L
+                seen = covered(p, n, esize, launch_tiles=L)
+                assert (seen == 1).all(), (dtype, bwd, n, off)
