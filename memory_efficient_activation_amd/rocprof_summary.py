@@ -12,6 +12,7 @@ Usage (after the rocprofv3 runs listed in each summary's header):
     python -m memory_efficient_activation_amd.rocprof_summary dense-traffic FETCH_DIR WRITE_DIR f32|bf16
     python -m memory_efficient_activation_amd.rocprof_summary fft-trace DIR
     python -m memory_efficient_activation_amd.rocprof_summary fft-traffic FETCH_DIR WRITE_DIR
+    python -m memory_efficient_activation_amd.rocprof_summary counters DIR act|dense|fft [--io f32]
 
 ``trace``   reads ``*_kernel_stats.csv`` and ``*_kernel_trace.csv`` from a
             ``--kernel-trace --stats --output-format csv`` run and prints the
@@ -40,6 +41,9 @@ Usage (after the rocprofv3 runs listed in each summary's header):
             each launch is attributed to its stage by kernel and grid size;
             transforms count their real maps and half spectra (8 bytes per
             bin), products their three spectrum arrays and 8 M N K P flops.
+``counters`` every counter of one ``--pmc`` run, as the mean per dispatch
+            of each kernel (grouped as the family's other modes group them),
+            with the sha256 of the family's kernel sources.
 """
 
 from __future__ import annotations
@@ -572,6 +576,42 @@ def fft_traffic(fetch_dir: str, write_dir: str) -> str:
     return "\n".join(out)
 
 
+def counters(d: str, family: str) -> str:
+    """Mean per dispatch of every collected counter, per kernel group."""
+    if family == "dense":
+        key, sources = (lambda r: dense_kind(r["Kernel_Name"])), DENSE_SOURCES
+    elif family == "fft":
+        def key(r):
+            k = fft_key(r)
+            return fft_stages().get(k, (f"{k[0]} {k[1]}",))[0] if k[0] != "copy" else "copy"
+        sources = FFT_SOURCES
+    else:
+        key, sources = (lambda r: kind(r["Kernel_Name"], act_of(r["Kernel_Name"]))), SOURCES
+    rows = list(csv.DictReader(open(_one(os.path.join(d, "*_counter_collection.csv")))))
+    acc: dict = {}
+    disp: dict = {}
+    names: list = []
+    for r in rows:
+        k = key(r)
+        if k == "other":
+            continue
+        c = r["Counter_Name"]
+        if c not in names:
+            names.append(c)
+        acc.setdefault(k, {}).setdefault(c, []).append(float(r["Counter_Value"]))
+        disp.setdefault(k, set()).add(r["Dispatch_Id"])
+    out = ["| kernel | dispatches | " + " | ".join(names) + " |",
+           "|---|---|" + "---|" * len(names)]
+    for k in sorted(acc):
+        vals = [f"{statistics.fmean(acc[k][c]):.6g}" if c in acc[k] else "-" for c in names]
+        out.append(f"| {k} | {len(disp[k])} | " + " | ".join(vals) + " |")
+    h = hashlib.sha256()
+    for path in sources:
+        h.update(open(path, "rb").read())
+    out += ["", f"kernel_source_sha256: {h.hexdigest()}"]
+    return "\n".join(out)
+
+
 def main(argv):
     io, elements = IO, None
     for flag in ("--io", "--elements"):
@@ -601,6 +641,8 @@ def main(argv):
         print(fft_trace(argv[1]))
     elif len(argv) >= 3 and argv[0] == "fft-traffic":
         print(fft_traffic(argv[1], argv[2]))
+    elif len(argv) >= 3 and argv[0] == "counters":
+        print(counters(argv[1], argv[2]))
     elif len(argv) >= 1 and argv[0] == "rare":
         print(rare_rate(int(argv[1]) if len(argv) >= 2 else 4))
     else:

@@ -98,3 +98,21 @@ def test_valu_table(tmp_path):
     rows = {r[0]: r for r in _rows(rs.valu(str(tmp_path)))}
     assert rows["swish fwd"][1:] == ["1", "60.0", "30.0", "9.00", "2.00"]
     assert rows["swish bwd"][1:] == ["2", "60.0", "45.0", "15.00", "2.00"]
+
+
+def test_counters_table(tmp_path):
+    """Means per dispatch per kernel group, one column per counter, in the
+    order the counters first appear; unrelated kernels are left out."""
+    fwd = "void dense_bn::fwd_kernel<float, 4>(dense_bn::Table, x)"
+    with open(tmp_path / "u_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Grid_Size", "Workgroup_Size", "Counter_Name",
+                    "Counter_Value"])
+        for d, (name, a, b) in enumerate([(fwd, 10, 1), (fwd, 30, 3), (COPY, 7, 2),
+                                          (OTHER, 99, 99)]):
+            w.writerow([d + 1, name, 256, 256, "A_CTR", a])
+            w.writerow([d + 1, name, 256, 256, "B_CTR", b])
+    rows = _rows(rs.counters(str(tmp_path), "dense"))
+    assert rows[0] == ["copy", "1", "7", "2"]
+    assert rows[1] == ["fwd", "2", "20", "2"]
+    assert len([r for r in rows if r and r[0] in ("copy", "fwd")]) == 2
