@@ -54,11 +54,23 @@ namespace dense_bn {
 #ifndef DENSE_BN_NT
 #define DENSE_BN_NT 4
 #endif
-// Elements of one channel per block in the forward's vector path (32 KiB
-// of binary32, 16 KiB of bfloat16): measured fastest for both, against 16,
-// 32, 64 and 128 KiB chunks.
-#ifndef DENSE_BN_FWD_CHUNK_ELEMS
-#define DENSE_BN_FWD_CHUNK_ELEMS 8192
+// The forward's vector path: threads per block and elements of one channel
+// per block, per element type.  8 KiB blocks measured fastest in both:
+// binary32 as one wave of 8 vectors per lane (5280 GB/s against 5018 for
+// 256 threads over 32 KiB), bfloat16 as two waves of 4 vectors per lane
+// (5237 against 5189); 1024- to 8192-element chunks of 64, 128 and 256
+// threads were measured.
+#ifndef DENSE_BN_FWD_BLOCK_F32
+#define DENSE_BN_FWD_BLOCK_F32 64
+#endif
+#ifndef DENSE_BN_FWD_CHUNK_F32
+#define DENSE_BN_FWD_CHUNK_F32 2048
+#endif
+#ifndef DENSE_BN_FWD_BLOCK_BF16
+#define DENSE_BN_FWD_BLOCK_BF16 128
+#endif
+#ifndef DENSE_BN_FWD_CHUNK_BF16
+#define DENSE_BN_FWD_CHUNK_BF16 4096
 #endif
 
 constexpr int kBlock = 256;             // threads per block
@@ -67,7 +79,9 @@ constexpr int kMaxSources = DENSE_BN_MAX_SOURCES;
 // The workspace is sized for the smallest chunk (binary32).
 constexpr int kMinChunk = DENSE_BN_CHUNK_BYTES / 4;
 static_assert(kMinChunk % (kBlock * 8) == 0, "a chunk must give every lane whole vectors");
-static_assert(DENSE_BN_FWD_CHUNK_ELEMS % (kBlock * 8) == 0, "whole 16-byte vectors per lane");
+static_assert(DENSE_BN_FWD_CHUNK_F32 % (DENSE_BN_FWD_BLOCK_F32 * 4) == 0 &&
+                  DENSE_BN_FWD_CHUNK_BF16 % (DENSE_BN_FWD_BLOCK_BF16 * 8) == 0,
+              "whole 16-byte vectors per lane");
 constexpr bool kNtX = (DENSE_BN_NT & 1) != 0;
 constexpr bool kNtDz = (DENSE_BN_NT & 2) != 0;
 constexpr bool kNtOut = (DENSE_BN_NT & 4) != 0;
@@ -214,13 +228,20 @@ template <typename IO> struct Raw<IO, 1> {
 template <typename IO, int kBytes = DENSE_BN_CHUNK_BYTES>
 constexpr int chunk_elems() { return kBytes / (int)sizeof(IO); }
 
-// The forward's vector path takes its own chunk: it keeps no partials, and
-// a fixed element count measured fastest for it in both element types (the
-// element-wise path keeps the common chunk, which bounds its registers).
+// The forward's vector path takes its own chunk and block: it keeps no
+// partials (the element-wise path keeps the common chunk and block, which
+// bound its registers).
 template <typename IO, int V>
 constexpr int fwd_chunk_bytes()
 {
-    return V == 1 ? DENSE_BN_CHUNK_BYTES : DENSE_BN_FWD_CHUNK_ELEMS * (int)sizeof(IO);
+    return V == 1 ? DENSE_BN_CHUNK_BYTES
+                  : (sizeof(IO) == 4 ? DENSE_BN_FWD_CHUNK_F32 : DENSE_BN_FWD_CHUNK_BF16) *
+                        (int)sizeof(IO);
+}
+
+template <typename IO, int V> constexpr int fwd_block()
+{
+    return V == 1 ? kBlock : sizeof(IO) == 4 ? DENSE_BN_FWD_BLOCK_F32 : DENSE_BN_FWD_BLOCK_BF16;
 }
 
 struct FastDiv {
@@ -464,13 +485,13 @@ __global__ __launch_bounds__(kBlock) void stats_final_kernel(const IO* __restric
 }
 
 template <typename IO, int V>
-__global__ __launch_bounds__(kBlock) void fwd_kernel(Table t, Geom geo, int z_channels,
-                                                     const float* __restrict__ gamma,
-                                                     const float* __restrict__ beta, float eps,
-                                                     IO* __restrict__ z)
+__global__ __launch_bounds__((fwd_block<IO, V>())) void fwd_kernel(
+    Table t, Geom geo, int z_channels, const float* __restrict__ gamma,
+    const float* __restrict__ beta, float eps, IO* __restrict__ z)
 {
     constexpr int kChunk = chunk_elems<IO, fwd_chunk_bytes<IO, V>()>();
-    constexpr int kPer = kChunk / (kBlock * V);
+    constexpr int kB = fwd_block<IO, V>();
+    constexpr int kPer = kChunk / (kB * V);
     const Where w = locate(t, geo.chunks);
     const IO* x = static_cast<const IO*>(t.x[w.j]);
     const int cj = t.channels[w.j];
@@ -479,7 +500,7 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(Table t, Geom geo, int z_ch
     bool ok[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-        vv[i] = (uint32_t)w.chunk * (uint32_t)(kChunk / V) + (uint32_t)(i * kBlock) + threadIdx.x;
+        vv[i] = (uint32_t)w.chunk * (uint32_t)(kChunk / V) + (uint32_t)(i * kB) + threadIdx.x;
         ok[i] = vv[i] < geo.mv;
         if (ok[i])
             rx[i].template fetch<kNtX>(x, elem_offset(vv[i], geo.pv, cj, w.cl, V));
@@ -654,11 +675,12 @@ static Geom make_geom(size_t n, size_t hw, int V)
     return g;
 }
 
-static int launch(const void* fn, int64_t grid, void** args, hipStream_t stream)
+static int launch(const void* fn, int64_t grid, void** args, hipStream_t stream,
+                  int block = kBlock)
 {
     if (grid <= 0 || grid > 0x7FFFFFFF)
         return MESWISH_EINVAL;
-    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kBlock), args, 0, stream);
+    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(block), args, 0, stream);
     return e == hipSuccess ? MESWISH_OK : MESWISH_EHIP;
 }
 
@@ -763,7 +785,7 @@ static int run_fwd(Table& t, int total, size_t n, size_t hw, int z_channels, con
     IO* zp = static_cast<IO*>(z);
     void* a[] = {&t, &geo, &z_channels, &gamma, &beta, &eps, &zp};
     return launch(reinterpret_cast<const void*>(&fwd_kernel<IO, V>),
-                  (int64_t)total * geo.chunks, a, stream);
+                  (int64_t)total * geo.chunks, a, stream, fwd_block<IO, V>());
 }
 
 template <typename IO, int V>
