@@ -31,10 +31,9 @@
 //     through LDS with the next step prefetched into registers; all tiles
 //     of one bin run on one XCD (shared operands stay in that XCD's L2).
 //   * Inverse.  Column transforms first, keeping only the rows that survive
-//     the crop, then row transforms of the Hermitian half rows, two rows
-//     per complex transform (one in the real part, one in the imaginary);
-//     only the kept m x m corner is written, scaled by 1/n^2, through LDS
-//     as whole 16-byte vectors when the rows are cropped.
+//     the crop, then row transforms of the Hermitian half rows; only the
+//     kept m x m corner is written, scaled by 1/n^2, through LDS as whole
+//     16-byte vectors when the rows are cropped.
 
 #include <hip/hip_runtime.h>
 
@@ -190,64 +189,6 @@ template <int N> using InvTile = Tile<N, true>;
 // zero-padded to N x N -> half spectra, bin-major.
 // ---------------------------------------------------------------------------
 
-// Row of m reals (m <= N) into x[0..N), zero-padded: 16-byte loads when
-// every row is 16-byte aligned (m = N and the maps' base aligned), pairs
-// when m is even (8-byte aligned rows), else one element at a time.
-template <int N>
-__device__ __forceinline__ void load_row(const float* row, int m, bool base16, float (&x)[N])
-{
-    if (m == N && base16) {
-#pragma unroll
-        for (int c = 0; c < N; c += 4) {
-            const float4 q = *reinterpret_cast<const float4*>(row + c);
-            x[c] = q.x;
-            x[c + 1] = q.y;
-            x[c + 2] = q.z;
-            x[c + 3] = q.w;
-        }
-    } else if ((m & 1) == 0 && ((uintptr_t)row & 7u) == 0) {
-#pragma unroll
-        for (int c = 0; c < N; c += 2) {
-            const float2 q = c < m ? *reinterpret_cast<const float2*>(row + c)
-                                   : make_float2(0.0f, 0.0f);
-            x[c] = q.x;
-            x[c + 1] = q.y;
-        }
-    } else {
-#pragma unroll
-        for (int c = 0; c < N; ++c)
-            x[c] = c < m ? row[c] : 0.0f;
-    }
-}
-
-// Row of m reals (the real parts of a[], or the imaginary parts when IM)
-// times scale to out: 16-byte stores when m is a multiple of 4 and the
-// output 16-byte aligned (then every row is), pairs when m is even and the
-// output 8-byte aligned, else one element at a time.
-template <int N>
-__device__ __forceinline__ void store_row(float* out, int m, bool base16, const float2 (&a)[N],
-                                          float scale, bool im)
-{
-    auto val = [&](int q) { return (im ? a[q].y : a[q].x) * scale; };
-    if ((m & 3) == 0 && base16) {
-#pragma unroll
-        for (int q = 0; q < N; q += 4)
-            if (q < m)
-                *reinterpret_cast<float4*>(out + q) = make_float4(val(q), val(q + 1), val(q + 2),
-                                                                  val(q + 3));
-    } else if ((m & 1) == 0 && ((uintptr_t)out & 7u) == 0) {
-#pragma unroll
-        for (int q = 0; q < N; q += 2)
-            if (q < m)
-                *reinterpret_cast<float2*>(out + q) = make_float2(val(q), val(q + 1));
-    } else {
-#pragma unroll
-        for (int q = 0; q < N; ++q)
-            if (q < m)
-                out[q] = val(q);
-    }
-}
-
 // One set of maps to transform: `batch` maps of m x m at x -> spec.
 struct R2cJob {
     const float* x;
@@ -272,12 +213,8 @@ __global__ __launch_bounds__(Tile<N>::kThreads) void r2c_kernel(R2cJob a, R2cJob
     const int m = second ? b.m : a.m;
     const int64_t b0 = (int64_t)((int)blockIdx.x - (second ? blocks0 : 0)) * T;
 
-    // Rows: job = (map, r), one row per transform.  (Two real rows per
-    // complex transform, as the inverse does, halves the arithmetic here but
-    // measured slower: each lane then holds two rows' loads in flight, and
-    // the 64 rows of a wave already touch 64 lines per load instruction.)
+    // Rows: job = (map, r).
     constexpr int NT = Tile<N>::kThreads;
-    const bool base16 = ((uintptr_t)x & 15u) == 0;
     for (int job = threadIdx.x; job < T * N; job += NT) {
         const int map = job / N, r = job - map * N;
         const int64_t b = b0 + map;
@@ -288,12 +225,31 @@ __global__ __launch_bounds__(Tile<N>::kThreads) void r2c_kernel(R2cJob a, R2cJob
                 out[v] = make_float2(0.0f, 0.0f);
             continue;
         }
-        float xr[N];
-        load_row<N>(x + (b * m + r) * (int64_t)m, m, base16, xr);
+        const float* row = x + (b * m + r) * (int64_t)m;
         float2 a[N];
+        if (m == N) {
 #pragma unroll
-        for (int c = 0; c < N; ++c)
-            a[c] = make_float2(xr[c], 0.0f);
+            for (int c = 0; c < N; c += 4) {
+                const float4 q = *reinterpret_cast<const float4*>(row + c);
+                a[c] = make_float2(q.x, 0.0f);
+                a[c + 1] = make_float2(q.y, 0.0f);
+                a[c + 2] = make_float2(q.z, 0.0f);
+                a[c + 3] = make_float2(q.w, 0.0f);
+            }
+        } else if ((m & 1) == 0 && ((uintptr_t)x & 7u) == 0) {
+            // Even m: every row starts 8-byte aligned; load pairs.
+#pragma unroll
+            for (int c = 0; c < N; c += 2) {
+                const float2 q = c < m ? *reinterpret_cast<const float2*>(row + c)
+                                       : make_float2(0.0f, 0.0f);
+                a[c] = make_float2(q.x, 0.0f);
+                a[c + 1] = make_float2(q.y, 0.0f);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < N; ++c)
+                a[c] = make_float2(c < m ? row[c] : 0.0f, 0.0f);
+        }
         fft_reg<N, false>(a);
 #pragma unroll
         for (int v = 0; v < H; ++v)
@@ -362,75 +318,87 @@ __global__ __launch_bounds__(InvTile<N>::kThreads) void c2r_kernel(const float2*
     }
     __syncthreads();
 
-    // Rows p < m, two at a time: job = (map, p0) for p0 < hm = ceil(m/2),
-    // rows p0 and p1 = p0 + hm (consecutive threads on consecutive rows).
-    // Each row holds the half spectrum of a real row (the imaginary parts
-    // at v = 0 and v = N/2 are not used, as in any real inverse); one
-    // complex inverse of Y_p0 + i Y_p1, both extended to full length by
-    // Hermitian symmetry, gives row p0 as its real part and row p1 as its
-    // imaginary part.
-    const int hm = (m + 1) >> 1;
-    auto inverse_pair = [&](int map, int p0, float2 (&a)[N]) {
-        const float2* in0 = buf + map * MS + p0 * H;
-        const float2* in1 = buf + map * MS + (p0 + hm) * H;
-        const bool two = p0 + hm < m;  // row p1 = m is past the crop (odd m)
-        const float2 e0 = in0[0], e1 = two ? in1[0] : make_float2(0.0f, 0.0f);
-        const float2 h0 = in0[N / 2], h1 = two ? in1[N / 2] : make_float2(0.0f, 0.0f);
-        a[0] = make_float2(e0.x, e1.x);
-        a[N / 2] = make_float2(h0.x, h1.x);
-#pragma unroll
-        for (int v = 1; v < N / 2; ++v) {
-            const float2 y0 = in0[v], y1 = two ? in1[v] : make_float2(0.0f, 0.0f);
-            a[v] = make_float2(y0.x - y1.y, y0.y + y1.x);
-            a[N - v] = make_float2(y0.x + y1.y, y1.x - y0.y);
-        }
-        fft_reg<N, true>(a);
-    };
+    // Rows p < m: the row is the half spectrum of a real signal.
     if constexpr (kStaged && N <= 32) {
         // The block's outputs (maps b0 .. b0 + T - 1, m x m each) are one
-        // contiguous range of y: keep each row pair in registers, rebuild
-        // the range in LDS once every row has been read, and store it with
-        // whole 16-byte vectors.  T ceil(m/2) <= T N/2 jobs over T H threads:
-        // one pair per thread at most.
-        static_assert(N / 2 <= H, "one row pair per thread");
-        const int job = (int)threadIdx.x;
-        const int map = job / hm;
-        const bool mine = job < T * hm && b0 + map < batch;
-        const int p0 = job - map * hm;
-        float2 a[N];
-        if (mine)
-            inverse_pair(map, p0, a);
+        // contiguous range of y: keep each row in registers, rebuild the
+        // range in LDS once every row has been read, and store it with
+        // whole 16-byte vectors.
+        constexpr int R = (N + H - 1) / H;  // rows per thread: T m <= T N jobs over T H threads
+        float keep[R][N];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int job = (int)threadIdx.x + r * NT;
+            const int map = job / m;
+            if (job >= T * m || b0 + map >= batch)
+                continue;
+            const float2* in = buf + map * MS + (job - map * m) * H;
+            float2 a[N];
+#pragma unroll
+            for (int v = 0; v < H; ++v)
+                a[v] = in[v];
+#pragma unroll
+            for (int v = H; v < N; ++v)
+                a[v] = conjf2(in[N - v]);
+            fft_reg<N, true>(a);
+#pragma unroll
+            for (int q = 0; q < N; ++q)
+                keep[r][q] = a[q].x * scale;
+        }
         __syncthreads();
         float* stage = reinterpret_cast<float*>(buf);
-        if (mine) {
-            float* row = stage + (map * m + p0) * m;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int job = (int)threadIdx.x + r * NT;
+            const int map = job / m;
+            if (job >= T * m || b0 + map >= batch)
+                continue;
+            float* row = stage + job * m;  // = map m^2 + p m
 #pragma unroll
             for (int q = 0; q < N; ++q)
                 if (q < m)
-                    row[q] = a[q].x * scale;
-            if (p0 + hm < m) {
-                row += hm * m;
-#pragma unroll
-                for (int q = 0; q < N; ++q)
-                    if (q < m)
-                        row[q] = a[q].y * scale;
-            }
+                    row[q] = keep[r][q];
         }
         __syncthreads();
         const int maps = (int)min<int64_t>(T, batch - b0);
         global_from_lds<NT>(y + b0 * m * m, stage, maps * m * m);
     } else {
-        for (int job = threadIdx.x; job < T * hm; job += NT) {
-            const int map = job / hm, p0 = job - map * hm;
+        for (int job = threadIdx.x; job < T * m; job += NT) {
+            const int map = job / m, p = job - map * m;
             const int64_t b = b0 + map;
             if (b >= batch)
                 continue;
+            const float2* in = buf + map * MS + p * H;
             float2 a[N];
-            inverse_pair(map, p0, a);
-            float* out = y + (b * m + p0) * (int64_t)m;
-            store_row<N>(out, m, ((uintptr_t)y & 15u) == 0, a, scale, false);
-            if (p0 + hm < m)
-                store_row<N>(out + hm * m, m, ((uintptr_t)y & 15u) == 0, a, scale, true);
+#pragma unroll
+            for (int v = 0; v < H; ++v)
+                a[v] = in[v];
+#pragma unroll
+            for (int v = H; v < N; ++v)
+                a[v] = conjf2(in[N - v]);
+            fft_reg<N, true>(a);
+            float* out = y + (b * m + p) * (int64_t)m;
+            if ((m & 3) == 0 && ((uintptr_t)y & 15u) == 0) {
+                // m a multiple of 4: every row starts 16-byte aligned; store quads.
+#pragma unroll
+                for (int q = 0; q < N; q += 4)
+                    if (q < m)
+                        *reinterpret_cast<float4*>(out + q) =
+                            make_float4(a[q].x * scale, a[q + 1].x * scale, a[q + 2].x * scale,
+                                        a[q + 3].x * scale);
+            } else if ((m & 1) == 0 && ((uintptr_t)y & 7u) == 0) {
+                // Even m: every row starts 8-byte aligned; store pairs.
+#pragma unroll
+                for (int q = 0; q < N; q += 2)
+                    if (q < m)
+                        *reinterpret_cast<float2*>(out + q) =
+                            make_float2(a[q].x * scale, a[q + 1].x * scale);
+            } else {
+#pragma unroll
+                for (int q = 0; q < N; ++q)
+                    if (q < m)
+                        out[q] = a[q].x * scale;
+            }
         }
     }
 }
