@@ -105,6 +105,45 @@ def test_bf16_element_path_past_2_31(oracle):
     _check(x, dy, y, None, 1.0, oracle, "bf16 element path")
 
 
+N32 = (1 << 32) + 4097  # bf16 elements: 8 GiB + 8 KiB per tensor
+
+
+def test_bf16_element_path_past_2_32_elements(oracle):
+    """x 2 bytes past alignment, y and dy aligned: the element-wise kernels on
+    n = 2^32 + 4097 elements, where one thread per 256-element tile would need
+    a grid of more than 2^32 threads.  The host caps the grid (the kernels
+    loop over the rest); sampled outputs at the start, around 2^31 and 2^32,
+    at the end and 200,000 uniform indices match the oracle."""
+    say(f"[large] bf16 element path n={N32}")
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(31)
+    xb = torch.empty(N32 + 1, dtype=torch.bfloat16, device=dev)
+    xb.normal_(0.0, 4.0, generator=g)
+    x = xb[1:]
+    dy = torch.empty(N32, dtype=torch.bfloat16, device=dev)
+    dy.normal_(0.0, 1.0, generator=g)
+    x[(1 << 32) - 1] = -30.0
+    x[1 << 32] = 7.5
+    y = torch.empty(N32, dtype=torch.bfloat16, device=dev)
+    mea.swish_fwd(x, 1.0, out=y)
+    dx = torch.empty(N32, dtype=torch.bfloat16, device=dev)
+    mea.swish_bwd(x, dy, 1.0, out=dx)
+    torch.cuda.synchronize()
+    idx = torch.cat([torch.arange(0, 2048), torch.arange((1 << 31) - 2048, (1 << 31) + 2048),
+                     torch.arange((1 << 32) - 4096, (1 << 32) + 4096), torch.arange(N32 - 4096, N32),
+                     torch.randint(0, N32, (200000,), generator=torch.Generator().manual_seed(7))])
+    idx = idx.to(dev)
+    xs, dys = to_host(x[idx]), to_host(dy[idx])
+    ry = bf16_report(to_host(y[idx]), oracle.fwd(xs, 1.0, threads=ORACLE_THREADS))
+    odx, _ = oracle.bwd(xs, dys, 1.0, threads=ORACLE_THREADS, want_scale=False)
+    rdx = bf16_report(to_host(dx[idx]), odx)
+    say(f"[large] bf16 element path past 2^32: fwd {ry} bwd {rdx}")
+    assert ry["ok"], ry
+    assert rdx["ok"], rdx
+    del xb, x, dy, y, dx
+
+
 def test_grouped_equals_single_past_2_31():
     say(f"[large] grouped, one tensor of n={N} and one of 1000")
     x, dy = _inputs(torch.bfloat16, 0, seed=23)
