@@ -65,10 +65,12 @@
 #ifndef MESWISH_BLOCK_F32
 #define MESWISH_BLOCK_F32 64
 #endif
-// Threads per block of the grouped kernel (bf16): a grouped block finds its
-// tensor by dependent scalar loads, so it keeps larger tiles.
+// Threads per block of the grouped kernel (bf16): one wave, as for single
+// tensors (measured against 128 and 256 with 1, 2 and 4 tiles per block:
+// 6583 GB/s for the EfficientNet-shaped group against 6253-6313 with 256
+// threads).
 #ifndef MESWISH_GROUP_BLOCK_BF16
-#define MESWISH_GROUP_BLOCK_BF16 256
+#define MESWISH_GROUP_BLOCK_BF16 64
 #endif
 // 16-byte vectors per thread and stream, per element type.
 #ifndef MESWISH_UNROLL_BF16
@@ -79,13 +81,13 @@
 #endif
 // Consecutive tiles per block of the grouped kernel.  A grouped block finds
 // its tensor through dependent scalar loads before its first vector load;
-// two tiles per block share that cost in the forward (+5 % there), while
-// the backward, with twice the bytes per tile, is fastest at one.
+// with one-wave blocks two tiles per block share that cost best in both
+// directions (one: 6344-6359 GB/s, four: 6229-6304).
 #ifndef MESWISH_GROUP_TILES_FWD
 #define MESWISH_GROUP_TILES_FWD 2
 #endif
 #ifndef MESWISH_GROUP_TILES_BWD
-#define MESWISH_GROUP_TILES_BWD 1
+#define MESWISH_GROUP_TILES_BWD 2
 #endif
 #ifndef MESWISH_BLOCKS_PER_CU
 #define MESWISH_BLOCKS_PER_CU 100000
