@@ -76,6 +76,8 @@ def test_binding_constants_match_header(lib):
     m = re.search(r"#define MESWISH_MAX_GROUP (\d+)", _header_text())
     assert int(m.group(1)) == _lib.MAX_GROUP
     assert set(_lib.EXPORTED) == set(declared_functions())
+    # The binding declares argument types for exactly those functions.
+    assert set(_lib._signatures()) == set(_lib.EXPORTED)
     m = re.findall(r"MESWISH_PATH_(\w+)\s*=\s*(-?\d+)", _header_text())
     assert {k: int(v) for k, v in m} == {"NONE": _lib.PATH_NONE, "VECTOR": _lib.PATH_VECTOR,
                                          "ELEMENT": _lib.PATH_ELEMENT}
