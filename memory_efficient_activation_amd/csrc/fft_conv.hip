@@ -32,8 +32,11 @@
 //     of one bin run on one XCD (shared operands stay in that XCD's L2).
 //   * Inverse.  Column transforms first, keeping only the rows that survive
 //     the crop, then row transforms of the Hermitian half rows; only the
-//     kept m x m corner is written, scaled by 1/n^2, through LDS as whole
-//     16-byte vectors when the rows are cropped.
+//     kept m x m corner is written, scaled by 1/n^2, and it goes out through
+//     LDS as whole 16-byte vectors over the block's contiguous range of
+//     maps (whole maps: each row's result over its own LDS row).
+//   * Forward rows are assigned only to the m rows a map has, so no lane of
+//     a wave idles on a zero row; the zero rows are filled in LDS.
 
 #include <hip/hip_runtime.h>
 
@@ -145,13 +148,20 @@ __device__ __forceinline__ void fft_reg(float2 (&a)[N])
 #ifndef FFTCONV_C2R_MAPS_32
 #define FFTCONV_C2R_MAPS_32 32
 #endif
-// Inverse transforms up to n = 32 can store their real maps through LDS as
-// whole 16-byte vectors over the block's contiguous range of maps, instead
-// of row by row from registers: 0 never, 1 for maps smaller than n x n (rows
-// that are not whole 16-byte multiples), 2 always.  (The same staging of the
-// forward transforms' loads measured slower on every map size.)
+// Inverse transforms up to n = 32 can store their cropped maps through LDS
+// as whole 16-byte vectors over the block's contiguous range of maps,
+// instead of row by row from registers: 0 never, 1 for maps smaller than
+// n x n (rows that are not whole 16-byte multiples), 2 always.  (The same
+// staging of the forward transforms' loads measured slower on every map
+// size.)  Whole maps (m = n) take FFTCONV_FULL_INPLACE instead: each row's
+// result is written over its own LDS row, with no registers held across
+// the block's barrier, then the block stores its range as 16-byte vectors
+// (1), or each row is stored from registers (0).
 #ifndef FFTCONV_STAGE_POLICY
 #define FFTCONV_STAGE_POLICY 1
+#endif
+#ifndef FFTCONV_FULL_INPLACE
+#define FFTCONV_FULL_INPLACE 1
 #endif
 
 static bool staged(int n, int m)
@@ -213,13 +223,15 @@ __global__ __launch_bounds__(Tile<N>::kThreads) void r2c_kernel(R2cJob a, R2cJob
     const int m = second ? b.m : a.m;
     const int64_t b0 = (int64_t)((int)blockIdx.x - (second ? blocks0 : 0)) * T;
 
-    // Rows: job = (map, r).
+    // Rows r < m: job = (map, r), so that no lane idles on a zero row while
+    // the others of its wave transform (kernels and output gradients are
+    // smaller than n x n).  Maps past the batch are zero.
     constexpr int NT = Tile<N>::kThreads;
-    for (int job = threadIdx.x; job < T * N; job += NT) {
-        const int map = job / N, r = job - map * N;
+    for (int job = threadIdx.x; job < T * m; job += NT) {
+        const int map = job / m, r = job - map * m;
         const int64_t b = b0 + map;
         float2* out = buf + map * MS + r * H;
-        if (b >= batch || r >= m) {
+        if (b >= batch) {
 #pragma unroll
             for (int v = 0; v < H; ++v)
                 out[v] = make_float2(0.0f, 0.0f);
@@ -254,6 +266,19 @@ __global__ __launch_bounds__(Tile<N>::kThreads) void r2c_kernel(R2cJob a, R2cJob
 #pragma unroll
         for (int v = 0; v < H; ++v)
             out[v] = a[v];
+    }
+    // Rows m .. N - 1 (the zero padding): one contiguous run of (N - m) H
+    // values per map, one whole wave per map (a partial last wave of the
+    // block takes none).
+    constexpr int kWholeWaves = NT / 64;
+    if (m < N && (int)threadIdx.x < kWholeWaves * 64) {
+        const int run = (N - m) * H;
+        const int lane = (int)threadIdx.x & 63;
+        for (int map = (int)threadIdx.x >> 6; map < T; map += kWholeWaves) {
+            float2* z = buf + map * MS + m * H;
+            for (int i = lane; i < run; i += 64)
+                z[i] = make_float2(0.0f, 0.0f);
+        }
     }
     __syncthreads();
 
@@ -362,6 +387,41 @@ __global__ __launch_bounds__(InvTile<N>::kThreads) void c2r_kernel(const float2*
         __syncthreads();
         const int maps = (int)min<int64_t>(T, batch - b0);
         global_from_lds<NT>(y + b0 * m * m, stage, maps * m * m);
+    } else if (FFTCONV_FULL_INPLACE && m == N && ((uintptr_t)y & 15u) == 0) {
+        // Whole maps: each row job writes its N real outputs over the LDS
+        // row it has just read (N floats fit in its H complex slots, and no
+        // other thread touches that row), then the block stores its maps --
+        // one contiguous range of y -- as whole 16-byte vectors, so that a
+        // wave's store covers contiguous lines instead of one 16-byte piece
+        // of 64 rows.
+        for (int job = threadIdx.x; job < T * N; job += NT) {
+            const int map = job / N, p = job - map * N;
+            if (b0 + map >= batch)
+                continue;
+            float2* in = buf + map * MS + p * H;
+            float2 a[N];
+#pragma unroll
+            for (int v = 0; v < H; ++v)
+                a[v] = in[v];
+#pragma unroll
+            for (int v = H; v < N; ++v)
+                a[v] = conjf2(in[N - v]);
+            fft_reg<N, true>(a);
+            float* o = reinterpret_cast<float*>(in);
+#pragma unroll
+            for (int q = 0; q < N; q += 2)
+                *reinterpret_cast<float2*>(o + q) = make_float2(a[q].x * scale, a[q + 1].x * scale);
+        }
+        __syncthreads();
+        const int maps = (int)min<int64_t>(T, batch - b0);
+        float4* out = reinterpret_cast<float4*>(y + b0 * N * N);
+        for (int e = threadIdx.x; e < maps * N * (N / 4); e += NT) {
+            const int row = e / (N / 4), q4 = e - row * (N / 4);  // row = map N + p
+            const int map = row / N, p = row - map * N;
+            const float2* src = buf + map * MS + p * H + 2 * q4;
+            const float2 lo = src[0], hi = src[1];
+            out[e] = make_float4(lo.x, lo.y, hi.x, hi.y);
+        }
     } else {
         for (int job = threadIdx.x; job < T * m; job += NT) {
             const int map = job / m, p = job - map * m;
