@@ -564,7 +564,7 @@ void cgemm_planar_kernel(const float2* __restrict__ A,
             float2 v = make_float2(0.0f, 0.0f);
             if ((a_inside && k_inside) || (i0 + i < M && k0 + k < K))
                 v = AK ? Ap[(int64_t)(i0 + i) * lda + (k0 + k)] : Ap[(int64_t)(k0 + k) * lda + (i0 + i)];
-            ra[qq] = CA ? conjf2(v) : v;
+            ra[qq] = v;
         }
 #pragma unroll
         for (int qq = 0; qq < LB; ++qq) {
@@ -573,30 +573,35 @@ void cgemm_planar_kernel(const float2* __restrict__ A,
             float2 w = make_float2(0.0f, 0.0f);
             if ((b_inside && k_inside) || (j0 + j < N && k0 + k < K))
                 w = BK ? Bp[(int64_t)(j0 + j) * ldb + (k0 + k)] : Bp[(int64_t)(k0 + k) * ldb + (j0 + j)];
-            rb[qq] = CB ? conjf2(w) : w;
+            rb[qq] = w;
         }
     };
+    // The conjugations are applied here, as the values go to LDS, and not
+    // as they arrive: an operation on a loaded register right after its load
+    // would make the wave wait for the prefetch at once.
     auto stash = [&]() {
 #pragma unroll
         for (int qq = 0; qq < LA; ++qq) {
             const int idx = threadIdx.x + qq * NT;
             const int k = AK ? idx % kPK : idx / BM, i = AK ? idx / kPK : idx % BM;
-            Ar[k][i] = ra[qq].x;
-            Ai[k][i] = ra[qq].y;
+            const float2 v = CA ? conjf2(ra[qq]) : ra[qq];
+            Ar[k][i] = v.x;
+            Ai[k][i] = v.y;
             if constexpr (kGauss)
-                As[k][i] = ra[qq].x + ra[qq].y;
+                As[k][i] = v.x + v.y;
         }
 #pragma unroll
         for (int qq = 0; qq < LB; ++qq) {
             const int idx = threadIdx.x + qq * NT;
             const int k = BK ? idx % kPK : idx / BN, j = BK ? idx / kPK : idx % BN;
+            const float2 w = CB ? conjf2(rb[qq]) : rb[qq];
             if constexpr (kGauss) {
-                Br[k][j] = rb[qq].x;
-                Bi[k][j] = rb[qq].y - rb[qq].x;
-                Bs[k][j] = rb[qq].x + rb[qq].y;
+                Br[k][j] = w.x;
+                Bi[k][j] = w.y - w.x;
+                Bs[k][j] = w.x + w.y;
             } else {
-                Br[k][j] = rb[qq].x;
-                Bi[k][j] = rb[qq].y;
+                Br[k][j] = w.x;
+                Bi[k][j] = w.y;
             }
         }
     };
