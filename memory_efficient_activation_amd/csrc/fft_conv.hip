@@ -43,6 +43,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fft_conv.h"
 
 namespace fftconv {
@@ -513,6 +515,12 @@ constexpr int kPK = FFTCONV_PLANAR_KT;
 // 128 x 32 tiles (four waves of 32 x 32 in a column) for the 32-column
 // products: 17 % fewer operand bytes per output than 64 x 32 tiles of two
 // waves, 5-8 % faster input- and weight-gradient products.
+// Operand loads in pairs of adjacent values, as 16-byte vectors where the
+// tile is wholly inside the matrix and the pairs are aligned (1), or value
+// by value (0).
+#ifndef FFTCONV_PAIR_LOADS
+#define FFTCONV_PAIR_LOADS 1
+#endif
 #ifndef FFTCONV_PLANAR_WR4
 #define FFTCONV_PLANAR_WR4 1
 #endif
@@ -551,29 +559,79 @@ void cgemm_planar_kernel(const float2* __restrict__ A,
 
     // Global -> register staging of one K-tile; the next tile's loads are
     // issued as soon as the current one is in LDS, before the barrier and
-    // the current tile's products.
+    // the current tile's products.  With kPairA (kPairB), each thread takes
+    // pairs of values adjacent along the operand's contiguous dimension, and
+    // a tile wholly inside the matrix with 16-byte aligned pairs loads each
+    // pair as one 16-byte vector.
+    constexpr bool kPairA = FFTCONV_PAIR_LOADS && LA % 2 == 0;
+    constexpr bool kPairB = FFTCONV_PAIR_LOADS && LB % 2 == 0;
     float2 ra[LA], rb[LB];
     // Tiles wholly inside the matrices load without per-element checks.
     const bool a_inside = i0 + BM <= M, b_inside = j0 + BN <= N;
-    auto fetch = [&](int k0) {
+    const bool a_aligned = ((uintptr_t)A & 15u) == 0 && (sAp & 1) == 0 && (lda & 1) == 0;
+    const bool b_aligned = ((uintptr_t)B & 15u) == 0 && (sBp & 1) == 0 && (ldb & 1) == 0;
+    // Value slot s of this thread: its (k, row) in the tile.  Pairs: slots
+    // 2q and 2q + 1 are adjacent along the contiguous dimension.
+    auto a_slot = [&](int s2, int& k, int& i) {
+        if constexpr (kPairA) {
+            const int idx = threadIdx.x + (s2 >> 1) * NT;
+            if (AK) { k = 2 * (idx % (kPK / 2)) + (s2 & 1); i = idx / (kPK / 2); }
+            else { i = 2 * (idx % (BM / 2)) + (s2 & 1); k = idx / (BM / 2); }
+        } else {
+            const int idx = threadIdx.x + s2 * NT;
+            k = AK ? idx % kPK : idx / BM;
+            i = AK ? idx / kPK : idx % BM;
+        }
+    };
+    auto b_slot = [&](int s2, int& k, int& j) {
+        if constexpr (kPairB) {
+            const int idx = threadIdx.x + (s2 >> 1) * NT;
+            if (BK) { k = 2 * (idx % (kPK / 2)) + (s2 & 1); j = idx / (kPK / 2); }
+            else { j = 2 * (idx % (BN / 2)) + (s2 & 1); k = idx / (BN / 2); }
+        } else {
+            const int idx = threadIdx.x + s2 * NT;
+            k = BK ? idx % kPK : idx / BN;
+            j = BK ? idx / kPK : idx % BN;
+        }
+    };
+    // VEC: the block's tiles are wholly inside both matrices at every K-tile
+    // and the pairs are 16-byte aligned, so the loads need no checks; the
+    // two cases run separate copies of the loop (a branch per K-tile would
+    // join the loaded registers and wait for the prefetch on the spot).
+    auto fetch = [&](int k0, auto vec) {
+        constexpr bool VEC = decltype(vec)::value;
         const bool k_inside = k0 + kPK <= K;
 #pragma unroll
-        for (int qq = 0; qq < LA; ++qq) {
-            const int idx = threadIdx.x + qq * NT;
-            const int k = AK ? idx % kPK : idx / BM, i = AK ? idx / kPK : idx % BM;
-            float2 v = make_float2(0.0f, 0.0f);
-            if ((a_inside && k_inside) || (i0 + i < M && k0 + k < K))
-                v = AK ? Ap[(int64_t)(i0 + i) * lda + (k0 + k)] : Ap[(int64_t)(k0 + k) * lda + (i0 + i)];
-            ra[qq] = v;
+        for (int qq = 0; qq < LA; qq += (VEC && kPairA) ? 2 : 1) {
+            int k, i;
+            a_slot(qq, k, i);
+            const int64_t off = AK ? (int64_t)(i0 + i) * lda + (k0 + k) : (int64_t)(k0 + k) * lda + (i0 + i);
+            if constexpr (VEC && kPairA) {
+                const float4 q4 = *reinterpret_cast<const float4*>(Ap + off);
+                ra[qq] = make_float2(q4.x, q4.y);
+                ra[qq + 1] = make_float2(q4.z, q4.w);
+            } else if constexpr (VEC) {
+                ra[qq] = Ap[off];
+            } else {
+                ra[qq] = ((a_inside && k_inside) || (i0 + i < M && k0 + k < K)) ? Ap[off]
+                                                                                : make_float2(0.0f, 0.0f);
+            }
         }
 #pragma unroll
-        for (int qq = 0; qq < LB; ++qq) {
-            const int idx = threadIdx.x + qq * NT;
-            const int k = BK ? idx % kPK : idx / BN, j = BK ? idx / kPK : idx % BN;
-            float2 w = make_float2(0.0f, 0.0f);
-            if ((b_inside && k_inside) || (j0 + j < N && k0 + k < K))
-                w = BK ? Bp[(int64_t)(j0 + j) * ldb + (k0 + k)] : Bp[(int64_t)(k0 + k) * ldb + (j0 + j)];
-            rb[qq] = w;
+        for (int qq = 0; qq < LB; qq += (VEC && kPairB) ? 2 : 1) {
+            int k, j;
+            b_slot(qq, k, j);
+            const int64_t off = BK ? (int64_t)(j0 + j) * ldb + (k0 + k) : (int64_t)(k0 + k) * ldb + (j0 + j);
+            if constexpr (VEC && kPairB) {
+                const float4 q4 = *reinterpret_cast<const float4*>(Bp + off);
+                rb[qq] = make_float2(q4.x, q4.y);
+                rb[qq + 1] = make_float2(q4.z, q4.w);
+            } else if constexpr (VEC) {
+                rb[qq] = Bp[off];
+            } else {
+                rb[qq] = ((b_inside && k_inside) || (j0 + j < N && k0 + k < K)) ? Bp[off]
+                                                                                : make_float2(0.0f, 0.0f);
+            }
         }
     };
     // The conjugations are applied here, as the values go to LDS, and not
@@ -582,8 +640,8 @@ void cgemm_planar_kernel(const float2* __restrict__ A,
     auto stash = [&]() {
 #pragma unroll
         for (int qq = 0; qq < LA; ++qq) {
-            const int idx = threadIdx.x + qq * NT;
-            const int k = AK ? idx % kPK : idx / BM, i = AK ? idx / kPK : idx % BM;
+            int k, i;
+            a_slot(qq, k, i);
             const float2 v = CA ? conjf2(ra[qq]) : ra[qq];
             Ar[k][i] = v.x;
             Ai[k][i] = v.y;
@@ -592,8 +650,8 @@ void cgemm_planar_kernel(const float2* __restrict__ A,
         }
 #pragma unroll
         for (int qq = 0; qq < LB; ++qq) {
-            const int idx = threadIdx.x + qq * NT;
-            const int k = BK ? idx % kPK : idx / BN, j = BK ? idx / kPK : idx % BN;
+            int k, j;
+            b_slot(qq, k, j);
             const float2 w = CB ? conjf2(rb[qq]) : rb[qq];
             if constexpr (kGauss) {
                 Br[k][j] = w.x;
@@ -606,31 +664,39 @@ void cgemm_planar_kernel(const float2* __restrict__ A,
         }
     };
 
-    fetch(0);
-    for (int k0 = 0; k0 < K; k0 += kPK) {
-        stash();
-        if (k0 + kPK < K)
-            fetch(k0 + kPK);  // the registers are free once stored
-        __syncthreads();
+    auto run = [&](auto vec) {
+        fetch(0, vec);
+        for (int k0 = 0; k0 < K; k0 += kPK) {
+            stash();
+            if (k0 + kPK < K)
+                fetch(k0 + kPK, vec);  // the registers are free once stored
+            __syncthreads();
 #pragma unroll
-        for (int kk = 0; kk < kPK; kk += 2) {
-            const float are = Ar[kk + h][wm * 32 + r], aim = Ai[kk + h][wm * 32 + r];
-            const float bre = Br[kk + h][wn * 32 + r], bim = Bi[kk + h][wn * 32 + r];
-            if constexpr (kGauss) {
-                // acc_re: T1 = P Re B; acc_im: T2 = Re A Q; acc_t3: T3 = Im A R.
-                const float asum = As[kk + h][wm * 32 + r], bsum = Bs[kk + h][wn * 32 + r];
-                acc_re = __builtin_amdgcn_mfma_f32_32x32x2f32(asum, bre, acc_re, 0, 0, 0);
-                acc_im = __builtin_amdgcn_mfma_f32_32x32x2f32(are, bim, acc_im, 0, 0, 0);
-                acc_t3 = __builtin_amdgcn_mfma_f32_32x32x2f32(aim, bsum, acc_t3, 0, 0, 0);
-            } else {
-                acc_re = __builtin_amdgcn_mfma_f32_32x32x2f32(are, bre, acc_re, 0, 0, 0);
-                acc_im = __builtin_amdgcn_mfma_f32_32x32x2f32(are, bim, acc_im, 0, 0, 0);
-                acc_re = __builtin_amdgcn_mfma_f32_32x32x2f32(-aim, bim, acc_re, 0, 0, 0);
-                acc_im = __builtin_amdgcn_mfma_f32_32x32x2f32(aim, bre, acc_im, 0, 0, 0);
+            for (int kk = 0; kk < kPK; kk += 2) {
+                const float are = Ar[kk + h][wm * 32 + r], aim = Ai[kk + h][wm * 32 + r];
+                const float bre = Br[kk + h][wn * 32 + r], bim = Bi[kk + h][wn * 32 + r];
+                if constexpr (kGauss) {
+                    // acc_re: T1 = P Re B; acc_im: T2 = Re A Q; acc_t3: T3 = Im A R.
+                    const float asum = As[kk + h][wm * 32 + r], bsum = Bs[kk + h][wn * 32 + r];
+                    acc_re = __builtin_amdgcn_mfma_f32_32x32x2f32(asum, bre, acc_re, 0, 0, 0);
+                    acc_im = __builtin_amdgcn_mfma_f32_32x32x2f32(are, bim, acc_im, 0, 0, 0);
+                    acc_t3 = __builtin_amdgcn_mfma_f32_32x32x2f32(aim, bsum, acc_t3, 0, 0, 0);
+                } else {
+                    acc_re = __builtin_amdgcn_mfma_f32_32x32x2f32(are, bre, acc_re, 0, 0, 0);
+                    acc_im = __builtin_amdgcn_mfma_f32_32x32x2f32(are, bim, acc_im, 0, 0, 0);
+                    acc_re = __builtin_amdgcn_mfma_f32_32x32x2f32(-aim, bim, acc_re, 0, 0, 0);
+                    acc_im = __builtin_amdgcn_mfma_f32_32x32x2f32(aim, bre, acc_im, 0, 0, 0);
+                }
             }
+            __syncthreads();
         }
-        __syncthreads();
-    }
+    };
+    const bool fast = a_inside && b_inside && K % kPK == 0 && (!kPairA || a_aligned) &&
+                      (!kPairB || b_aligned);
+    if (fast)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
     float2* Cp = C + (int64_t)p * M * N;
     const int j = j0 + wn * 32 + r;
 #pragma unroll
