@@ -722,7 +722,7 @@ def measure_fft(args, lib, torch, dev):
         "ms_per_operation": ops,
         "stages_fprop": stages,
         "direct_equivalent_TFLOPs": round(3 * direct_flops / (step_ms * 1e-3) / 1e12, 2),
-        "roofline": {"kernel": "cgemm_planar_kernel (per-bin complex products on the matrix cores, forward)",
+        "roofline": {"kernel": "cgemm_kernel (per-bin complex products on the matrix cores, forward)",
                      "bound": "mfma", "achieved": round(cm_tf, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(cm_tf / PEAK_FP32_MFMA_TFLOPS, 4),
                      "traffic": fft_traffic[0], "traffic_note": fft_traffic[1],

@@ -23,13 +23,14 @@
 //     T consecutive maps of one bin together.
 //   * Contraction.  For every bin, a complex matrix product (M x K) (K x N)
 //     -- S x f by f x f' for the forward: a dense contraction, so it runs on
-//     the matrix cores (v_mfma_f32_32x32x2f32, binary32 in and out), real
-//     and imaginary parts in separate LDS planes, three real products per
-//     pair of complex k (Gauss's form of the complex product, with the
-//     operand sums formed once per staged value).  Tiles of 64 x 64 (or
-//     64 x 32 where that pads less) complex outputs, K in steps of 8
-//     through LDS with the next step prefetched into registers; all tiles
-//     of one bin run on one XCD (shared operands stay in that XCD's L2).
+//     the matrix cores (v_mfma_f32_32x32x2f32, binary32 in and out), three
+//     real products per pair of complex k (Gauss's form of the complex
+//     product, its operand sums formed in registers after each LDS read).
+//     Tiles of 64 x 64 (or 128 x 32 where that pads less) complex outputs,
+//     K in steps of 8 through LDS, the next step's operands loaded as
+//     16-byte pairs into registers while the current one is multiplied;
+//     all tiles of one bin run on one XCD (shared operands stay in that
+//     XCD's L2).
 //   * Inverse.  Column transforms first, keeping only the rows that survive
 //     the crop, then row transforms of the Hermitian half rows; only the
 //     kept m x m corner is written, scaled by 1/n^2, and it goes out through
@@ -475,29 +476,28 @@ __global__ __launch_bounds__(InvTile<N>::kThreads) void c2r_kernel(const float2*
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// The products run on the matrix cores with planar operands: real and
-// imaginary parts in separate LDS planes, and one MFMA k-step takes two
-// complex k.  Per pair of k:
-//   Re C += Re A Re B - Im A Im B,   Im C += Re A Im B + Im A Re B
-// as four v_mfma_f32_32x32x2f32 on accumulators acc_re, acc_im; no
-// per-lane selects, a third of the LDS bytes of the interleaved form.  Lane
-// l supplies A[row l%32][k l/32] and B[k l/32][col l%32] of the pair.
+// The products run on the matrix cores, and one MFMA k-step takes two
+// complex k: lane l supplies A[row l%32][k l/32] and B[k l/32][col l%32] of
+// the pair.  Operands are staged into LDS as the complex values they are
+// loaded as (re, im interleaved): one 8-byte LDS read gives a lane both
+// parts, and the operand sums of the product (below) and the conjugations
+// are formed in registers after the read.
 // Block tile: 32 WR rows x 32 WC columns, WR WC waves of 32 x 32 each.  WC = 2
 // in general; WC = 1 where 64-column tiles would pad the product (96
 // columns take 3 tiles of 32 instead of 2 of 64, a quarter of them empty),
 // and then WR = 4 where 128-row tiles pad no more than 64-row ones.
 // (Two column subtiles per wave, reusing A, measured slower: 178 VGPRs.)
-// Complex k per K-tile of the planar kernel: 8 measured fastest on the
-// measured layer (16: +2 %, 32: +6 %, registers 174-226).  Two LDS buffers
-// per K-tile (one barrier instead of two) measured slower at 8 and 16.
-#ifndef FFTCONV_PLANAR_KT
-#define FFTCONV_PLANAR_KT 8
+// Complex k per K-tile: 8 measured fastest on the measured layer (16: +2 %,
+// 32: +6 %, registers 174-226).  Two LDS buffers per K-tile (one barrier
+// instead of two) measured slower at 8 and 16.
+#ifndef FFTCONV_KT
+#define FFTCONV_KT 8
 #endif
-constexpr int kPK = FFTCONV_PLANAR_KT;
+constexpr int kPK = FFTCONV_KT;
 // Complex products with three real products per complex term instead of
 // four (Gauss): with P = Re A + Im A, Q = Im B - Re B, R = Re B + Im B,
 //   T1 = P Re B,  T2 = Re A Q,  T3 = Im A R,  Re C = T1 - T3,  Im C = T1 + T2.
-// The sums are formed once per operand as it is staged into LDS.
+// (0: the four products Re A Re B, Im A Im B, Re A Im B, Im A Re B.)
 #ifndef FFTCONV_GAUSS
 #define FFTCONV_GAUSS 1
 #endif
@@ -506,11 +506,11 @@ constexpr int kPK = FFTCONV_PLANAR_KT;
 // Unbounded, the weight gradient's 64 x 32 kernel takes 64 VGPRs + 34 AGPRs
 // (4 waves); bounded at 5 it keeps its accumulators in 96 VGPRs, without
 // spilling, and its products run 6 % faster.  A bound of 6 spills.
-#ifndef FFTCONV_PLANAR_WPE1
-#define FFTCONV_PLANAR_WPE1 (FFTCONV_GAUSS ? 4 : 5)
+#ifndef FFTCONV_WPE1
+#define FFTCONV_WPE1 (FFTCONV_GAUSS ? 4 : 5)
 #endif
-#ifndef FFTCONV_PLANAR_WPE2
-#define FFTCONV_PLANAR_WPE2 1
+#ifndef FFTCONV_WPE2
+#define FFTCONV_WPE2 1
 #endif
 // 128 x 32 tiles (four waves of 32 x 32 in a column) for the 32-column
 // products: 17 % fewer operand bytes per output than 64 x 32 tiles of two
@@ -521,14 +521,14 @@ constexpr int kPK = FFTCONV_PLANAR_KT;
 #ifndef FFTCONV_PAIR_LOADS
 #define FFTCONV_PAIR_LOADS 1
 #endif
-#ifndef FFTCONV_PLANAR_WR4
-#define FFTCONV_PLANAR_WR4 1
+#ifndef FFTCONV_WR4
+#define FFTCONV_WR4 1
 #endif
 
 
 template <bool AK, bool BK, bool CA, bool CB, int WC, int WR = 2>
-__global__ __launch_bounds__(64 * WR * WC, WR * WC == 2 ? FFTCONV_PLANAR_WPE1 : FFTCONV_PLANAR_WPE2)
-void cgemm_planar_kernel(const float2* __restrict__ A,
+__global__ __launch_bounds__(64 * WR * WC, WR * WC == 2 ? FFTCONV_WPE1 : FFTCONV_WPE2)
+void cgemm_kernel(const float2* __restrict__ A,
                                                                const float2* __restrict__ B,
                                                                float2* __restrict__ C, int M,
                                                                int N, int K, int64_t sAp,
@@ -542,8 +542,9 @@ void cgemm_planar_kernel(const float2* __restrict__ A,
     constexpr int LB = BN * kPK / NT;   // B values per thread per K-tile
     static_assert(LA * NT == BM * kPK && LB * NT == BN * kPK, "whole values per thread");
     constexpr bool kGauss = FFTCONV_GAUSS != 0;
-    __shared__ float Ar[kPK][BM + 4], Ai[kPK][BM + 4], As[kGauss ? kPK : 1][BM + 4];
-    __shared__ float Br[kPK][BN + 4], Bi[kPK][BN + 4], Bs[kGauss ? kPK : 1][BN + 4];
+    // Operands in LDS as complex values (re, im), one row of the tile per k.
+    __shared__ __align__(16) float2 Al[kPK][BM + 2];
+    __shared__ __align__(16) float2 Bl[kPK][BN + 2];
     const int xcd = (int)(blockIdx.x & 7u), q = (int)(blockIdx.x >> 3);
     const int p = (q / tiles) * 8 + xcd;
     if (p >= nbins)
@@ -565,7 +566,12 @@ void cgemm_planar_kernel(const float2* __restrict__ A,
     // pair as one 16-byte vector.
     constexpr bool kPairA = FFTCONV_PAIR_LOADS && LA % 2 == 0;
     constexpr bool kPairB = FFTCONV_PAIR_LOADS && LB % 2 == 0;
-    float2 ra[LA], rb[LB];
+    // Paired slots are held as the 16-byte vectors they are loaded as, and
+    // split only when stored to LDS: the loop then carries the load's own
+    // registers (splitting at the load made the compiler copy them across
+    // the loop's back edge, which waited for the loads at once).
+    float2 ra[kPairA ? 1 : LA], rb[kPairB ? 1 : LB];
+    float4 ra4[kPairA ? LA / 2 : 1], rb4[kPairB ? LB / 2 : 1];
     // Tiles wholly inside the matrices load without per-element checks.
     const bool a_inside = i0 + BM <= M, b_inside = j0 + BN <= N;
     const bool a_aligned = ((uintptr_t)A & 15u) == 0 && (sAp & 1) == 0 && (lda & 1) == 0;
@@ -601,65 +607,120 @@ void cgemm_planar_kernel(const float2* __restrict__ A,
     auto fetch = [&](int k0, auto vec) {
         constexpr bool VEC = decltype(vec)::value;
         const bool k_inside = k0 + kPK <= K;
-#pragma unroll
-        for (int qq = 0; qq < LA; qq += (VEC && kPairA) ? 2 : 1) {
+        auto a_get = [&](int s2) {
             int k, i;
-            a_slot(qq, k, i);
+            a_slot(s2, k, i);
             const int64_t off = AK ? (int64_t)(i0 + i) * lda + (k0 + k) : (int64_t)(k0 + k) * lda + (i0 + i);
-            if constexpr (VEC && kPairA) {
-                const float4 q4 = *reinterpret_cast<const float4*>(Ap + off);
-                ra[qq] = make_float2(q4.x, q4.y);
-                ra[qq + 1] = make_float2(q4.z, q4.w);
-            } else if constexpr (VEC) {
-                ra[qq] = Ap[off];
-            } else {
-                ra[qq] = ((a_inside && k_inside) || (i0 + i < M && k0 + k < K)) ? Ap[off]
-                                                                                : make_float2(0.0f, 0.0f);
-            }
-        }
-#pragma unroll
-        for (int qq = 0; qq < LB; qq += (VEC && kPairB) ? 2 : 1) {
+            if (VEC)
+                return Ap[off];
+            return ((a_inside && k_inside) || (i0 + i < M && k0 + k < K)) ? Ap[off]
+                                                                        : make_float2(0.0f, 0.0f);
+        };
+        auto b_get = [&](int s2) {
             int k, j;
-            b_slot(qq, k, j);
+            b_slot(s2, k, j);
             const int64_t off = BK ? (int64_t)(j0 + j) * ldb + (k0 + k) : (int64_t)(k0 + k) * ldb + (j0 + j);
-            if constexpr (VEC && kPairB) {
-                const float4 q4 = *reinterpret_cast<const float4*>(Bp + off);
-                rb[qq] = make_float2(q4.x, q4.y);
-                rb[qq + 1] = make_float2(q4.z, q4.w);
-            } else if constexpr (VEC) {
-                rb[qq] = Bp[off];
-            } else {
-                rb[qq] = ((b_inside && k_inside) || (j0 + j < N && k0 + k < K)) ? Bp[off]
-                                                                                : make_float2(0.0f, 0.0f);
+            if (VEC)
+                return Bp[off];
+            return ((b_inside && k_inside) || (j0 + j < N && k0 + k < K)) ? Bp[off]
+                                                                        : make_float2(0.0f, 0.0f);
+        };
+        if constexpr (kPairA) {
+#pragma unroll
+            for (int qq = 0; qq < LA; qq += 2) {
+                if constexpr (VEC) {
+                    int k, i;
+                    a_slot(qq, k, i);
+                    const int64_t off = AK ? (int64_t)(i0 + i) * lda + (k0 + k) : (int64_t)(k0 + k) * lda + (i0 + i);
+                    ra4[qq / 2] = *reinterpret_cast<const float4*>(Ap + off);
+                } else {
+                    const float2 v0 = a_get(qq), v1 = a_get(qq + 1);
+                    ra4[qq / 2] = make_float4(v0.x, v0.y, v1.x, v1.y);
+                }
             }
+        } else {
+#pragma unroll
+            for (int qq = 0; qq < LA; ++qq)
+                ra[qq] = a_get(qq);
+        }
+        if constexpr (kPairB) {
+#pragma unroll
+            for (int qq = 0; qq < LB; qq += 2) {
+                if constexpr (VEC) {
+                    int k, j;
+                    b_slot(qq, k, j);
+                    const int64_t off = BK ? (int64_t)(j0 + j) * ldb + (k0 + k) : (int64_t)(k0 + k) * ldb + (j0 + j);
+                    rb4[qq / 2] = *reinterpret_cast<const float4*>(Bp + off);
+                } else {
+                    const float2 w0 = b_get(qq), w1 = b_get(qq + 1);
+                    rb4[qq / 2] = make_float4(w0.x, w0.y, w1.x, w1.y);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int qq = 0; qq < LB; ++qq)
+                rb[qq] = b_get(qq);
         }
     };
-    // The conjugations are applied here, as the values go to LDS, and not
-    // as they arrive: an operation on a loaded register right after its load
-    // would make the wave wait for the prefetch at once.
-    auto stash = [&]() {
-#pragma unroll
-        for (int qq = 0; qq < LA; ++qq) {
-            int k, i;
-            a_slot(qq, k, i);
-            const float2 v = CA ? conjf2(ra[qq]) : ra[qq];
-            Ar[k][i] = v.x;
-            Ai[k][i] = v.y;
-            if constexpr (kGauss)
-                As[k][i] = v.x + v.y;
+    auto a_held = [&](int qq) {
+        if constexpr (kPairA) {
+            const float4 q4 = ra4[qq / 2];
+            return (qq & 1) ? make_float2(q4.z, q4.w) : make_float2(q4.x, q4.y);
+        } else {
+            return ra[qq];
         }
+    };
+    auto b_held = [&](int qq) {
+        if constexpr (kPairB) {
+            const float4 q4 = rb4[qq / 2];
+            return (qq & 1) ? make_float2(q4.z, q4.w) : make_float2(q4.x, q4.y);
+        } else {
+            return rb[qq];
+        }
+    };
+    // Values go to LDS as loaded: a pair along k to two rows, a pair along
+    // the rows or columns as one 16-byte store.
+    auto stash = [&]() {
+        if constexpr (kPairA) {
 #pragma unroll
-        for (int qq = 0; qq < LB; ++qq) {
-            int k, j;
-            b_slot(qq, k, j);
-            const float2 w = CB ? conjf2(rb[qq]) : rb[qq];
-            if constexpr (kGauss) {
-                Br[k][j] = w.x;
-                Bi[k][j] = w.y - w.x;
-                Bs[k][j] = w.x + w.y;
-            } else {
-                Br[k][j] = w.x;
-                Bi[k][j] = w.y;
+            for (int qq = 0; qq < LA; qq += 2) {
+                int k, i;
+                a_slot(qq, k, i);
+                const float4 q4 = ra4[qq / 2];
+                if (AK) {
+                    Al[k][i] = make_float2(q4.x, q4.y);
+                    Al[k + 1][i] = make_float2(q4.z, q4.w);
+                } else {
+                    *reinterpret_cast<float4*>(&Al[k][i]) = q4;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int qq = 0; qq < LA; ++qq) {
+                int k, i;
+                a_slot(qq, k, i);
+                Al[k][i] = ra[qq];
+            }
+        }
+        if constexpr (kPairB) {
+#pragma unroll
+            for (int qq = 0; qq < LB; qq += 2) {
+                int k, j;
+                b_slot(qq, k, j);
+                const float4 q4 = rb4[qq / 2];
+                if (BK) {
+                    Bl[k][j] = make_float2(q4.x, q4.y);
+                    Bl[k + 1][j] = make_float2(q4.z, q4.w);
+                } else {
+                    *reinterpret_cast<float4*>(&Bl[k][j]) = q4;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int qq = 0; qq < LB; ++qq) {
+                int k, j;
+                b_slot(qq, k, j);
+                Bl[k][j] = rb[qq];
             }
         }
     };
@@ -673,19 +734,25 @@ void cgemm_planar_kernel(const float2* __restrict__ A,
             __syncthreads();
 #pragma unroll
             for (int kk = 0; kk < kPK; kk += 2) {
-                const float are = Ar[kk + h][wm * 32 + r], aim = Ai[kk + h][wm * 32 + r];
-                const float bre = Br[kk + h][wn * 32 + r], bim = Bi[kk + h][wn * 32 + r];
+                const float2 a = Al[kk + h][wm * 32 + r];
+                const float2 b = Bl[kk + h][wn * 32 + r];
                 if constexpr (kGauss) {
-                    // acc_re: T1 = P Re B; acc_im: T2 = Re A Q; acc_t3: T3 = Im A R.
-                    const float asum = As[kk + h][wm * 32 + r], bsum = Bs[kk + h][wn * 32 + r];
-                    acc_re = __builtin_amdgcn_mfma_f32_32x32x2f32(asum, bre, acc_re, 0, 0, 0);
-                    acc_im = __builtin_amdgcn_mfma_f32_32x32x2f32(are, bim, acc_im, 0, 0, 0);
-                    acc_t3 = __builtin_amdgcn_mfma_f32_32x32x2f32(aim, bsum, acc_t3, 0, 0, 0);
+                    // With a' = conj(a) under CA and b' = conj(b) under CB:
+                    // acc_re: T1 = P Re b, P = Re a' + Im a'; acc_im: T2 =
+                    // Re a Q, Q = Im b' - Re b; acc_t3: Im a R, R = Re b +
+                    // Im b' (that is T3 = Im a' R up to the sign of CA).
+                    const float pa = CA ? a.x - a.y : a.x + a.y;
+                    const float qb = CB ? -(b.x + b.y) : b.y - b.x;
+                    const float rb_ = CB ? b.x - b.y : b.x + b.y;
+                    acc_re = __builtin_amdgcn_mfma_f32_32x32x2f32(pa, b.x, acc_re, 0, 0, 0);
+                    acc_im = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, qb, acc_im, 0, 0, 0);
+                    acc_t3 = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, rb_, acc_t3, 0, 0, 0);
                 } else {
-                    acc_re = __builtin_amdgcn_mfma_f32_32x32x2f32(are, bre, acc_re, 0, 0, 0);
-                    acc_im = __builtin_amdgcn_mfma_f32_32x32x2f32(are, bim, acc_im, 0, 0, 0);
-                    acc_re = __builtin_amdgcn_mfma_f32_32x32x2f32(-aim, bim, acc_re, 0, 0, 0);
-                    acc_im = __builtin_amdgcn_mfma_f32_32x32x2f32(aim, bre, acc_im, 0, 0, 0);
+                    const float ai = CA ? -a.y : a.y, bi = CB ? -b.y : b.y;
+                    acc_re = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b.x, acc_re, 0, 0, 0);
+                    acc_im = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, bi, acc_im, 0, 0, 0);
+                    acc_re = __builtin_amdgcn_mfma_f32_32x32x2f32(-ai, bi, acc_re, 0, 0, 0);
+                    acc_im = __builtin_amdgcn_mfma_f32_32x32x2f32(ai, b.x, acc_im, 0, 0, 0);
                 }
             }
             __syncthreads();
@@ -704,7 +771,8 @@ void cgemm_planar_kernel(const float2* __restrict__ A,
         const int i = i0 + wm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
         if (i < M && j < N) {
             if constexpr (kGauss)
-                Cp[(int64_t)i * N + j] = make_float2(acc_re[v] - acc_t3[v], acc_re[v] + acc_im[v]);
+                Cp[(int64_t)i * N + j] = make_float2(CA ? acc_re[v] + acc_t3[v] : acc_re[v] - acc_t3[v],
+                                                     acc_re[v] + acc_im[v]);
             else
                 Cp[(int64_t)i * N + j] = make_float2(acc_re[v], acc_im[v]);
         }
@@ -789,14 +857,14 @@ static int launch_cmul(int op, const float2* a, const float2* b, float2* c, int 
         M = fo; N = f; K = S; sAp = (int64_t)S * fo; sBp = (int64_t)S * f; lda = fo; ldb = f;
     }
     // 32-column block tiles where they pad less than 64-column ones.
-#ifndef FFTCONV_PLANAR_WC
+#ifndef FFTCONV_WC
     const int wc = ((N + 63) / 64 * 64 - N > (N + 31) / 32 * 32 - N) ? 1 : 2;
 #else
-    const int wc = FFTCONV_PLANAR_WC;
+    const int wc = FFTCONV_WC;
 #endif
     // 128-row tiles (four waves) for the 32-column kernel where they pad M
     // no more than 64-row ones.
-    const int wr = (FFTCONV_PLANAR_WR4 && wc == 1 &&
+    const int wr = (FFTCONV_WR4 && wc == 1 &&
                     (M + 127) / 128 * 128 - M <= (M + 63) / 64 * 64 - M) ? 4 : 2;
     const int ptm = (M + 32 * wr - 1) / (32 * wr);
     const int ptn = (N + 32 * wc - 1) / (32 * wc), ptiles = ptn * ptm;
@@ -804,25 +872,25 @@ static int launch_cmul(int op, const float2* a, const float2* b, float2* c, int 
     if (pblocks > 0x7FFFFFFF)
         return MESWISH_EINVAL;
     const dim3 pgrid((unsigned)pblocks), pthreads(64 * wr * wc);
-#define FFTCONV_PLANAR(AK, BK, CA, CB)                                                            \
+#define FFTCONV_CGEMM(AK, BK, CA, CB)                                                            \
     do {                                                                                          \
         if (wc == 1 && wr == 4)                                                                   \
-            hipLaunchKernelGGL((cgemm_planar_kernel<AK, BK, CA, CB, 1, 4>), pgrid, pthreads, 0, s, \
+            hipLaunchKernelGGL((cgemm_kernel<AK, BK, CA, CB, 1, 4>), pgrid, pthreads, 0, s, \
                                a, b, c, M, N, K, sAp, sBp, lda, ldb, ptn, ptiles, nbins);         \
         else if (wc == 1)                                                                         \
-            hipLaunchKernelGGL((cgemm_planar_kernel<AK, BK, CA, CB, 1>), pgrid, pthreads, 0, s, a, \
+            hipLaunchKernelGGL((cgemm_kernel<AK, BK, CA, CB, 1>), pgrid, pthreads, 0, s, a, \
                                b, c, M, N, K, sAp, sBp, lda, ldb, ptn, ptiles, nbins);            \
         else                                                                                      \
-            hipLaunchKernelGGL((cgemm_planar_kernel<AK, BK, CA, CB, 2>), pgrid, pthreads, 0, s, a, \
+            hipLaunchKernelGGL((cgemm_kernel<AK, BK, CA, CB, 2>), pgrid, pthreads, 0, s, a, \
                                b, c, M, N, K, sAp, sBp, lda, ldb, ptn, ptiles, nbins);            \
     } while (0)
     if (op == 0)
-        FFTCONV_PLANAR(true, true, false, true);
+        FFTCONV_CGEMM(true, true, false, true);
     else if (op == 1)
-        FFTCONV_PLANAR(true, false, false, false);
+        FFTCONV_CGEMM(true, false, false, false);
     else
-        FFTCONV_PLANAR(false, false, true, false);
-#undef FFTCONV_PLANAR
+        FFTCONV_CGEMM(false, false, true, false);
+#undef FFTCONV_CGEMM
     return status_of(hipGetLastError());
 }
 
