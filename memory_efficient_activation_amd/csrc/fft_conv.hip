@@ -502,15 +502,19 @@ constexpr int kPK = FFTCONV_KT;
 #define FFTCONV_GAUSS 1
 #endif
 // Least waves per SIMD the compiler must leave room for (register budget),
-// for the 64 x 32 (WC = 1) and 64 x 64 (WC = 2) tiles; 1 sets no bound.
-// Unbounded, the weight gradient's 64 x 32 kernel takes 64 VGPRs + 34 AGPRs
-// (4 waves); bounded at 5 it keeps its accumulators in 96 VGPRs, without
-// spilling, and its products run 6 % faster.  A bound of 6 spills.
-#ifndef FFTCONV_WPE1
-#define FFTCONV_WPE1 (FFTCONV_GAUSS ? 4 : 5)
+// per block tile; 1 sets no bound.  Unbounded, the 4-wave kernels keep
+// their three accumulators in 48 AGPRs beside 54-58 VGPRs: 4 waves per
+// SIMD.  Bounded, they keep them in VGPRs without spilling: 64 x 64 at 6
+// waves (80 VGPRs; forward products 104 -> 98-99 us), 128 x 32 at 5 (80-92
+// VGPRs; at 6 they spill).  The 2-wave 64 x 32 kernel: at most 4.
+#ifndef FFTCONV_WPE_64X32
+#define FFTCONV_WPE_64X32 (FFTCONV_GAUSS ? 4 : 5)
 #endif
-#ifndef FFTCONV_WPE2
-#define FFTCONV_WPE2 1
+#ifndef FFTCONV_WPE_128X32
+#define FFTCONV_WPE_128X32 5
+#endif
+#ifndef FFTCONV_WPE_64X64
+#define FFTCONV_WPE_64X64 6
 #endif
 // 128 x 32 tiles (four waves of 32 x 32 in a column) for the 32-column
 // products: 17 % fewer operand bytes per output than 64 x 32 tiles of two
@@ -527,7 +531,8 @@ constexpr int kPK = FFTCONV_KT;
 
 
 template <bool AK, bool BK, bool CA, bool CB, int WC, int WR = 2>
-__global__ __launch_bounds__(64 * WR * WC, WR * WC == 2 ? FFTCONV_WPE1 : FFTCONV_WPE2)
+__global__ __launch_bounds__(64 * WR * WC, WR * WC == 2 ? FFTCONV_WPE_64X32
+                                          : WC == 2 ? FFTCONV_WPE_64X64 : FFTCONV_WPE_128X32)
 void cgemm_kernel(const float2* __restrict__ A,
                                                                const float2* __restrict__ B,
                                                                float2* __restrict__ C, int M,
