@@ -667,22 +667,6 @@ void cgemm_kernel(const float2* __restrict__ A,
                 rb[qq] = b_get(qq);
         }
     };
-    auto a_held = [&](int qq) {
-        if constexpr (kPairA) {
-            const float4 q4 = ra4[qq / 2];
-            return (qq & 1) ? make_float2(q4.z, q4.w) : make_float2(q4.x, q4.y);
-        } else {
-            return ra[qq];
-        }
-    };
-    auto b_held = [&](int qq) {
-        if constexpr (kPairB) {
-            const float4 q4 = rb4[qq / 2];
-            return (qq & 1) ? make_float2(q4.z, q4.w) : make_float2(q4.x, q4.y);
-        } else {
-            return rb[qq];
-        }
-    };
     // Values go to LDS as loaded: a pair along k to two rows, a pair along
     // the rows or columns as one 16-byte store.
     auto stash = [&]() {
