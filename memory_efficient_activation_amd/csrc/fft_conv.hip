@@ -50,8 +50,6 @@
 
 namespace fftconv {
 
-constexpr int kThreads = 256;
-
 // ---------------------------------------------------------------------------
 // Complex helpers and the in-register transform.
 // ---------------------------------------------------------------------------
