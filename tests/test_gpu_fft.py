@@ -119,6 +119,45 @@ def test_cmul_matches_the_per_bin_products(op, S, f, fo, P):
     assert r <= RTOL
 
 
+@pytest.mark.parametrize("op", [0, 1, 2])
+def test_cmul_operands_off_a_16_byte_boundary(op):
+    """The measured layer's shapes with spectra 8 bytes past a 16-byte
+    boundary: every tile lies inside the matrices, but the 16-byte pair loads
+    need aligned pairs, so the products take the checked loads.  They must
+    equal the aligned call's products bit for bit, and the oracle's."""
+    S, f, fo, P = 128, 96, 256, 3
+    rng = np.random.default_rng(40 + op)
+    na, nb = {0: S * f, 1: S * fo, 2: S * fo}[op], {0: fo * f, 1: fo * f, 2: S * f}[op]
+
+    def spec(maps):
+        return (rng.standard_normal((P, maps)) + 1j * rng.standard_normal((P, maps))).astype(np.complex64)
+
+    a, b = spec(na), spec(nb)
+
+    def shifted(h):
+        buf = torch.empty(h.size + 1, dtype=torch.complex64, device="cuda:0")
+        v = buf[1:].view(h.shape)
+        v.copy_(torch.from_numpy(h).to("cuda:0"))
+        assert v.data_ptr() % 16 == 8
+        return v
+
+    aligned = fft.cmul(op, _dev(a), _dev(b), S, f, fo)
+    off = fft.cmul(op, shifted(a), shifted(b), S, f, fo)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.view_as_real(aligned), torch.view_as_real(off))
+    A = a.astype(np.complex128).T.reshape({0: (S, f), 1: (S, fo), 2: (S, fo)}[op] + (P, 1))
+    Bm = b.astype(np.complex128).T.reshape({0: (fo, f), 1: (fo, f), 2: (S, f)}[op] + (P, 1))
+    fun = {0: fo_.freq_fprop, 1: fo_.freq_bprop, 2: fo_.freq_accgrad}[op]
+    args = (Bm, A) if op == 2 else (A, Bm)
+    want = fun(*args)
+    scale = fun(*(np.abs(t) for t in args)).real
+    want = want.reshape(want.shape[0] * want.shape[1], P).T
+    scale = scale.reshape(scale.shape[0] * scale.shape[1], P).T
+    r = _maxrel(np.abs(_host(off) - want), scale)
+    say(f"[fft] cmul op={op} off 16-byte boundary: bitwise equal to aligned, max err / term size = {r:.2e}")
+    assert r <= RTOL
+
+
 CASES = [(2, 3, 4, 8, 3), (3, 5, 2, 16, 5), (1, 1, 1, 8, 8), (2, 2, 3, 8, 1), (4, 7, 9, 32, 7),
          (2, 3, 5, 64, 13), (5, 17, 33, 16, 3)]
 
